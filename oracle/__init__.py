@@ -1,0 +1,276 @@
+"""CPU oracle for the DSA hot path: indexer score -> top-k -> sparse absorbed MLA.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The product path
+(``sparse_attention_10_amd``, the HIP kernels and the C ABI) never imports,
+links or calls it, and shares no code with it.
+
+Every function computes the plain definition of its step in float64 with
+numpy (a matmul, an exp and a stable sort are the only library steps), with no
+blocking, fusion or reordering beyond the definition, and rounds results to
+float32 (round to nearest even) at the end. Inputs are decoded exactly: bf16
+and f16 bit patterns convert exactly to float64.
+
+Sources (web pages; cited by title and section):
+
+* ik_llama_opt squash-commit log, sub-commit "Add GLM-5.2/DeepSeek-V3.2 DSA
+  lightning indexer": the score is relu(k . q) per indexer head, scaled by the
+  per-head weights, summed over heads, plus the causal mask; then top_k of
+  min(top_k, n_tokens). The selection is used only as a set (a mask scatter).
+* same log, "decode-correct via persistent indexer-K cache": queries are
+  scored against all cached indexer keys; q and k are Hadamard-rotated, which
+  leaves the scores unchanged; the selection is a descending argsort (same set).
+* ds4 "hy3: Metal decode path" PR, GLM CPU oracle section: MLA over cached
+  576-wide rows (512 latent + 64 already-rotated rope), score over qk_nope +
+  qk_rope = 256 dims, one softmax over the candidate rows, values from the
+  latent part.
+* ds4 "Hy3 (295B): CUDA backend support" PR, online-softmax commit: the
+  single-pass online softmax equals the two-pass one (split-K + merge here).
+
+Readings where the pages are silent or garbled (each also listed in the design doc):
+the indexer ``scale`` is an explicit factor applied after the head sum; relu
+is applied per head before the weight; masked keys score exactly -inf; a
+decode query sits at cache position kv_len - 1; NaN and -inf scores are never
+selected and do not count as valid, +inf is valid; -0.0 equals +0.0; ties go
+to the lower index and the selection is returned in ascending index order,
+padded with -1; the attention value is the 512-wide latent part only; an
+empty selection gives out = 0 and lse = -inf.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+F32, BF16, F16 = 0, 1, 2
+
+
+# ----------------------------------------------------------------------------
+# exact decoding of the storage dtypes
+# ----------------------------------------------------------------------------
+def decode(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Storage array -> float64, exactly. bf16/f16 arrive as uint16 bit patterns."""
+    x = np.asarray(x)
+    if dtype == F32:
+        return x.astype(np.float64)
+    if dtype == BF16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == F16:
+        return x.view(np.float16).astype(np.float64)
+    if dtype == -1:  # float64 passthrough, used by the invariance pins
+        return x.astype(np.float64)
+    raise ValueError(f"unknown dtype code {dtype}")
+
+
+def _default_q_pos(kv_len: np.ndarray, n_q: int) -> np.ndarray:
+    return (kv_len[:, None].astype(np.int64) - n_q + np.arange(n_q)[None, :])
+
+
+# ----------------------------------------------------------------------------
+# 1. lightning-indexer score
+# ----------------------------------------------------------------------------
+def index_score_f64(q, k, w, kv_len=None, q_pos=None, scale: float = 1.0,
+                    q_dtype: int = F32, k_dtype: int = F32, block: int = 32) -> np.ndarray:
+    """S[b,i,t] = scale * sum_h w[b,i,h] * max(0, sum_d q[b,i,h,d] * k[b,t,d]),
+    and S = -inf where t > q_pos[b,i] or t >= kv_len[b].
+
+    ik_llama_opt "DSA lightning indexer" sub-commit (score = relu(k.q) per
+    head, scaled per-head weights, summed over heads, + causal mask) and the
+    "persistent indexer-K cache" sub-commit (each query against every cached
+    key). q [B][n_q][H][D], k [B][n_kv][D], w [B][n_q][H]; float64 result.
+    """
+    qd = decode(q, q_dtype)
+    kd = decode(k, k_dtype)
+    wd = np.asarray(w, dtype=np.float64)
+    B, n_q, H, D = qd.shape
+    n_kv = kd.shape[1]
+    kv_len = np.full((B,), n_kv, np.int64) if kv_len is None else np.asarray(kv_len, np.int64)
+    q_pos = _default_q_pos(kv_len, n_q) if q_pos is None else np.asarray(q_pos, np.int64)
+    S = np.empty((B, n_q, n_kv), dtype=np.float64)
+    t = np.arange(n_kv)
+    for b in range(B):
+        for i0 in range(0, n_q, block):
+            i1 = min(n_q, i0 + block)
+            # logits[i, h, t] = sum_d q[i,h,d] k[t,d]
+            logits = (qd[b, i0:i1].reshape(-1, D) @ kd[b].T).reshape(i1 - i0, H, n_kv)
+            per_head = np.maximum(logits, 0.0)                      # relu per head
+            s = (wd[b, i0:i1, :, None] * per_head).sum(axis=1)      # weight, then head sum
+            s = scale * s
+            masked = (t[None, :] > q_pos[b, i0:i1, None]) | (t[None, :] >= kv_len[b])
+            s[masked] = -np.inf
+            S[b, i0:i1] = s
+    return S
+
+
+def index_score(q, k, w, kv_len=None, q_pos=None, scale: float = 1.0,
+                q_dtype: int = F32, k_dtype: int = F32) -> np.ndarray:
+    """The oracle score array: index_score_f64 rounded to float32 (nearest even)."""
+    return index_score_f64(q, k, w, kv_len, q_pos, scale, q_dtype, k_dtype).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# 2. top-k selection
+# ----------------------------------------------------------------------------
+def topk(scores: np.ndarray, top_k: int) -> np.ndarray:
+    """Per row: the min(top_k, n_valid) largest valid scores.
+
+    ik_llama_opt "DSA lightning indexer" sub-commit: top_k of
+    min(top_k, n_tokens), used as a set. Rank by a stable sort on (score
+    descending, index ascending) comparing values numerically (-0.0 == +0.0);
+    NaN and -inf are not valid. The chosen indices are returned in ascending
+    order and padded with -1 to top_k. scores [rows][n] float32 -> [rows][top_k] int32.
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    rows, n = s.shape
+    out = np.full((rows, top_k), -1, dtype=np.int32)
+    for r in range(rows):
+        row = s[r]
+        valid = np.nonzero(~np.isnan(row) & (row != -np.inf))[0]   # ascending indices
+        order = valid[np.argsort(-row[valid], kind="stable")]      # ties keep ascending index
+        K = min(top_k, valid.size)
+        out[r, :K] = np.sort(order[:K])
+    return out
+
+
+# ----------------------------------------------------------------------------
+# 3. sparse absorbed MLA over the selected latent rows
+# ----------------------------------------------------------------------------
+def _attend(qa_bi: np.ndarray, rows: np.ndarray, sm_scale: float, d_latent: int):
+    """One query, all heads, over the given rows (float64).
+
+    z[h,j] = sm_scale * qa[h,:] . row_j[:];  p = softmax_j(z);
+    out[h,:] = sum_j p[h,j] * row_j[:d_latent];  lse[h] = log sum_j exp(z[h,j]).
+    ds4 "hy3: Metal decode path" PR, GLM CPU oracle: one softmax over the
+    candidate rows, score over the full 576 (latent + rope) row, values from
+    the latent part.
+    """
+    Hm = qa_bi.shape[0]
+    if rows.shape[0] == 0:
+        return np.zeros((Hm, d_latent)), np.full((Hm,), -np.inf)
+    z = sm_scale * (qa_bi @ rows.T)                 # [Hm][J]
+    M = z.max(axis=1, keepdims=True)
+    e = np.exp(z - M)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    out = p @ rows[:, :d_latent]
+    lse = M[:, 0] + np.log(l[:, 0])
+    return out, lse
+
+
+def sparse_mla_f64(qa, latent, idx, sm_scale: float, d_latent: int, dtype: int = F32,
+                   kv_len=None) -> Tuple[np.ndarray, np.ndarray]:
+    """qa [B][n_q][Hm][Dc], latent [B][n_kv][Dc], idx [B][n_q][top_k] int32.
+
+    Index entries outside [0, kv_len[b]) (in particular the -1 padding) are
+    skipped. Returns out [B][n_q][Hm][d_latent] and lse [B][n_q][Hm], float64.
+    """
+    idx = np.asarray(idx)
+    B, n_q, Hm, Dc = qa.shape
+    n_kv = latent.shape[1]
+    kv_len = np.full((B,), n_kv, np.int64) if kv_len is None else np.asarray(kv_len, np.int64)
+    out = np.zeros((B, n_q, Hm, d_latent))
+    lse = np.zeros((B, n_q, Hm))
+    for b in range(B):
+        for i in range(n_q):
+            sel = idx[b, i]
+            sel = sel[(sel >= 0) & (sel < kv_len[b])]
+            rows = decode(latent[b, sel], dtype)
+            out[b, i], lse[b, i] = _attend(decode(qa[b, i], dtype), rows, sm_scale, d_latent)
+    return out, lse
+
+
+def sparse_mla(qa, latent, idx, sm_scale: float, d_latent: int, dtype: int = F32,
+               kv_len=None) -> Tuple[np.ndarray, np.ndarray]:
+    """sparse_mla_f64 rounded to float32."""
+    out, lse = sparse_mla_f64(qa, latent, idx, sm_scale, d_latent, dtype, kv_len)
+    return out.astype(np.float32), lse.astype(np.float32)
+
+
+def dense_mla_f64(qa, latent, sm_scale: float, d_latent: int, dtype: int = F32,
+                  kv_len=None, q_pos=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense causal MLA: every query attends to cache rows 0..q_pos[b,i] (< kv_len).
+
+    Used only as a check: with top_k >= n_kv the sparse path must equal it
+    (ik_llama_opt sub-commits report DSA-on identical to dense when
+    top_k >= n_kv). Written head by head, independently of _attend.
+    """
+    B, n_q, Hm, Dc = qa.shape
+    n_kv = latent.shape[1]
+    kv_len = np.full((B,), n_kv, np.int64) if kv_len is None else np.asarray(kv_len, np.int64)
+    q_pos = _default_q_pos(kv_len, n_q) if q_pos is None else np.asarray(q_pos, np.int64)
+    out = np.zeros((B, n_q, Hm, d_latent))
+    lse = np.full((B, n_q, Hm), -np.inf)
+    for b in range(B):
+        for i in range(n_q):
+            last = min(int(q_pos[b, i]), int(kv_len[b]) - 1)
+            if last < 0:
+                continue
+            rows = decode(latent[b, :last + 1], dtype)
+            qb = decode(qa[b, i], dtype)
+            for h in range(Hm):
+                z = np.array([sm_scale * float(np.dot(qb[h], rows[j])) for j in range(rows.shape[0])])
+                zmax = z.max()
+                wts = np.exp(z - zmax)
+                tot = wts.sum()
+                out[b, i, h] = (wts[:, None] * rows[:, :d_latent]).sum(axis=0) / tot
+                lse[b, i, h] = zmax + math.log(tot)
+    return out, lse
+
+
+def sparse_mla_split_merge_f64(qa, latent, idx, sm_scale: float, d_latent: int, dtype: int,
+                               n_split: int, kv_len=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Split-K partials and their log-sum-exp merge, in float64.
+
+    Split s covers index slots [s*c, (s+1)*c) with c = ceil(top_k / n_split):
+    m_s = max z, l_s = sum exp(z - m_s), o_s = sum exp(z - m_s) row[:d_latent];
+    merge: M = max_s m_s, L = sum_s exp(m_s - M) l_s,
+    out = sum_s exp(m_s - M) o_s / L, lse = M + log L. Empty splits carry
+    m = -inf, l = 0. ds4 "Hy3 (295B)" online-softmax commit: the running
+    max/denominator rescale reproduces the single softmax.
+    """
+    idx = np.asarray(idx)
+    B, n_q, Hm, Dc = qa.shape
+    top_k = idx.shape[2]
+    n_kv = latent.shape[1]
+    kv_len = np.full((B,), n_kv, np.int64) if kv_len is None else np.asarray(kv_len, np.int64)
+    c = -(-top_k // n_split)
+    out = np.zeros((B, n_q, Hm, d_latent))
+    lse = np.full((B, n_q, Hm), -np.inf)
+    for b in range(B):
+        for i in range(n_q):
+            qb = decode(qa[b, i], dtype)
+            ms, ls, os_ = [], [], []
+            for s in range(n_split):
+                sel = idx[b, i, s * c:(s + 1) * c]
+                sel = sel[(sel >= 0) & (sel < kv_len[b])]
+                if sel.size == 0:
+                    ms.append(np.full((Hm,), -np.inf)); ls.append(np.zeros(Hm)); os_.append(np.zeros((Hm, d_latent)))
+                    continue
+                rows = decode(latent[b, sel], dtype)
+                z = sm_scale * (qb @ rows.T)
+                m = z.max(axis=1)
+                e = np.exp(z - m[:, None])
+                ms.append(m); ls.append(e.sum(axis=1)); os_.append(e @ rows[:, :d_latent])
+            m_all = np.stack(ms)                      # [S][Hm]
+            M = m_all.max(axis=0)
+            if not np.isfinite(M).any():
+                continue
+            f = np.where(np.isfinite(m_all), np.exp(m_all - M[None, :]), 0.0)
+            L = (f * np.stack(ls)).sum(axis=0)
+            out[b, i] = (f[:, :, None] * np.stack(os_)).sum(axis=0) / L[:, None]
+            lse[b, i] = M + np.log(L)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# the whole chain, as one decode/prefill step of one DSA layer
+# ----------------------------------------------------------------------------
+def dsa_step(inp: dict, wl) -> dict:
+    """Scores -> selection -> attention for one workload's inputs (see workloads.gen_all)."""
+    S = index_score(inp["q"], inp["k"], inp["w"], inp["kv_len"], inp["q_pos"], wl.scale,
+                    wl.idx_dtype, wl.idx_dtype)
+    idx = topk(S.reshape(-1, S.shape[-1]), wl.top_k).reshape(wl.B, wl.n_q, wl.top_k)
+    out, lse = sparse_mla(inp["qa"], inp["latent"], idx, wl.sm_scale, wl.d_latent, wl.mla_dtype,
+                          inp["kv_len"])
+    return {"scores": S, "idx": idx, "out": out, "lse": lse}

@@ -1,0 +1,301 @@
+"""Pins of the CPU oracle to facts other than its own code.
+
+Each ``pins_*`` function takes an implementation of one oracle step and raises
+AssertionError when it breaks a fact that the pages or the mathematics fix:
+an invariant (Hadamard rotation, head additivity, permutation), a closed form
+(one-hot inputs, one selected row, uniform weights), a library routine
+(scipy's softmax / logsumexp, a Sylvester Hadamard matrix), a different
+formulation (MLA expanded at attend time), or brute force over all subsets on
+tiny inputs. tests/test_oracle.py runs them on the oracle and on copies of it
+with planted mistakes, which must fail.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import scipy.linalg
+import scipy.special
+
+F64 = -1  # float64 passthrough dtype code of the oracle
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), f"{what}: finite pattern differs"
+    assert np.array_equal(a[~fin], b[~fin]), f"{what}: non-finite values differ"
+    if fin.any():
+        err = np.max(np.abs(a[fin] - b[fin]))
+        ref = max(np.max(np.abs(b[fin])), 1e-300)
+        assert err <= rtol * ref, f"{what}: max err {err:.3e} vs {rtol:.1e} * {ref:.3e}"
+
+
+# ----------------------------------------------------------------------------
+# indexer scores: fn(q, k, w, kv_len, q_pos, scale, q_dtype, k_dtype) -> float64 [B][n_q][n_kv]
+# ----------------------------------------------------------------------------
+def sylvester(n: int) -> np.ndarray:
+    """Textbook Sylvester construction H_1 = [1], H_2n = [[H, H], [H, -H]]."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def pins_scores(fn):
+    rng = _rng(11)
+    B, n_q, H, D, n_kv = 2, 3, 4, 128, 37
+
+    # (a) Hadamard rotation of q and k leaves the scores unchanged
+    #     (ik_llama_opt "DSA lightning indexer": (Hq).(Hk) == q.k).
+    Hm = sylvester(128) / math.sqrt(128.0)
+    assert np.array_equal(sylvester(128), scipy.linalg.hadamard(128)), "Sylvester H_128"
+    assert np.allclose(Hm @ Hm.T, np.eye(128), atol=1e-13), "orthonormal H_128"
+    q = rng.standard_normal((B, n_q, H, D)) / math.sqrt(D)
+    k = rng.standard_normal((B, n_kv, D)) / math.sqrt(D)
+    w = rng.random((B, n_q, H))
+    s0 = fn(q, k, w, None, None, 1.0, F64, F64)
+    s1 = fn(q @ Hm, k @ Hm, w, None, None, 1.0, F64, F64)
+    _close(s1, s0, 1e-12, "Hadamard invariance")
+    assert np.any(s0 > 0), "scores not all zero"
+
+    # (b) one-hot weight and unit query vectors: the score is scale*c*relu(k[t, a_h])
+    #     for the one head h that carries weight c (c < 0 tells relu(x)*w from relu(x*w)).
+    dims = [5, 77, 3, 120]
+    qe = np.zeros((1, 1, H, D))
+    for h in range(H):
+        qe[0, 0, h, dims[h]] = 1.0
+    ks = rng.standard_normal((1, n_kv, D))
+    for h, c, scale in [(0, 0.75, 1.0), (2, -1.25, 0.5), (3, 2.0, 3.0)]:
+        we = np.zeros((1, 1, H))
+        we[0, 0, h] = c
+        got = fn(qe, ks, we, None, np.array([[n_kv - 1]]), scale, F64, F64)[0, 0]
+        want = scale * c * np.maximum(ks[0, :, dims[h]], 0.0)
+        _close(got, want, 1e-14, f"one-hot head {h}")
+
+    # (c) head additivity: S(w) = sum_h S(w * e_h)  (relu per head, then weighted sum)
+    wn = rng.standard_normal((B, n_q, H))
+    full = fn(q, k, wn, None, None, 1.0, F64, F64)
+    parts = np.zeros_like(full)
+    for h in range(H):
+        we = np.zeros_like(wn)
+        we[:, :, h] = wn[:, :, h]
+        parts += fn(q, k, we, None, None, 1.0, F64, F64)
+    _close(full, parts, 1e-12, "head additivity")
+
+    # (d) relu(x) - relu(-x) = x: S(q) - S(-q) = scale * (sum_h w_h q_h) . k
+    scale = 0.7
+    allpos = np.full((B, n_q), n_kv - 1)
+    sp = fn(q, k, wn, None, allpos, scale, F64, F64)
+    sm = fn(-q, k, wn, None, allpos, scale, F64, F64)
+    lin = scale * np.einsum("bid,btd->bit", np.einsum("bih,bihd->bid", wn, q), k)
+    _close(sp - sm, lin, 1e-12, "relu odd part")
+
+    # (e) mask: -inf exactly where t > q_pos or t >= kv_len, finite elsewhere
+    kv_len = np.array([30, 37])
+    q_pos = np.array([[0, 17, 36], [5, 29, 36]])
+    sc = fn(q, k, w, kv_len, q_pos, 1.0, F64, F64)
+    t = np.arange(n_kv)
+    masked = (t[None, None, :] > q_pos[:, :, None]) | (t[None, None, :] >= kv_len[:, None, None])
+    assert np.array_equal(np.isneginf(sc), masked), "mask pattern"
+    assert np.all(np.isfinite(sc[~masked])), "unmasked finite"
+    # default positions: decode queries are the last n_q cache rows
+    sd = fn(q, k, w, kv_len, None, 1.0, F64, F64)
+    qd = kv_len[:, None] - n_q + np.arange(n_q)[None, :]
+    md = (t[None, None, :] > qd[:, :, None]) | (t[None, None, :] >= kv_len[:, None, None])
+    assert np.array_equal(np.isneginf(sd), md), "default decode positions"
+
+    # (f) scale 0 -> zeros; all dot products negative -> zeros
+    z = fn(q, k, w, None, None, 0.0, F64, F64)
+    assert np.all(z[np.isfinite(z)] == 0.0), "scale 0"
+    kp = np.abs(k) + 0.01
+    qn = -np.abs(q) - 0.01
+    zn = fn(qn, kp, w, None, None, 1.0, F64, F64)
+    assert np.all(zn[np.isfinite(zn)] == 0.0), "negative dots"
+
+
+# ----------------------------------------------------------------------------
+# top-k: fn(scores [rows][n] f32, top_k) -> int32 [rows][top_k]
+# ----------------------------------------------------------------------------
+def _beats(a_val, a_idx, b_val, b_idx):
+    return a_val > b_val or (a_val == b_val and a_idx < b_idx)
+
+
+def brute_topk_row(row: np.ndarray, top_k: int) -> np.ndarray:
+    """The unique subset of size K = min(top_k, n_valid) whose every member beats
+    every valid non-member under (value descending, index ascending), found by
+    trying every subset."""
+    valid = [i for i in range(row.size) if not (np.isnan(row[i]) or row[i] == -np.inf)]
+    K = min(top_k, len(valid))
+    found = None
+    for comb in itertools.combinations(valid, K):
+        inside = set(comb)
+        ok = all(_beats(float(row[a]), a, float(row[b]), b) for a in comb for b in valid if b not in inside)
+        if ok:
+            assert found is None, "selection not unique"
+            found = comb
+    out = np.full((top_k,), -1, np.int32)
+    out[:K] = sorted(found)
+    return out
+
+
+def pins_topk(fn):
+    rng = _rng(5)
+    # (a) brute force over all subsets, with ties, signed zeros, -inf and NaN
+    for trial in range(60):
+        n = int(rng.integers(1, 9))
+        vals = rng.choice(np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 1.0, 2.0, np.inf, -np.inf, np.nan],
+                                   dtype=np.float32), size=n)
+        if trial % 3 == 0:
+            vals = rng.standard_normal(n).astype(np.float32)
+        top_k = int(rng.integers(1, n + 3))
+        got = fn(vals[None, :], top_k)[0]
+        want = brute_topk_row(vals, top_k)
+        assert np.array_equal(got, want), f"brute force: {vals} k={top_k}: {got} vs {want}"
+    # (b) closed forms
+    n = 40
+    eq = np.full((1, n), 0.5, np.float32)
+    assert np.array_equal(fn(eq, 7)[0], np.arange(7)), "all equal -> first k"
+    inc = np.arange(n, dtype=np.float32)[None, :]
+    assert np.array_equal(fn(inc, 7)[0], np.arange(n - 7, n)), "increasing -> last k"
+    part = np.full((1, n), -np.inf, np.float32)
+    part[0, [3, 9, 20]] = [1.0, -2.0, 0.0]
+    assert np.array_equal(fn(part, 5)[0], np.array([3, 9, 20, -1, -1])), "k >= n_valid"
+    assert np.all(fn(np.full((2, n), np.nan, np.float32), 4) == -1), "no valid entries"
+    # -0.0 and +0.0 are the same value: the tie goes to the lower index
+    sz = np.array([[-1.0, -0.0, 0.0, -0.5], [0.0, -0.0, -2.0, -3.0]], np.float32)
+    assert np.array_equal(fn(sz, 1), np.array([[1], [0]])), "signed zeros tie"
+    assert np.array_equal(fn(sz, 2), np.array([[1, 2], [0, 1]])), "signed zeros tie (2)"
+    # (c) permutation equivariance on tie-free rows
+    row = rng.permutation(np.arange(200, dtype=np.float32) * 0.37)
+    perm = rng.permutation(200)
+    a = set(fn(row[None, :], 31)[0].tolist())
+    b = set(perm[fn(row[perm][None, :], 31)[0]].tolist())
+    assert a == b, "permutation equivariance"
+    # (d) ascending, distinct, top_k wide
+    s = rng.standard_normal((4, 300)).astype(np.float32)
+    o = fn(s, 50)
+    assert o.shape == (4, 50) and o.dtype == np.int32
+    assert np.all(np.diff(o, axis=1) > 0), "ascending distinct"
+
+
+# ----------------------------------------------------------------------------
+# sparse MLA: fn(qa, latent, idx, sm_scale, d_latent, dtype, kv_len) -> (out, lse) float64
+# ----------------------------------------------------------------------------
+def pins_mla(fn, dense_fn=None, split_fn=None):
+    rng = _rng(23)
+    dl, dr = 512, 64
+    Dc = dl + dr
+
+    # (a) absorbed MLA equals MLA expanded at attend time (ds4 "hy3: Metal
+    #     decode path" GLM CPU oracle: per row K_nope = first 192 of the kv_b
+    #     expansion of row[:512], K_rope = row[512:576], score over 256 dims,
+    #     one softmax, V = the 256-wide value part of the expansion).
+    Hh, J, n_kv = 3, 9, 20
+    W_uk = rng.standard_normal((Hh, 192, dl)) / math.sqrt(dl)
+    W_uv = rng.standard_normal((Hh, 256, dl)) / math.sqrt(dl)
+    q_nope = rng.standard_normal((Hh, 192))
+    q_rope = rng.standard_normal((Hh, 64))
+    lat = rng.standard_normal((n_kv, Dc))
+    sel = np.array(sorted(rng.choice(n_kv, J, replace=False)), np.int32)
+    sm = 1.0 / math.sqrt(192 + 64)
+    out_exp = np.zeros((Hh, 256))
+    lse_exp = np.zeros(Hh)
+    for h in range(Hh):
+        kn = lat[sel, :dl] @ W_uk[h].T            # [J][192]
+        kr = lat[sel, dl:]                        # [J][64]
+        z = sm * (kn @ q_nope[h] + kr @ q_rope[h])
+        p = scipy.special.softmax(z)
+        v = lat[sel, :dl] @ W_uv[h].T             # [J][256]
+        out_exp[h] = p @ v
+        lse_exp[h] = scipy.special.logsumexp(z)
+    qa = np.concatenate([np.einsum("hnd,hn->hd", W_uk, q_nope), q_rope], axis=1)
+    out_abs, lse_abs = fn(qa[None, None], lat[None], sel[None, None], sm, dl, F64, None)
+    up = np.einsum("hvd,hd->hv", W_uv, out_abs[0, 0])
+    _close(up, out_exp, 1e-11, "absorbed == expanded")
+    _close(lse_abs[0, 0], lse_exp, 1e-12, "lse == logsumexp")
+
+    # (b) softmax rows sum to 1 and equal scipy's softmax: one-hot latent rows
+    #     make out[h, j] the weight of row j.
+    J2 = 50
+    lat2 = np.zeros((J2, Dc))
+    lat2[np.arange(J2), np.arange(J2)] = 1.0
+    lat2[:, dl:] = rng.standard_normal((J2, dr))
+    qa2 = rng.standard_normal((4, Dc)) * 3.0
+    idx2 = np.arange(J2, dtype=np.int32)
+    o2, l2 = fn(qa2[None, None], lat2[None], idx2[None, None], 0.3, dl, F64, None)
+    z2 = 0.3 * qa2 @ lat2.T
+    assert np.allclose(o2[0, 0].sum(axis=1), 1.0, atol=1e-12), "softmax sums to 1"
+    _close(o2[0, 0][:, :J2], scipy.special.softmax(z2, axis=1), 1e-12, "softmax == scipy")
+    _close(l2[0, 0], scipy.special.logsumexp(z2, axis=1), 1e-12, "lse == scipy")
+
+    # (c) closed forms: one row -> that row, lse = z; zero query -> mean, lse = log J;
+    #     two rows -> sigmoid weights
+    qa3 = rng.standard_normal((2, Dc))
+    lat3 = rng.standard_normal((6, Dc))
+    o, l = fn(qa3[None, None], lat3[None], np.array([[[4, -1, -1]]], np.int32), 0.2, dl, F64, None)
+    _close(o[0, 0], np.tile(lat3[4, :dl], (2, 1)), 1e-15, "one row")
+    _close(l[0, 0], 0.2 * qa3 @ lat3[4], 1e-14, "one row lse")
+    o, l = fn(np.zeros((1, 1, 2, Dc)), lat3[None], np.array([[[0, 2, 5]]], np.int32), 0.2, dl, F64, None)
+    _close(o[0, 0], np.tile(lat3[[0, 2, 5], :dl].mean(axis=0), (2, 1)), 1e-14, "uniform mean")
+    _close(l[0, 0], np.full(2, math.log(3.0)), 1e-14, "uniform lse")
+    o, l = fn(qa3[None, None], lat3[None], np.array([[[1, 3]]], np.int32), 0.2, dl, F64, None)
+    d = 0.2 * (qa3 @ lat3[1] - qa3 @ lat3[3])
+    pw = 1.0 / (1.0 + np.exp(-d))
+    _close(o[0, 0], pw[:, None] * lat3[1, :dl] + (1 - pw)[:, None] * lat3[3, :dl], 1e-13, "two rows")
+
+    # (d) padding / out-of-range entries are skipped; order of idx does not matter;
+    #     empty selection -> zeros and -inf
+    idx_a = np.array([[[5, 1, 3]]], np.int32)
+    idx_b = np.array([[[-1, 3, 9, 1, -1, 5]]], np.int32)   # 9 >= kv_len (=6)
+    oa, la = fn(qa3[None, None], lat3[None], idx_a, 0.2, dl, F64, np.array([6]))
+    ob, lb = fn(qa3[None, None], lat3[None], idx_b, 0.2, dl, F64, np.array([6]))
+    _close(ob, oa, 1e-14, "skip padding")
+    _close(lb, la, 1e-14, "skip padding lse")
+    oe, le = fn(qa3[None, None], lat3[None], np.full((1, 1, 4), -1, np.int32), 0.2, dl, F64, None)
+    assert np.all(oe == 0) and np.all(np.isneginf(le)), "empty selection"
+
+    # (e) batching: a batched call equals per-sequence calls
+    Bq, nq, Hb, nk = 3, 2, 2, 11
+    qb = rng.standard_normal((Bq, nq, Hb, Dc))
+    lb_ = rng.standard_normal((Bq, nk, Dc))
+    ib = np.stack([np.stack([np.sort(rng.choice(nk, 5, replace=False)) for _ in range(nq)])
+                   for _ in range(Bq)]).astype(np.int32)
+    ob_all, lb_all = fn(qb, lb_, ib, 0.1, dl, F64, None)
+    for b in range(Bq):
+        o1, l1 = fn(qb[b:b + 1], lb_[b:b + 1], ib[b:b + 1], 0.1, dl, F64, None)
+        _close(ob_all[b:b + 1], o1, 1e-15, "batching")
+
+    if dense_fn is not None:
+        # (f) top_k >= n_kv: every causal row selected -> equals dense causal attention
+        nk = 13
+        qd = rng.standard_normal((2, 2, 3, Dc))
+        ld = rng.standard_normal((2, nk, Dc))
+        q_pos = np.array([[6, 12], [0, 9]])
+        idx = np.full((2, 2, nk + 4), -1, np.int32)
+        for b in range(2):
+            for i in range(2):
+                idx[b, i, :q_pos[b, i] + 1] = np.arange(q_pos[b, i] + 1)
+        os_, ls_ = fn(qd, ld, idx, 0.125, dl, F64, None)
+        od, ld2 = dense_fn(qd, ld, 0.125, dl, F64, None, q_pos)
+        _close(os_, od, 1e-12, "sparse(all) == dense")
+        _close(ls_, ld2, 1e-12, "sparse(all) == dense lse")
+
+    if split_fn is not None:
+        # (g) split-K partials + log-sum-exp merge == single pass, any split count
+        qs = rng.standard_normal((1, 2, 3, Dc)) * 2
+        ls3 = rng.standard_normal((1, 40, Dc))
+        idx = np.stack([np.sort(rng.choice(40, 17, replace=False)) for _ in range(2)])[None].astype(np.int32)
+        idx[0, 1, -3:] = -1
+        o1, l1 = fn(qs, ls3, idx, 0.3, dl, F64, None)
+        for n_split in (1, 2, 3, 7, 17, 25):
+            o2, l2 = split_fn(qs, ls3, idx, 0.3, dl, F64, n_split, None)
+            _close(o2, o1, 1e-12, f"split merge {n_split}")
+            _close(l2, l1, 1e-12, f"split merge lse {n_split}")

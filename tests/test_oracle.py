@@ -1,0 +1,191 @@
+"""The oracle against its pins, and planted mistakes that the pins must catch (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle_pins import F64, pins_mla, pins_scores, pins_topk
+
+
+def test_score_pins():
+    pins_scores(oracle.index_score_f64)
+
+
+def test_topk_pins():
+    pins_topk(oracle.topk)
+
+
+def test_mla_pins():
+    pins_mla(oracle.sparse_mla_f64, oracle.dense_mla_f64, oracle.sparse_mla_split_merge_f64)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each copy of an oracle step below differs from the oracle
+# in one plausible way; the pins must reject every one of them.
+# ---------------------------------------------------------------------------
+def _score_mutant(kind):
+    def fn(q, k, w, kv_len=None, q_pos=None, scale=1.0, q_dtype=F64, k_dtype=F64):
+        qd = oracle.decode(q, q_dtype)
+        kd = oracle.decode(k, k_dtype)
+        wd = np.asarray(w, np.float64)
+        B, n_q, H, D = qd.shape
+        n_kv = kd.shape[1]
+        kv_len_ = np.full((B,), n_kv) if kv_len is None else np.asarray(kv_len)
+        q_pos_ = (kv_len_[:, None] - n_q + np.arange(n_q)[None]) if q_pos is None else np.asarray(q_pos)
+        logits = np.einsum("bihd,btd->biht", qd, kd)
+        if kind == "transpose_k":
+            logits = np.einsum("bihd,btd->biht", qd, kd[:, :, ::-1])
+        if kind == "relu_after_sum":
+            s = np.maximum(np.einsum("bih,biht->bit", wd, logits), 0)
+        elif kind == "relu_of_weighted":
+            s = np.einsum("biht->bit", np.maximum(wd[..., None] * logits, 0))
+        elif kind == "no_relu":
+            s = np.einsum("bih,biht->bit", wd, logits)
+        else:
+            s = np.einsum("bih,biht->bit", wd, np.maximum(logits, 0))
+        if kind != "no_scale":
+            s = s * scale
+        t = np.arange(n_kv)
+        off = 1 if kind == "mask_off_by_one" else 0
+        m = (t[None, None] > q_pos_[:, :, None] - off) | (t[None, None] >= kv_len_[:, None, None])
+        if kind != "no_mask":
+            s[m] = -np.inf
+        if kind == "drop_head":
+            s = s - scale * np.maximum(logits[:, :, -1], 0) * wd[:, :, -1:]
+            s[m] = -np.inf
+        return s
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["transpose_k", "relu_after_sum", "relu_of_weighted", "no_relu",
+                                  "no_scale", "mask_off_by_one", "no_mask", "drop_head"])
+def test_score_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_scores(_score_mutant(kind))
+
+
+def test_score_mutant_harness_is_faithful():
+    pins_scores(_score_mutant("none"))
+
+
+def _topk_mutant(kind):
+    def fn(scores, top_k):
+        s = np.asarray(scores, np.float32)
+        out = np.full((s.shape[0], top_k), -1, np.int32)
+        for r in range(s.shape[0]):
+            row = s[r]
+            if kind == "nan_valid":
+                valid = np.nonzero(row != -np.inf)[0]
+            elif kind == "neginf_valid":
+                valid = np.nonzero(~np.isnan(row))[0]
+            else:
+                valid = np.nonzero(~np.isnan(row) & (row != -np.inf))[0]
+            if kind == "ties_high_index":
+                order = valid[::-1][np.argsort(-row[valid][::-1], kind="stable")]
+            elif kind == "signed_zero":
+                key = row[valid].copy()
+                key[(key == 0) & np.signbit(key)] = -1e-30
+                order = valid[np.argsort(-key, kind="stable")]
+            else:
+                order = valid[np.argsort(-row[valid], kind="stable")]
+            K = min(top_k, valid.size)
+            if kind == "k_off_by_one":
+                K = max(0, K - 1)
+            sel = order[:K] if kind == "rank_order" else np.sort(order[:K])
+            out[r, :K] = sel
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["nan_valid", "neginf_valid", "ties_high_index", "signed_zero",
+                                  "k_off_by_one", "rank_order"])
+def test_topk_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_topk(_topk_mutant(kind))
+
+
+def test_topk_mutant_harness_is_faithful():
+    pins_topk(_topk_mutant("none"))
+
+
+def _mla_mutant(kind):
+    def fn(qa, latent, idx, sm_scale, d_latent, dtype=F64, kv_len=None):
+        idx = np.asarray(idx)
+        B, n_q, Hm, Dc = np.shape(qa)
+        n_kv = np.shape(latent)[1]
+        kv_len_ = np.full((B,), n_kv) if kv_len is None else np.asarray(kv_len)
+        out = np.zeros((B, n_q, Hm, d_latent))
+        lse = np.zeros((B, n_q, Hm))
+        for b in range(B):
+            for i in range(n_q):
+                sel = idx[b, i]
+                if kind != "keep_padding":
+                    sel = sel[(sel >= 0) & (sel < kv_len_[b])]
+                rows = oracle.decode(latent[b, sel], dtype)
+                qb = oracle.decode(qa[b, i], dtype)
+                if rows.shape[0] == 0:
+                    out[b, i] = 0
+                    lse[b, i] = -np.inf
+                    continue
+                if kind == "no_rope":
+                    z = sm_scale * (qb[:, :d_latent] @ rows[:, :d_latent].T)
+                elif kind == "no_sm_scale":
+                    z = qb @ rows.T
+                else:
+                    z = sm_scale * (qb @ rows.T)
+                M = z.max(axis=1, keepdims=True)
+                e = np.exp(z - M)
+                l = e.sum(axis=1, keepdims=True)
+                v = rows[:, Dc - d_latent:] if kind == "value_from_tail" else rows[:, :d_latent]
+                out[b, i] = (e @ v) / (1.0 if kind == "no_normalise" else l)
+                lse[b, i] = (0 if kind == "lse_no_max" else M[:, 0]) + np.log(l[:, 0])
+        return out, lse
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["keep_padding", "no_rope", "no_sm_scale", "value_from_tail",
+                                  "no_normalise", "lse_no_max"])
+def test_mla_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_mla(_mla_mutant(kind))
+
+
+def test_mla_mutant_harness_is_faithful():
+    pins_mla(_mla_mutant("none"))
+
+
+# ---------------------------------------------------------------------------
+# whole chain on the tiny fp32 workload and the generator's contract
+# ---------------------------------------------------------------------------
+def test_tiny_chain_and_invariants():
+    wl = workloads.TINY_FP32
+    inp = workloads.gen_all(wl, seed=0)
+    r = oracle.dsa_step(inp, wl)
+    assert r["scores"].shape == (1, 1, 256) and np.all(np.isfinite(r["scores"]))
+    assert np.all(r["idx"] >= 0) and np.all(np.diff(r["idx"][0, 0]) > 0)
+    # top_k >= n_kv selects every row -> dense causal attention (decode: rows 0..n_kv-1)
+    full = oracle.topk(r["scores"].reshape(1, -1), wl.n_kv + 5).reshape(1, 1, -1)
+    assert np.array_equal(full[0, 0, :wl.n_kv], np.arange(wl.n_kv))
+    o_s, l_s = oracle.sparse_mla_f64(inp["qa"], inp["latent"], full, wl.sm_scale, wl.d_latent, wl.mla_dtype)
+    o_d, l_d = oracle.dense_mla_f64(inp["qa"][:, :, :2], inp["latent"], wl.sm_scale, wl.d_latent, wl.mla_dtype)
+    assert np.allclose(o_s[:, :, :2], o_d, rtol=0, atol=1e-12)
+
+
+def test_generator_is_per_tensor_and_seeded():
+    wl = workloads.GLM_DECODE_8K.scaled(n_kv=300, B=3)
+    a = workloads.gen_all(wl, seed=7)
+    b = workloads.gen_seq(wl, 7, 2)
+    for name in ("q", "k", "w", "qa", "latent"):
+        assert np.array_equal(a[name][2], b[name]), name
+    c = workloads.gen_all(wl, seed=8)
+    assert not np.array_equal(a["k"], c["k"])
+    # bf16 rounding is round-to-nearest-even from float32
+    x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e38], np.float32)
+    bits = workloads.f32_to_bf16_bits(x)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.015625 and back[3] == -2.5
+    # the rotation keeps the indexer statistics: std of q entries ~ 1/sqrt(128)
+    q = oracle.decode(a["q"], workloads.BF16)
+    assert abs(q.std() * math.sqrt(128) - 1.0) < 0.1
