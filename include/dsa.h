@@ -1,0 +1,147 @@
+/*
+ * libdsa — DeepSeek Sparse Attention (DSA) hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Three calls, one per step of the method, run back to back on one HIP stream:
+ *
+ *   dsa_index_score      lightning-indexer scores of each query against every cached key
+ *   dsa_topk             the top_k highest-scoring cache rows of each query
+ *   dsa_sparse_mla_attn  absorbed MLA attention over only the selected 576-wide latent rows
+ *
+ * Conventions shared by every call:
+ *   - Pointers named as device buffers must be device memory (hipMalloc, or a torch
+ *     tensor on the GPU). The caller owns every buffer; the library never allocates,
+ *     frees or keeps a pointer beyond the call. Scratch memory is a caller-provided
+ *     workspace whose size the matching *_workspace_size query returns.
+ *   - Arrays are dense and row-major with the shapes written next to each argument.
+ *   - Every call returns a status (DSA_OK or a negative DSA_ERR_*). Argument errors are
+ *     detected on the host before anything is launched; the call then writes nothing.
+ *     DSA_ERR_HIP reports a failed kernel launch. No call synchronises the host or the
+ *     stream: faults inside a kernel surface at the caller's next synchronisation.
+ *   - Calls are stateless and may be made from several host threads at once
+ *     (dsa_last_error is per thread). Two calls that share a workspace must not
+ *     overlap in time on the device.
+ *   - bf16 and f16 data are 16-bit IEEE bit patterns (bfloat16: top half of an fp32).
+ */
+#ifndef LIBDSA_DSA_H
+#define LIBDSA_DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_F16 = 2 } dsa_dtype;
+
+enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL */
+  DSA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  DSA_ERR_DTYPE = -3,       /* unknown dtype, or a dtype pairing the call does not take */
+  DSA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than *_workspace_size */
+  DSA_ERR_UNSUPPORTED = -5, /* valid arguments outside what the kernels implement */
+  DSA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+};
+
+/*
+ * Lightning-indexer score (ik_llama_opt commit log, sub-commit "Add GLM-5.2/DeepSeek-V3.2
+ * DSA lightning indexer": relu(k.q) per indexer head, scaled by per-head weights, summed
+ * over heads, plus the causal mask; sub-commit "decode-correct via persistent indexer-K
+ * cache": every query is scored against all cached indexer keys).
+ *
+ *   scores[b][i][t] = scale * sum_h w[b][i][h] * max(0, sum_d q[b][i][h][d] * k_cache[b][t][d])
+ *   scores[b][i][t] = -inf  where t > q_pos[b][i] or t >= kv_len[b]
+ *
+ * q        device, [B][n_q][H][D], q_dtype
+ * k_cache  device, [B][n_kv][D], k_dtype (keys already roped and Hadamard-rotated upstream)
+ * w        device, [B][n_q][H] fp32 per-head weights
+ * kv_len   device, [B] int32 valid rows per sequence, or NULL (every sequence has n_kv)
+ * q_pos    device, [B][n_q] int32 cache position of each query, or NULL
+ *          (NULL: q_pos[b][i] = kv_len[b] - n_q + i, the queries are the last n_q rows)
+ * scores   device, [B][n_q][n_kv] fp32, written in full
+ * scale    factor applied after the head sum
+ * Sizes: B, n_q, H, D, n_kv >= 1. q_dtype must equal k_dtype (F32, BF16 or F16).
+ * bf16/f16 with D = 128 and H <= 32 run on MFMA; other shapes run a plain kernel that
+ * needs H * D <= 16384.
+ */
+int dsa_index_score(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
+                    const int32_t* q_pos, float* scores, int B, int n_q, int H, int D, int n_kv,
+                    int q_dtype, int k_dtype, float scale, hipStream_t stream);
+
+/*
+ * Top-k selection (ik_llama_opt "DSA lightning indexer" sub-commit: top_k of
+ * min(top_k, n_tokens), used as a set; "persistent indexer-K cache" sub-commit: the same
+ * set from a descending argsort).
+ *
+ * For each row, the K = min(top_k, n_valid) largest valid scores, where NaN and -inf are
+ * not valid and +inf is. Order: score descending, ties to the lower index; -0.0 equals
+ * +0.0. idx[r] holds the chosen indices in ascending order followed by -1 up to top_k.
+ * The result is unique, so it does not depend on the path or on timing.
+ *
+ * scores     device, [rows][n_kv] fp32
+ * idx        device, [rows][top_k] int32, written in full
+ * workspace  device scratch of at least dsa_topk_workspace_size(rows, n_kv, top_k) bytes
+ *            (NULL allowed when that size is 0)
+ * Sizes: rows >= 1, n_kv >= 1, top_k >= 1 (top_k > n_kv is allowed).
+ */
+size_t dsa_topk_workspace_size(int rows, int n_kv, int top_k);
+int dsa_topk(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, void* workspace,
+             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sparse absorbed MLA over the selected latent rows (ds4 "hy3: Metal decode path" PR,
+ * GLM CPU oracle section: cached rows are 512 latent + 64 already-rotated rope values,
+ * one softmax over the candidate rows; ik_llama_opt "MLA tensor parallelism" sub-commit:
+ * absorbed per-head wk_b / wv_b; ds4 "Hy3 (295B)" PR: single-pass online softmax).
+ *
+ *   z[j]    = sm_scale * sum_{d < Dc} q_abs[b][i][h][d] * latent[b][j][d],  Dc = d_latent + d_rope
+ *   out[b][i][h][:] = sum_j softmax(z)[j] * latent[b][j][0:d_latent]
+ *   lse[b][i][h]    = log sum_j exp(z[j])
+ * over the rows j = idx[b][i][s] with 0 <= j < kv_len[b] (other entries, e.g. -1, skip).
+ * An empty selection gives out = 0 and lse = -inf.
+ *
+ * The selected rows are processed in n_split parts of ceil(top_k / n_split) index slots
+ * each (online softmax inside a part) and the parts are merged by log-sum-exp.
+ *
+ * q_abs      device, [B][n_q][Hm][Dc], dtype
+ * latent     device, [B][n_kv][Dc], dtype
+ * idx        device, [B][n_q][top_k] int32
+ * kv_len     device, [B] int32, or NULL (every sequence has n_kv valid rows)
+ * out        device, [B][n_q][Hm][d_latent] fp32, written in full
+ * lse        device, [B][n_q][Hm] fp32, or NULL
+ * n_split    number of parts; <= 0 picks dsa_sparse_mla_num_splits(B, n_q, top_k)
+ * workspace  device scratch of at least dsa_sparse_mla_workspace_size(...) bytes with the
+ *            same B, n_q, Hm, top_k, d_latent, n_split (NULL allowed when that is 0)
+ * dtype: F32 or BF16. BF16 with Hm a multiple of 16 (<= 64), d_latent = 512 and
+ * d_rope in {0, 64} runs on MFMA; other shapes run a plain kernel that needs
+ * Dc <= 1024 and d_latent <= 1024.
+ */
+int dsa_sparse_mla_num_splits(int B, int n_q, int top_k);
+size_t dsa_sparse_mla_workspace_size(int B, int n_q, int Hm, int top_k, int d_latent, int n_split);
+int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* idx,
+                        const int32_t* kv_len, float* out, float* lse, int B, int n_q, int Hm,
+                        int n_kv, int top_k, int d_latent, int d_rope, float sm_scale, int dtype,
+                        int n_split, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Tuning switches. They choose between kernels that compute identical results and
+ * change only speed. key "topk_path": 0 = automatic, 1 = one workgroup per row,
+ * 2 = two-stage (segments, then candidates). Returns DSA_OK, or DSA_ERR_SHAPE for an
+ * unknown key or value. Process-wide; set it before launching work.
+ */
+int dsa_set_tuning(const char* key, int value);
+
+/* Static text of a status code. */
+const char* dsa_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDSA_DSA_H */

@@ -1,0 +1,170 @@
+// C ABI of libdsa: argument validation, path selection and error reporting.
+// Every check runs on the host before any launch; a rejected call writes nothing.
+#include "../../include/dsa.h"
+
+#include <atomic>
+#include <climits>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int> g_topk_path{0};
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int d) { return d == DSA_F32 || d == DSA_BF16 || d == DSA_F16; }
+
+}  // namespace
+
+extern "C" {
+
+int dsa_version(void) { return 100; }
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size is out of range or inconsistent";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE: unsupported dtype or dtype pairing";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: valid arguments outside the implemented set";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "unknown libdsa status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+int dsa_set_tuning(const char* key, int value) {
+  if (!key) return fail(DSA_ERR_NULL, "dsa_set_tuning: key is NULL");
+  if (std::strcmp(key, "topk_path") == 0) {
+    if (value < 0 || value > 2) return fail(DSA_ERR_SHAPE, "topk_path must be 0, 1 or 2 (got %d)", value);
+    g_topk_path.store(value);
+    return ok();
+  }
+  return fail(DSA_ERR_SHAPE, "dsa_set_tuning: unknown key '%s'", key);
+}
+
+int dsa_index_score(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
+                    const int32_t* q_pos, float* scores, int B, int n_q, int H, int D, int n_kv,
+                    int q_dtype, int k_dtype, float scale, hipStream_t stream) {
+  if (!q || !k_cache || !w || !scores)
+    return fail(DSA_ERR_NULL, "dsa_index_score: q, k_cache, w and scores must be non-NULL");
+  if (B < 1 || n_q < 1 || H < 1 || D < 1 || n_kv < 1)
+    return fail(DSA_ERR_SHAPE, "dsa_index_score: B=%d n_q=%d H=%d D=%d n_kv=%d must all be >= 1", B, n_q,
+                H, D, n_kv);
+  if ((long long)B * n_q > INT_MAX || (long long)B * n_q * n_kv > (1LL << 40))
+    return fail(DSA_ERR_SHAPE, "dsa_index_score: B*n_q*n_kv too large");
+  if (!valid_dtype(q_dtype) || !valid_dtype(k_dtype))
+    return fail(DSA_ERR_DTYPE, "dsa_index_score: unknown dtype (q %d, k %d)", q_dtype, k_dtype);
+  if (q_dtype != k_dtype)
+    return fail(DSA_ERR_DTYPE, "dsa_index_score: q_dtype (%d) must equal k_dtype (%d)", q_dtype, k_dtype);
+  const bool mfma = D == 128 && H <= 32 && q_dtype != DSA_F32;
+  if (mfma && (!aligned16(q) || !aligned16(k_cache)))
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_index_score: q and k_cache must be 16-byte aligned");
+  if (!mfma && (long long)H * D > 16384)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_index_score: H*D = %lld exceeds 16384 outside the MFMA shape (16-bit, D=128, H<=32)",
+                (long long)H * D);
+  return hip_status(dsa::launch_index_score(q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv,
+                                            q_dtype, scale, stream),
+                    "dsa_index_score launch");
+}
+
+size_t dsa_topk_workspace_size(int rows, int n_kv, int top_k) {
+  if (rows < 1 || n_kv < 1 || top_k < 1) return 0;
+  return dsa::plan_topk(rows, n_kv, top_k, 2).ws_bytes;
+}
+
+int dsa_topk(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+  if (!scores || !idx) return fail(DSA_ERR_NULL, "dsa_topk: scores and idx must be non-NULL");
+  if (rows < 1 || n_kv < 1 || top_k < 1)
+    return fail(DSA_ERR_SHAPE, "dsa_topk: rows=%d n_kv=%d top_k=%d must all be >= 1", rows, n_kv, top_k);
+  if ((long long)rows * n_kv > (1LL << 40) || rows > 65535)
+    return fail(DSA_ERR_SHAPE, "dsa_topk: rows=%d x n_kv=%d out of range (rows <= 65535)", rows, n_kv);
+  const size_t need = dsa_topk_workspace_size(rows, n_kv, top_k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_topk: workspace of %zu bytes needed, got %zu%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  const dsa::TopkPlan plan = dsa::plan_topk(rows, n_kv, top_k, g_topk_path.load());
+  return hip_status(dsa::launch_topk(scores, idx, rows, n_kv, top_k, plan, workspace, stream),
+                    "dsa_topk launch");
+}
+
+int dsa_sparse_mla_num_splits(int B, int n_q, int top_k) {
+  if (B < 1 || n_q < 1 || top_k < 1) return 1;
+  return dsa::mla_auto_splits(B, n_q, top_k);
+}
+
+size_t dsa_sparse_mla_workspace_size(int B, int n_q, int Hm, int top_k, int d_latent, int n_split) {
+  if (B < 1 || n_q < 1 || Hm < 1 || top_k < 1 || d_latent < 1) return 0;
+  if (n_split <= 0) n_split = dsa::mla_auto_splits(B, n_q, top_k);
+  if (n_split > top_k) n_split = top_k;
+  return dsa::mla_workspace_bytes(B, n_q, Hm, top_k, d_latent, n_split);
+}
+
+int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* idx,
+                        const int32_t* kv_len, float* out, float* lse, int B, int n_q, int Hm,
+                        int n_kv, int top_k, int d_latent, int d_rope, float sm_scale, int dtype,
+                        int n_split, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q_abs || !latent || !idx || !out)
+    return fail(DSA_ERR_NULL, "dsa_sparse_mla_attn: q_abs, latent, idx and out must be non-NULL");
+  if (B < 1 || n_q < 1 || Hm < 1 || n_kv < 1 || top_k < 1 || d_latent < 1 || d_rope < 0)
+    return fail(DSA_ERR_SHAPE,
+                "dsa_sparse_mla_attn: B=%d n_q=%d Hm=%d n_kv=%d top_k=%d d_latent=%d d_rope=%d out of range",
+                B, n_q, Hm, n_kv, top_k, d_latent, d_rope);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_DTYPE, "dsa_sparse_mla_attn: dtype must be F32 or BF16 (got %d)", dtype);
+  if (n_split <= 0) n_split = dsa::mla_auto_splits(B, n_q, top_k);
+  if (n_split > top_k) n_split = top_k;
+  if ((long long)B * n_q * n_split * Hm > INT_MAX)
+    return fail(DSA_ERR_SHAPE, "dsa_sparse_mla_attn: B*n_q*n_split*Hm too large");
+  const int chunk = (top_k + n_split - 1) / n_split;
+  const bool mfma = dsa::mla_mfma_supported(Hm, d_latent, d_rope, dtype);
+  if (mfma) {
+    if (chunk > 2048)
+      return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_mla_attn: %d index slots per part exceed 2048; use n_split >= %d",
+                  chunk, (top_k + 2047) / 2048);
+    if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out))
+      return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_mla_attn: q_abs, latent and out must be 16-byte aligned");
+  } else if (d_latent + d_rope > 1024 || d_latent > 1024) {
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_sparse_mla_attn: d_latent + d_rope = %d exceeds 1024 outside the MFMA shape "
+                "(bf16, Hm %% 16 == 0, Hm <= 64, d_latent 512, d_rope 0 or 64)",
+                d_latent + d_rope);
+  }
+  const size_t need = dsa::mla_workspace_bytes(B, n_q, Hm, top_k, d_latent, n_split);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_sparse_mla_attn: workspace of %zu bytes needed, got %zu%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  return hip_status(dsa::launch_sparse_mla(q_abs, latent, idx, kv_len, out, lse, B, n_q, Hm, n_kv, top_k,
+                                           d_latent, d_rope, sm_scale, dtype, n_split, workspace, stream),
+                    "dsa_sparse_mla_attn launch");
+}
+
+}  // extern "C"

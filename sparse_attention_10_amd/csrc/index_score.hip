@@ -1,0 +1,381 @@
+// Lightning-indexer scores (ik_llama_opt commit log, sub-commits "Add GLM-5.2/DeepSeek-V3.2
+// DSA lightning indexer" and "decode-correct via persistent indexer-K cache"):
+//   S[b,i,t] = scale * sum_h w[b,i,h] * relu(sum_d q[b,i,h,d] * k[b,t,d]),  -inf if masked.
+//
+// Three kernels:
+//   index_score_plain        any dtype / shape, one thread per key (fp32 inputs, odd shapes)
+//   index_score_decode_mfma  16-bit inputs, D = 128, H <= 32, few queries per sequence:
+//                            each wave owns 64 keys per step, the 32 heads sit on the MFMA M
+//                            dimension, relu + head weights + head sum run in the epilogue.
+//   index_score_prefill_mfma 16-bit inputs, D = 128, H <= 32, many queries: a 64-key tile is
+//                            staged in LDS once and shared by 8 queries (2 per wave).
+// Keys are read from HBM exactly once per (query block, key) with coalesced 16-byte loads and
+// re-laid out through XOR-swizzled LDS into the MFMA operand layout.
+#include "common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------------------
+// plain kernel
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void index_score_plain(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ w,
+    const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
+    int n_q, int H, int D, int n_kv, float scale) {
+  extern __shared__ float qs[];  // [H][D] of this query
+  const int bi = blockIdx.y;
+  const int b = bi / n_q, i = bi - b * n_q;
+  const T* qp = q + (long)bi * H * D;
+  for (int e = threadIdx.x; e < H * D; e += blockDim.x) qs[e] = load_as_f32(qp, e);
+  __syncthreads();
+  const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
+  const int pos = q_pos ? q_pos[bi] : len - n_q + i;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_kv) return;
+  float* out = scores + (long)bi * n_kv;
+  if (t > pos || t >= len) {
+    out[t] = -INFINITY;
+    return;
+  }
+  const T* kp = k + ((long)b * n_kv + t) * D;
+  const float* wp = w + (long)bi * H;
+  float s = 0.f;
+  for (int h = 0; h < H; ++h) {
+    float dot = 0.f;
+    for (int d = 0; d < D; ++d) dot = fmaf(qs[h * D + d], load_as_f32(kp, d), dot);
+    s = fmaf(wp[h], fmaxf(dot, 0.f), s);
+  }
+  out[t] = scale * s;
+}
+
+// ---------------------------------------------------------------------------------------
+// MFMA helpers. v_mfma_f32_16x16x32_{bf16,f16}: lane l holds A[l%16][8*(l/16)+j] and
+// B[8*(l/16)+j][l%16] (j = 0..7) and receives D[4*(l/16)+e][l%16] (e = 0..3).
+// ---------------------------------------------------------------------------------------
+template <typename T16> struct Mma16;
+template <> struct Mma16<bf16_t> {
+  static __device__ __forceinline__ f32x4 run(i32x4 a, i32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma16<f16_t> {
+  static __device__ __forceinline__ f32x4 run(i32x4 a, i32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+// One 128-dim key row is 256 bytes = 16 chunks of 16 bytes. In LDS, chunk c of tile row r
+// sits at position c ^ (r & 15): the 16 lanes that read the same chunk of 16 consecutive
+// rows then hit 16 different 16-byte bank groups.
+__device__ __forceinline__ int key_lds_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+
+// Query operand of one wave: heads 16*mt + (lane%16), k-step s covers dims 32*s + 8*(lane/16) .. +8.
+template <typename T16>
+__device__ __forceinline__ void load_q_operand(const T16* q_bi, int H, int lane, i32x4 (&qa)[2][4]) {
+  const int g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int head = 16 * mt + r16;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (head < H)
+        qa[mt][s] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(q_bi) +
+                                                    head * 256 + (4 * s + g) * 16);
+      else
+        qa[mt][s] = i32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// Weights of the accumulator rows a lane holds: heads 16*mt + 4*(lane/16) + e.
+__device__ __forceinline__ void load_w_rows(const float* w_bi, int H, int lane, float (&wr)[2][4]) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int head = 16 * mt + 4 * g + e;
+      wr[mt][e] = head < H ? w_bi[head] : 0.f;
+    }
+}
+
+// relu, head weight and head sum of one 16-key N tile; every lane of a column ends with the sum.
+__device__ __forceinline__ float head_reduce(const f32x4& a0, const f32x4& a1, const float (&wr)[2][4]) {
+  float p = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    p = fmaf(wr[0][e], fmaxf(a0[e], 0.f), p);
+    p = fmaf(wr[1][e], fmaxf(a1[e], 0.f), p);
+  }
+  p += shfl_xor(p, 16);
+  p += shfl_xor(p, 32);
+  return p;
+}
+
+// ---------------------------------------------------------------------------------------
+// decode: grid (key blocks, B * n_q), 4 waves; wave w of block x handles the 64-key chunks
+// ((x * iters + it) * 4 + w) for it < iters.
+// ---------------------------------------------------------------------------------------
+constexpr int kDecWaves = 4;
+
+template <typename T16>
+__global__ __launch_bounds__(256) void index_score_decode_mfma(
+    const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
+    const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
+    int n_q, int H, int n_kv, int iters, float scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDecWaves][64 * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int bi = blockIdx.y;
+  const int b = bi / n_q, i = bi - b * n_q;
+  const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
+  const int pos = q_pos ? q_pos[bi] : len - n_q + i;
+  const int limit = min(len, pos + 1);  // keys [0, limit) are scored, the rest are -inf
+
+  i32x4 qa[2][4];
+  float wr[2][4];
+  load_q_operand(q + (long)bi * H * 128, H, lane, qa);
+  load_w_rows(w + (long)bi * H, H, lane, wr);
+
+  const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k) + (long)b * n_kv * 256;
+  float* out = scores + (long)bi * n_kv;
+  uint8_t* my = lds[wave];
+
+  i32x4 pre[16];
+  auto issue = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = kb + 4 * j + g;
+      pre[j] = row < limit ? *reinterpret_cast<const i32x4*>(kseq + (long)row * 256 + r16 * 16)
+                           : i32x4{0, 0, 0, 0};
+    }
+  };
+  const int first = ((blockIdx.x * iters) * kDecWaves + wave) * 64;
+  if (first < limit) issue(first);
+
+  for (int it = 0; it < iters; ++it) {
+    // block-uniform exit: every wave reaches the same barriers
+    if ((blockIdx.x * iters + it) * kDecWaves * 64 >= n_kv) break;
+    const int kb = ((blockIdx.x * iters + it) * kDecWaves + wave) * 64;
+    const bool active = kb < limit;
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 4 * j + g;
+        *reinterpret_cast<i32x4*>(my + key_lds_off(r, r16)) = pre[j];
+      }
+    }
+    const int kb_next = kb + kDecWaves * 64;
+    if (it + 1 < iters && kb_next < limit) issue(kb_next);
+    __syncthreads();
+    float v = -INFINITY;
+    if (active) {
+      float sc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const i32x4 kv = *reinterpret_cast<const i32x4*>(my + key_lds_off(nt * 16 + r16, 4 * s + g));
+          a0 = Mma16<T16>::run(qa[0][s], kv, a0);
+          a1 = Mma16<T16>::run(qa[1][s], kv, a1);
+        }
+        sc[nt] = head_reduce(a0, a1, wr);
+      }
+      v = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+    }
+    const int t = kb + lane;
+    if (t < n_kv) out[t] = t < limit ? scale * v : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// prefill: grid (ceil(n_q / 8), key spans, B), 4 waves x 2 queries. Every block walks its key
+// span in 64-key tiles held in two LDS buffers; the next tile is fetched into registers while
+// the current one feeds the MFMAs.
+// ---------------------------------------------------------------------------------------
+constexpr int kPreQPW = 2;
+constexpr int kPreQB = 4 * kPreQPW;
+
+template <typename T16>
+__global__ __launch_bounds__(256) void index_score_prefill_mfma(
+    const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
+    const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
+    int n_q, int H, int n_kv, int key_span, float scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][64 * 256];
+  __shared__ int s_limit[kPreQB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int b = blockIdx.z;
+  const int q0 = blockIdx.x * kPreQB;
+  const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
+  if (tid < kPreQB) {
+    const int qi = q0 + tid;
+    int lim = 0;
+    if (qi < n_q) {
+      const int pos = q_pos ? q_pos[(long)b * n_q + qi] : len - n_q + qi;
+      lim = max(0, min(len, pos + 1));
+    }
+    s_limit[tid] = lim;
+  }
+  __syncthreads();
+  int kmax = 0;
+#pragma unroll
+  for (int j = 0; j < kPreQB; ++j) kmax = max(kmax, s_limit[j]);
+
+  const int kbeg = blockIdx.y * key_span;
+  const int kend = min(n_kv, kbeg + key_span);
+  const int kc_end = min(kend, kmax);  // keys [kbeg, kc_end) need the contraction
+
+  // queries of this wave
+  int qi[kPreQPW], lim[kPreQPW];
+  i32x4 qa[kPreQPW][2][4];
+  float wr[kPreQPW][2][4];
+#pragma unroll
+  for (int qq = 0; qq < kPreQPW; ++qq) {
+    qi[qq] = q0 + wave * kPreQPW + qq;
+    lim[qq] = s_limit[wave * kPreQPW + qq];
+    if (qi[qq] < n_q) {
+      const long bi = (long)b * n_q + qi[qq];
+      load_q_operand(q + bi * H * 128, H, lane, qa[qq]);
+      load_w_rows(w + bi * H, H, lane, wr[qq]);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qa[qq][mt][s] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wr[qq][mt][e] = 0.f;
+    }
+  }
+
+  const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k) + (long)b * n_kv * 256;
+  // tile staging: thread tid copies chunks (j * 256 + tid), j < 4, of the 64 x 16 chunk tile
+  i32x4 pre[4];
+  auto issue = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = j * 16 + (tid >> 4);
+      const int row = kb + r;
+      pre[j] = row < kc_end ? *reinterpret_cast<const i32x4*>(kseq + (long)row * 256 + (tid & 15) * 16)
+                            : i32x4{0, 0, 0, 0};
+    }
+  };
+  const int ntiles = kc_end > kbeg ? (kc_end - kbeg + 63) / 64 : 0;
+  if (ntiles > 0) issue(kbeg);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int kb = kbeg + tile * 64;
+    uint8_t* buf = lds[tile & 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = j * 16 + (tid >> 4);
+      *reinterpret_cast<i32x4*>(buf + key_lds_off(r, tid & 15)) = pre[j];
+    }
+    __syncthreads();
+    if (tile + 1 < ntiles) issue(kb + 64);
+    float sc[kPreQPW][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4 acc[kPreQPW][2];
+#pragma unroll
+      for (int qq = 0; qq < kPreQPW; ++qq) acc[qq][0] = acc[qq][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const i32x4 kv = *reinterpret_cast<const i32x4*>(buf + key_lds_off(nt * 16 + r16, 4 * s + g));
+#pragma unroll
+        for (int qq = 0; qq < kPreQPW; ++qq) {
+          acc[qq][0] = Mma16<T16>::run(qa[qq][0][s], kv, acc[qq][0]);
+          acc[qq][1] = Mma16<T16>::run(qa[qq][1][s], kv, acc[qq][1]);
+        }
+      }
+#pragma unroll
+      for (int qq = 0; qq < kPreQPW; ++qq) sc[qq][nt] = head_reduce(acc[qq][0], acc[qq][1], wr[qq]);
+    }
+    const int t = kb + lane;
+#pragma unroll
+    for (int qq = 0; qq < kPreQPW; ++qq) {
+      if (qi[qq] < n_q && t < kend) {
+        const float v = g == 0 ? sc[qq][0] : g == 1 ? sc[qq][1] : g == 2 ? sc[qq][2] : sc[qq][3];
+        scores[((long)b * n_q + qi[qq]) * n_kv + t] = t < lim[qq] ? scale * v : -INFINITY;
+      }
+    }
+  }
+  // keys of the span past every query's limit are masked for all of them
+  const int mstart = max(kbeg, kbeg + ntiles * 64);
+#pragma unroll
+  for (int qq = 0; qq < kPreQPW; ++qq) {
+    if (qi[qq] >= n_q) continue;
+    float* o = scores + ((long)b * n_q + qi[qq]) * n_kv;
+    for (int t = mstart + lane; t < kend; t += 64) o[t] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------------------
+template <typename T16>
+static hipError_t launch_mfma(const void* q, const void* k, const float* w, const int* kv_len,
+                              const int* q_pos, float* scores, int B, int n_q, int H, int n_kv,
+                              float scale, hipStream_t stream) {
+  if (n_q >= kPreQB) {
+    const int qblocks = (n_q + kPreQB - 1) / kPreQB;
+    int spans = 2048 / max(1, qblocks * B);
+    spans = max(1, min(spans, (n_kv + 255) / 256));
+    int key_span = (n_kv + spans - 1) / spans;
+    key_span = (key_span + 63) / 64 * 64;
+    spans = (n_kv + key_span - 1) / key_span;
+    dim3 grid(qblocks, spans, B);
+    hipLaunchKernelGGL(index_score_prefill_mfma<T16>, grid, dim3(256), 0, stream,
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv,
+                       key_span, scale);
+  } else {
+    const long chunks = (n_kv + 255) / 256;  // 256-key block steps per query
+    const long rows = (long)B * n_q;
+    // aim for about 1024 blocks, each wave walking up to 8 chunks of 64 keys
+    long iters = (chunks * rows) / 1024;
+    iters = iters < 1 ? 1 : (iters > 8 ? 8 : iters);
+    const long xblocks = (chunks + iters - 1) / iters;
+    dim3 grid((unsigned)xblocks, (unsigned)rows);
+    hipLaunchKernelGGL(index_score_decode_mfma<T16>, grid, dim3(256), 0, stream,
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv,
+                       (int)iters, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score(const void* q, const void* k, const float* w, const int* kv_len,
+                              const int* q_pos, float* scores, int B, int n_q, int H, int D,
+                              int n_kv, int dtype, float scale, hipStream_t stream) {
+  const bool mfma_ok = D == 128 && H <= 32 && (dtype == kBF16 || dtype == kF16);
+  if (mfma_ok) {
+    if (dtype == kBF16)
+      return launch_mfma<bf16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, stream);
+    return launch_mfma<f16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, stream);
+  }
+  dim3 grid((n_kv + 255) / 256, (unsigned)((long)B * n_q));
+  const size_t shm = (size_t)H * D * sizeof(float);
+  if (dtype == kF32)
+    hipLaunchKernelGGL(index_score_plain<float>, grid, dim3(256), shm, stream, (const float*)q,
+                       (const float*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale);
+  else if (dtype == kBF16)
+    hipLaunchKernelGGL(index_score_plain<bf16_t>, grid, dim3(256), shm, stream, (const bf16_t*)q,
+                       (const bf16_t*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale);
+  else
+    hipLaunchKernelGGL(index_score_plain<f16_t>, grid, dim3(256), shm, stream, (const f16_t*)q,
+                       (const f16_t*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,36 @@
+// Launchers of the libdsa kernels (internal; the public interface is include/dsa.h).
+// Each launcher assumes validated arguments and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace dsa {
+
+constexpr int kF32 = 0, kBF16 = 1, kF16 = 2;
+
+hipError_t launch_index_score(const void* q, const void* k, const float* w, const int* kv_len,
+                              const int* q_pos, float* scores, int B, int n_q, int H, int D,
+                              int n_kv, int dtype, float scale, hipStream_t stream);
+
+// top-k: path 0 = automatic, 1 = one workgroup per row, 2 = two-stage
+struct TopkPlan {
+  int two_stage;   // 1 when segments + candidates are used
+  int segments;    // segments per row (two-stage)
+  int seg_len;     // elements per segment (two-stage)
+  size_t ws_bytes; // workspace the plan needs
+};
+TopkPlan plan_topk(int rows, int n_kv, int top_k, int path);
+hipError_t launch_topk(const float* scores, int* idx, int rows, int n_kv, int top_k,
+                       const TopkPlan& plan, void* workspace, hipStream_t stream);
+
+// sparse MLA
+int mla_auto_splits(int B, int n_q, int top_k);
+size_t mla_workspace_bytes(int B, int n_q, int Hm, int top_k, int d_latent, int n_split);
+bool mla_mfma_supported(int Hm, int d_latent, int d_rope, int dtype);
+hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* idx,
+                             const int* kv_len, float* out, float* lse, int B, int n_q, int Hm,
+                             int n_kv, int top_k, int d_latent, int d_rope, float sm_scale,
+                             int dtype, int n_split, void* workspace, hipStream_t stream);
+
+}  // namespace dsa

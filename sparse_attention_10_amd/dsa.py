@@ -1,0 +1,175 @@
+"""ctypes binding of libdsa.so: the three DSA calls with the C names.
+
+Argument marshalling only: each function checks dtypes, shapes and contiguity of the
+torch tensors it is given, passes their device pointers and the current HIP stream to
+the C ABI (include/dsa.h) and raises DsaError on a nonzero status. Every step of the
+hot path runs in the HIP kernels of libdsa.so; there is no fallback. PyTorch only
+provides device memory and the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_F32, DSA_BF16, DSA_F16 = 0, 1, 2
+_DTYPE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.float16: DSA_F16}
+
+EXPORTED = ("dsa_index_score", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
+            "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_set_tuning",
+            "dsa_status_string", "dsa_last_error", "dsa_version")
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where} failed with status {status}: {detail}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_attention_10_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.dsa_index_score.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+    lib.dsa_index_score.restype = I
+    lib.dsa_topk_workspace_size.argtypes = [I, I, I]
+    lib.dsa_topk_workspace_size.restype = S
+    lib.dsa_topk.argtypes = [P, P, I, I, I, P, S, P]
+    lib.dsa_topk.restype = I
+    lib.dsa_sparse_mla_num_splits.argtypes = [I, I, I]
+    lib.dsa_sparse_mla_num_splits.restype = I
+    lib.dsa_sparse_mla_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.dsa_sparse_mla_workspace_size.restype = S
+    lib.dsa_sparse_mla_attn.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, S, P]
+    lib.dsa_sparse_mla_attn.restype = I
+    lib.dsa_set_tuning.argtypes = [ctypes.c_char_p, I]
+    lib.dsa_set_tuning.restype = I
+    lib.dsa_status_string.argtypes = [I]
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_last_error.argtypes = []
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_version.argtypes = []
+    lib.dsa_version.restype = I
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DsaError(status, where, lib.dsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def dsa_index_score(q: torch.Tensor, k_cache: torch.Tensor, w: torch.Tensor, scores: torch.Tensor,
+                    kv_len: Optional[torch.Tensor] = None, q_pos: Optional[torch.Tensor] = None,
+                    scale: float = 1.0, stream=None) -> torch.Tensor:
+    """q [B][n_q][H][D], k_cache [B][n_kv][D] (same dtype), w [B][n_q][H] fp32,
+    scores [B][n_q][n_kv] fp32 (output); kv_len [B] / q_pos [B][n_q] int32 or None."""
+    B, n_q, H, D = q.shape
+    n_kv = k_cache.shape[1]
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (w, "w"), (scores, "scores")):
+        _dev(t, n)
+    if tuple(k_cache.shape) != (B, n_kv, D) or tuple(w.shape) != (B, n_q, H) \
+            or tuple(scores.shape) != (B, n_q, n_kv):
+        raise ValueError("dsa_index_score: inconsistent shapes")
+    if w.dtype != torch.float32 or scores.dtype != torch.float32:
+        raise ValueError("w and scores must be float32")
+    for t, n in ((kv_len, "kv_len"), (q_pos, "q_pos")):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != torch.int32:
+                raise ValueError(f"{n} must be int32")
+    _check(lib.dsa_index_score(q.data_ptr(), k_cache.data_ptr(), w.data_ptr(), _ptr(kv_len), _ptr(q_pos),
+                               scores.data_ptr(), B, n_q, H, D, n_kv, _DTYPE[q.dtype], _DTYPE[k_cache.dtype],
+                               float(scale), _stream(stream)), "dsa_index_score")
+    return scores
+
+
+def dsa_topk_workspace_size(rows: int, n_kv: int, top_k: int) -> int:
+    return int(lib.dsa_topk_workspace_size(rows, n_kv, top_k))
+
+
+def dsa_topk(scores: torch.Tensor, idx: torch.Tensor, top_k: int,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """scores [rows][n_kv] fp32 (any leading shape, flattened), idx [rows][top_k] int32 (output)."""
+    _dev(scores, "scores")
+    _dev(idx, "idx")
+    n_kv = scores.shape[-1]
+    rows = scores.numel() // n_kv
+    if idx.numel() != rows * top_k or idx.dtype != torch.int32 or scores.dtype != torch.float32:
+        raise ValueError("dsa_topk: idx must be int32 [rows][top_k], scores float32")
+    need = dsa_topk_workspace_size(rows, n_kv, top_k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dsa_topk(scores.data_ptr(), idx.data_ptr(), rows, n_kv, top_k, _ptr(workspace), wbytes,
+                        _stream(stream)), "dsa_topk")
+    return idx
+
+
+def dsa_sparse_mla_num_splits(B: int, n_q: int, top_k: int) -> int:
+    return int(lib.dsa_sparse_mla_num_splits(B, n_q, top_k))
+
+
+def dsa_sparse_mla_workspace_size(B: int, n_q: int, Hm: int, top_k: int, d_latent: int, n_split: int) -> int:
+    return int(lib.dsa_sparse_mla_workspace_size(B, n_q, Hm, top_k, d_latent, n_split))
+
+
+def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, out: torch.Tensor,
+                        d_latent: int, sm_scale: float, lse: Optional[torch.Tensor] = None,
+                        kv_len: Optional[torch.Tensor] = None, n_split: int = 0,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q_abs [B][n_q][Hm][Dc], latent [B][n_kv][Dc] (same dtype), idx [B][n_q][top_k] int32,
+    out [B][n_q][Hm][d_latent] fp32 (output), lse [B][n_q][Hm] fp32 or None."""
+    B, n_q, Hm, Dc = q_abs.shape
+    n_kv = latent.shape[1]
+    top_k = idx.shape[-1]
+    for t, n in ((q_abs, "q_abs"), (latent, "latent"), (idx, "idx"), (out, "out")):
+        _dev(t, n)
+    if tuple(latent.shape) != (B, n_kv, Dc) or tuple(idx.shape) != (B, n_q, top_k) \
+            or tuple(out.shape) != (B, n_q, Hm, d_latent) or latent.dtype != q_abs.dtype:
+        raise ValueError("dsa_sparse_mla_attn: inconsistent shapes or dtypes")
+    if idx.dtype != torch.int32 or out.dtype != torch.float32:
+        raise ValueError("idx must be int32 and out float32")
+    if lse is not None:
+        _dev(lse, "lse")
+    if kv_len is not None:
+        _dev(kv_len, "kv_len")
+    need = dsa_sparse_mla_workspace_size(B, n_q, Hm, top_k, d_latent, n_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_abs.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dsa_sparse_mla_attn(q_abs.data_ptr(), latent.data_ptr(), idx.data_ptr(), _ptr(kv_len),
+                                   out.data_ptr(), _ptr(lse), B, n_q, Hm, n_kv, top_k, d_latent,
+                                   Dc - d_latent, float(sm_scale), _DTYPE[q_abs.dtype], int(n_split),
+                                   _ptr(workspace), wbytes, _stream(stream)), "dsa_sparse_mla_attn")
+    return out
+
+
+def dsa_set_tuning(key: str, value: int) -> None:
+    _check(lib.dsa_set_tuning(key.encode(), int(value)), "dsa_set_tuning")

@@ -1,0 +1,111 @@
+"""The whole chain (score -> top-k -> sparse MLA) on the GPU against the oracle.
+
+Small cases are compared in full. The five workloads run at full size in the launch
+configuration the bench times; sampled rows are compared with the oracle and every row is
+checked for the properties a correct selection has at any size.
+Rules: S1 scores within tolerance; S2 top-k fed the oracle's scores is bit-exact; S3 an
+end-to-end index may differ only where its oracle score is within 1e-4 relative of the
+k-th; S5 outputs within tolerance of the oracle evaluated on the GPU's own indices.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import (RTOL, assert_rowwise, binding, check_index_rule, check_topk_properties, dev, host,
+                      run_chain, to_device_inputs)
+
+pytestmark = pytest.mark.gpu
+import torch  # noqa: E402
+
+
+def _compare_rows(wl, inp, scores, idx, out, lse, sel_b, sel_i):
+    """Oracle on sequences sel_b and queries sel_i only."""
+    sl_q = np.asarray(sel_i)
+    for b in sel_b:
+        q = inp["q"][b:b + 1][:, sl_q]
+        w = inp["w"][b:b + 1][:, sl_q]
+        qp = inp["q_pos"][b:b + 1][:, sl_q]
+        S = oracle.index_score(q, inp["k"][b:b + 1], w, inp["kv_len"][b:b + 1], qp, wl.scale,
+                               wl.idx_dtype, wl.idx_dtype)
+        g_s = scores[b:b + 1][:, sl_q]
+        assert_rowwise(g_s, S, RTOL[wl.idx_dtype], f"{wl.name} scores b={b}")            # S1
+        o_idx = oracle.topk(S.reshape(-1, wl.n_kv), wl.top_k).reshape(1, len(sl_q), wl.top_k)
+        g_idx = idx[b:b + 1][:, sl_q]
+        check_index_rule(g_idx, o_idx, S, f"{wl.name} idx b={b}")                         # S3
+        o_out, o_lse = oracle.sparse_mla(inp["qa"][b:b + 1][:, sl_q], inp["latent"][b:b + 1], g_idx,
+                                         wl.sm_scale, wl.d_latent, wl.mla_dtype, inp["kv_len"][b:b + 1])
+        assert_rowwise(out[b:b + 1][:, sl_q], o_out, RTOL[wl.mla_dtype], f"{wl.name} out b={b}")  # S5
+        assert_rowwise(lse[b:b + 1][:, sl_q], o_lse, RTOL[wl.mla_dtype], f"{wl.name} lse b={b}")
+        yield b, S, o_idx
+
+
+SMALL = [
+    workloads.TINY_FP32,
+    workloads.GLM_DECODE_8K.scaled(B=2, n_kv=3000, top_k=512),
+    workloads.LONG_DECODE_128K.scaled(B=3, n_kv=5000, top_k=700),
+    workloads.CHUNKED_PREFILL_16K.scaled(n_q=40, n_kv=900, q_pos_start=860 - 40, top_k=256),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name + "_small" for w in SMALL])
+def test_chain_small(wl):
+    L = binding()
+    inp = workloads.gen_all(wl, 0)
+    d = to_device_inputs(wl, inp)
+    scores, idx, out, lse = (host(t) for t in run_chain(wl, d))
+    for b, S, o_idx in _compare_rows(wl, inp, scores, idx, out, lse, range(wl.B), range(wl.n_q)):
+        # S2: the selection kernel fed the oracle's scores returns the oracle's indices exactly
+        g = torch.empty((wl.n_q, wl.top_k), dtype=torch.int32, device="cuda")
+        L.dsa_topk(dev(np.ascontiguousarray(S.reshape(-1, wl.n_kv))), g, wl.top_k)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(g), o_idx.reshape(-1, wl.top_k))
+
+
+def _full(name, sel_b, sel_i):
+    L = binding()
+    wl = workloads.WORKLOADS[name]
+    print(f"[full-size] {name}: generating inputs", flush=True)
+    inp = workloads.gen_all(wl, 0)
+    d = to_device_inputs(wl, inp)
+    print(f"[full-size] {name}: running the chain", flush=True)
+    scores_t, idx_t, out_t, lse_t = run_chain(wl, d)
+    torch.cuda.synchronize()
+    check_topk_properties(scores_t, idx_t, wl.top_k, name)
+    assert torch.isfinite(out_t).all() and torch.isfinite(lse_t).all()
+    scores, idx, out, lse = (host(t) for t in (scores_t, idx_t, out_t, lse_t))
+    print(f"[full-size] {name}: oracle on the sample", flush=True)
+    rows = []
+    for b, S, o_idx in _compare_rows(wl, inp, scores, idx, out, lse, sel_b, sel_i):
+        rows.append((b, S, o_idx))
+    # S2 in the same launch configuration: oracle rows substituted into the full score array
+    mixed = scores.copy()
+    for b, S, _ in rows:
+        mixed[b][np.asarray(sel_i)] = S[0]
+    g = torch.empty_like(idx_t)
+    L.dsa_topk(dev(mixed), g, wl.top_k)
+    torch.cuda.synchronize()
+    g = host(g)
+    for b, S, o_idx in rows:
+        assert np.array_equal(g[b][np.asarray(sel_i)], o_idx[0]), f"{name}: S2 fails in sequence {b}"
+
+
+def test_full_glm_decode_b1_8k():
+    _full("glm_decode_b1_8k", [0], [0])
+
+
+def test_full_batched_decode_b32_32k():
+    _full("batched_decode_b32_32k", [0, 17, 31], [0])
+
+
+def test_full_long_decode_b8_128k():
+    _full("long_decode_b8_128k", [0, 5], [0])
+
+
+def test_full_chunked_prefill():
+    sel = sorted(set(range(0, 16)) | set(range(4080, 4096)) | set(range(0, 4096, 256)))
+    _full("chunked_prefill_4096_after_12288", [0], sel)
+
+
+def test_full_tiny():
+    _full("tiny_fp32_decode_256", [0], [0])
