@@ -1,6 +1,6 @@
 // C ABI of libdsa: argument validation, path selection and error reporting.
 // Every check runs on the host before any launch; a rejected call writes nothing.
-#include "../../include/dsa.h"
+#include "dsa.h"
 
 #include <atomic>
 #include <climits>

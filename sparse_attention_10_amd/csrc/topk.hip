@@ -68,21 +68,21 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 // with above(d) the count of bins > d. Result in s_sel[0] = d, s_sel[1] = above(d).
 template <int BLOCK>
 __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* s_wsum,
-                                         uint32_t* s_sel, uint32_t* total_out) {
-  const int per = nb >= BLOCK ? nb / BLOCK : 1;
+                                         uint32_t* s_sel) {
+  const int per = (nb + BLOCK - 1) / BLOCK;
   const int gi = BLOCK - 1 - (int)threadIdx.x;  // thread 0 owns the highest bins
   const int lo = gi * per;
+  const int hi = min(nb, lo + per);
   uint32_t gsum = 0;
-  if (lo < nb)
-    for (int j = 0; j < per; ++j) gsum += hist[lo + j];
+  for (int j = lo; j < hi; ++j) gsum += hist[j];
   uint32_t total;
   const uint32_t above = block_exclusive_scan<BLOCK>(gsum, s_wsum, &total);
-  if (lo < nb && above < need && need <= above + gsum) {
+  if (lo < hi && above < need && need <= above + gsum) {
     uint32_t acc = above;
-    for (int j = per - 1; j >= 0; --j) {
-      const uint32_t c = hist[lo + j];
+    for (int j = hi - 1; j >= lo; --j) {
+      const uint32_t c = hist[j];
       if (acc + c >= need) {
-        s_sel[0] = (uint32_t)(lo + j);
+        s_sel[0] = (uint32_t)j;
         s_sel[1] = acc;
         break;
       }
@@ -90,12 +90,21 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, uint32_t 
     }
   }
   __syncthreads();
-  *total_out = total;
 }
 
-// One workgroup per (segment, row). MAXN > 0 keeps the segment's keys in LDS; MAXN == 0 reads
-// them from global memory on every pass (any length).
-template <int BLOCK, int MAXN>
+__device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __clz(x) : 0; }
+
+// Streaming fallback for segments longer than the register-resident kernels take: one
+// workgroup per (segment, row); MAXN > 0 would keep keys in LDS, MAXN == 0 reads them from
+// global memory on every pass (any length).
+//
+// Radix rounds on a shrinking key range [lo, lo + span]: each round bins (key - lo) >> shift
+// into at most 4096 bins with shift = max(0, bit_width(span) - 12), picks the bin holding the
+// need-th largest key and narrows the range to it. The first range is [min, max] of the row's
+// valid keys, so the bins cover where the scores actually are (scores of one row usually sit
+// within a binade or two; fixed top-bit digits would pile them into a few bins and serialise
+// the LDS atomics). At most three rounds reach shift 0, where lo is the K-th largest key.
+template <int BLOCK, int MAXN, bool CAND>
 __global__ __launch_bounds__(BLOCK) void topk_rows(const float* __restrict__ vals, long row_stride,
                                                    int seg_len, int n_total,
                                                    const int* __restrict__ cand, int top_k,
@@ -104,8 +113,9 @@ __global__ __launch_bounds__(BLOCK) void topk_rows(const float* __restrict__ val
   constexpr int NW = BLOCK / 64;
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t s_keys[MAXN > 0 ? MAXN : 1];
+  __shared__ int s_cand[(MAXN > 0 && CAND) ? MAXN : 1];  // candidate indices (stage 2)
   __shared__ uint32_t s_wsum[NW];
-  __shared__ uint32_t s_wa[NW], s_wb[NW];
+  __shared__ uint32_t s_wa[NW], s_wb[NW], s_wc[NW];
   __shared__ uint32_t s_sel[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -122,19 +132,58 @@ __global__ __launch_bounds__(BLOCK) void topk_rows(const float* __restrict__ val
     else return score_key(vals[base + e]);
   };
 
-  // round 0: load keys (into LDS) and count bits 31..20
-  for (int j = tid; j < 4096; j += BLOCK) hist[j] = 0u;
-  __syncthreads();
-  for (int e = tid; e < n; e += BLOCK) {
-    const uint32_t kk = score_key(vals[base + e]);
-    if constexpr (MAXN > 0) s_keys[e] = kk;
-    if (kk) atomicAdd(&hist[kk >> 20], 1u);
+  // pass 0: keys into LDS; count, min and max of the valid keys. The loads of a batch are
+  // issued together (unrolled) so their memory latencies overlap.
+  constexpr int ITEMS = MAXN > 0 ? MAXN / BLOCK : 8;
+  uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
+  for (int e0 = 0; e0 < n; e0 += ITEMS * BLOCK) {
+    float v[ITEMS];
+    int ci[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int e = e0 + j * BLOCK + tid;
+      v[j] = e < n ? vals[base + e] : __int_as_float(0x7fc00000);
+      if constexpr (CAND && MAXN > 0) ci[j] = e < n ? cand[base + e] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int e = e0 + j * BLOCK + tid;
+      const uint32_t kk = score_key(v[j]);
+      if constexpr (MAXN > 0) {
+        if (e < n) s_keys[e] = kk;
+        if constexpr (CAND) {
+          if (e < n) s_cand[e] = ci[j];
+        }
+      }
+      if (kk) {
+        ++cnt;
+        kmin = min(kmin, kk);
+        kmax = max(kmax, kk);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    cnt += __shfl_xor(cnt, off, 64);
+    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, off, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, off, 64));
+  }
+  if (lane == 0) {
+    s_wa[wave] = cnt;
+    s_wb[wave] = kmin;
+    s_wc[wave] = kmax;
   }
   __syncthreads();
-
-  uint32_t n_valid;
-  // K is only known after the total; find_bin with need = top_k, then clamp.
-  find_bin<BLOCK>(hist, 4096, (uint32_t)top_k, s_wsum, s_sel, &n_valid);
+  uint32_t n_valid = 0;
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    n_valid += s_wa[w];
+    kmin = min(kmin, s_wb[w]);
+    kmax = max(kmax, s_wc[w]);
+  }
+  __syncthreads();
   const uint32_t K = min((uint32_t)top_k, n_valid);
   if (K == 0) {
     for (int p = tid; p < top_k; p += BLOCK) {
@@ -143,47 +192,29 @@ __global__ __launch_bounds__(BLOCK) void topk_rows(const float* __restrict__ val
     }
     return;
   }
+
   uint32_t need = K;
-  uint32_t prefix, mask;
-  if (K == (uint32_t)top_k) {
-    prefix = s_sel[0] << 20;
-    need -= s_sel[1];
-  } else {
-    // every valid key is taken: the threshold is the smallest valid key's bin
+  uint32_t lo = kmin, span = kmax - kmin;
+  for (int round = 0; round < 4; ++round) {
+    const int shift = max(0, bit_width(span) - 12);
+    const int nb = (int)(span >> shift) + 1;
+    for (int j = tid; j < nb; j += BLOCK) hist[j] = 0u;
     __syncthreads();
-    find_bin<BLOCK>(hist, 4096, K, s_wsum, s_sel, &n_valid);
-    prefix = s_sel[0] << 20;
+    for (int e = tid; e < n; e += BLOCK) {
+      const uint32_t kk = key_at(e);
+      const uint32_t rel = kk - lo;
+      if (kk && kk >= lo && rel <= span) atomicAdd(&hist[rel >> shift], 1u);
+    }
+    __syncthreads();
+    find_bin<BLOCK>(hist, nb, need, s_wsum, s_sel);
+    const uint32_t d = s_sel[0];
     need -= s_sel[1];
+    lo += d << shift;
+    if (shift == 0) break;
+    span = min(span - (d << shift), (1u << shift) - 1u);
+    __syncthreads();
   }
-  mask = 0xfff00000u;
-
-  // round 1: bits 19..8 of the keys in bin prefix
-  __syncthreads();
-  for (int j = tid; j < 4096; j += BLOCK) hist[j] = 0u;
-  __syncthreads();
-  for (int e = tid; e < n; e += BLOCK) {
-    const uint32_t kk = key_at(e);
-    if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> 8) & 0xfffu], 1u);
-  }
-  __syncthreads();
-  uint32_t tmp;
-  find_bin<BLOCK>(hist, 4096, need, s_wsum, s_sel, &tmp);
-  prefix |= s_sel[0] << 8;
-  need -= s_sel[1];
-  mask = 0xffffff00u;
-
-  // round 2: bits 7..0
-  __syncthreads();
-  for (int j = tid; j < 256; j += BLOCK) hist[j] = 0u;
-  __syncthreads();
-  for (int e = tid; e < n; e += BLOCK) {
-    const uint32_t kk = key_at(e);
-    if ((kk & mask) == prefix) atomicAdd(&hist[kk & 0xffu], 1u);
-  }
-  __syncthreads();
-  find_bin<BLOCK>(hist, 256, need, s_wsum, s_sel, &tmp);
-  const uint32_t T = prefix | s_sel[0];
-  need -= s_sel[1];  // keys == T still to take, lowest index first (>= 1)
+  const uint32_t T = lo;  // the K-th largest key; `need` keys equal to T are taken (>= 1)
 
   // ordered compaction: wave w owns the 64-wide steps [w * spw, (w + 1) * spw)
   const int steps = (n + 63) / 64;
@@ -219,7 +250,12 @@ __global__ __launch_bounds__(BLOCK) void topk_rows(const float* __restrict__ val
     const uint64_t bsel = __ballot(sel);
     const uint32_t p = run_sel + mbcnt(bsel);
     if (sel && p < K) {
-      o_idx[p] = cand ? cand[base + e] : idx_base + e;
+      int ix = idx_base + e;
+      if constexpr (CAND) {
+        if constexpr (MAXN > 0) ix = s_cand[e];
+        else ix = cand[base + e];
+      }
+      o_idx[p] = ix;
       if (o_val) o_val[p] = key_value(kk);
     }
     run_eq += __popcll(beq);
@@ -232,9 +268,165 @@ __global__ __launch_bounds__(BLOCK) void topk_rows(const float* __restrict__ val
 }
 
 // ---------------------------------------------------------------------------------------
+// Register-resident kernel: thread t holds elements j * BLOCK + t (j < ITEMS) of its segment,
+// so a wave's lanes hold 64 consecutive elements for each j ("chunk" j * NW + wave, chunks in
+// ascending element order). Histogram rounds read keys from registers and issue their LDS
+// atomics back to back; 8192 bins usually finish in two rounds. The ordered compaction
+// counts every chunk's keys > T and == T with ballots, turns the counts into output offsets
+// with two block scans, and writes each chunk with ballot + mbcnt.
+// ---------------------------------------------------------------------------------------
+template <int BLOCK, int ITEMS, bool CAND>
+__global__ __launch_bounds__(BLOCK) void topk_rows_reg(const float* __restrict__ vals, long row_stride,
+                                                       int seg_len, int n_total,
+                                                       const int* __restrict__ cand, int top_k,
+                                                       int* __restrict__ out_idx,
+                                                       float* __restrict__ out_val) {
+  constexpr int NW = BLOCK / 64;
+  constexpr int NB = 8192;
+  constexpr int NCH = ITEMS * NW;  // chunks of 64
+  static_assert(NCH <= BLOCK, "one thread per chunk in the offset scans");
+  __shared__ uint32_t hist[NB];
+  __shared__ uint32_t s_wsum[NW];
+  __shared__ uint32_t s_wa[NW], s_wb[NW], s_wc[NW];
+  __shared__ uint32_t s_gt[NCH], s_eq[NCH];
+  __shared__ uint32_t s_sel[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.y, seg = blockIdx.x;
+  const long base = (long)row * row_stride + (long)seg * seg_len;
+  const int n = min(seg_len, n_total - seg * seg_len);
+  const int idx_base = seg * seg_len;
+  const long obase = ((long)row * gridDim.x + seg) * top_k;
+  int* o_idx = out_idx + obase;
+  float* o_val = out_val ? out_val + obase : nullptr;
+
+  uint32_t key[ITEMS];
+  int ci[ITEMS];
+  {
+    float v[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int e = j * BLOCK + tid;
+      v[j] = e < n ? vals[base + e] : __int_as_float(0x7fc00000);
+      if constexpr (CAND) ci[j] = e < n ? cand[base + e] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) key[j] = score_key(v[j]);
+  }
+  uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    if (key[j]) {
+      ++cnt;
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    cnt += __shfl_xor(cnt, off, 64);
+    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, off, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, off, 64));
+  }
+  if (lane == 0) {
+    s_wa[wave] = cnt;
+    s_wb[wave] = kmin;
+    s_wc[wave] = kmax;
+  }
+  __syncthreads();
+  uint32_t n_valid = 0;
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    n_valid += s_wa[w];
+    kmin = min(kmin, s_wb[w]);
+    kmax = max(kmax, s_wc[w]);
+  }
+  const uint32_t K = min((uint32_t)top_k, n_valid);
+  if (K == 0) {
+    for (int p = tid; p < top_k; p += BLOCK) {
+      o_idx[p] = -1;
+      if (o_val) o_val[p] = -INFINITY;
+    }
+    return;
+  }
+
+  // radix rounds on the shrinking key range [lo, lo + span]
+  uint32_t need = K;
+  uint32_t lo = kmin, span = kmax - kmin;
+  for (int round = 0; round < 4; ++round) {
+    const int shift = max(0, bit_width(span) - 13);
+    const int nb = (int)(span >> shift) + 1;
+    for (int j = tid; j < nb; j += BLOCK) hist[j] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const uint32_t rel = key[j] - lo;
+      if (key[j] && key[j] >= lo && rel <= span) atomicAdd(&hist[rel >> shift], 1u);
+    }
+    __syncthreads();
+    find_bin<BLOCK>(hist, nb, need, s_wsum, s_sel);
+    const uint32_t d = s_sel[0];
+    need -= s_sel[1];
+    lo += d << shift;
+    if (shift == 0) break;
+    span = min(span - (d << shift), (1u << shift) - 1u);
+    __syncthreads();
+  }
+  const uint32_t T = lo;  // the K-th largest key; `need` keys equal to T are taken (>= 1)
+
+  // per-chunk counts
+  uint64_t bgt[ITEMS], beq[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    bgt[j] = __ballot(key[j] > T);
+    beq[j] = __ballot(key[j] == T);
+    if (lane == 0) {
+      s_gt[j * NW + wave] = (uint32_t)__popcll(bgt[j]);
+      s_eq[j * NW + wave] = (uint32_t)__popcll(beq[j]);
+    }
+  }
+  __syncthreads();
+  // chunk c = tid: keys == T before it, then output offset before it
+  const uint32_t my_eq = tid < NCH ? s_eq[tid] : 0u;
+  const uint32_t my_gt = tid < NCH ? s_gt[tid] : 0u;
+  uint32_t tot;
+  const uint32_t eq_before = block_exclusive_scan<BLOCK>(my_eq, s_wsum, &tot);
+  const uint32_t take = need > eq_before ? min(my_eq, need - eq_before) : 0u;
+  const uint32_t sel_before = block_exclusive_scan<BLOCK>(my_gt + take, s_wsum, &tot);
+  if (tid < NCH) {
+    s_eq[tid] = eq_before;
+    s_gt[tid] = sel_before;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int c = j * NW + wave;
+    const uint32_t eqb = s_eq[c], selb = s_gt[c];
+    const bool gt = key[j] > T;
+    const bool eq = key[j] == T;
+    const bool sel = gt || (eq && eqb + mbcnt(beq[j]) < need);
+    const uint64_t bsel = __ballot(sel);
+    const uint32_t p = selb + mbcnt(bsel);
+    if (sel && p < K) {
+      int ix = idx_base + j * BLOCK + tid;
+      if constexpr (CAND) ix = ci[j];
+      o_idx[p] = ix;
+      if (o_val) o_val[p] = key_value(key[j]);
+    }
+  }
+  for (int p = (int)K + tid; p < top_k; p += BLOCK) {
+    o_idx[p] = -1;
+    if (o_val) o_val[p] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-static constexpr int kResidentMax = 32768;
+static constexpr int kResidentMax = 32768;  // longest segment held in registers by one workgroup
+static constexpr int kCandMax = 32768;      // candidates of one row in the second stage
 static constexpr int kSegTarget = 8192;
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -243,16 +435,18 @@ TopkPlan plan_topk(int rows, int n_kv, int top_k, int path) {
   TopkPlan p{0, 1, n_kv, 0};
   // two-stage feasibility: segments shorter than the row, each keeps top_k candidates, and
   // the candidates of a row fit one LDS-resident stage-2 pass
+  // segments of about kSegTarget entries, but no more candidates than one LDS-resident
+  // stage-2 pass with indices holds
   int S = (n_kv + kSegTarget - 1) / kSegTarget;
+  if (S > kCandMax / top_k) S = kCandMax / top_k;
   if (S < 2) S = 2;
   int seg = (n_kv + S - 1) / S;
   seg = (seg + 63) / 64 * 64;
   S = (n_kv + seg - 1) / seg;
-  const bool feasible = S >= 2 && (long)S * top_k <= kResidentMax && seg <= kResidentMax &&
-                        seg >= 2 * top_k;
+  const bool feasible = S >= 2 && (long)S * top_k <= kCandMax && seg <= kResidentMax && seg >= 2 * top_k;
   bool use = false;
   if (path == 2) use = feasible;
-  else if (path == 0) use = feasible && (n_kv > kResidentMax || (rows < 128 && n_kv >= 4 * top_k));
+  else if (path == 0) use = feasible && n_kv > kResidentMax;  // one pass is faster when it fits
   if (feasible) {
     const size_t cand = (size_t)rows * S * top_k;
     p.ws_bytes = align256(cand * sizeof(int)) + align256(cand * sizeof(float));
@@ -265,22 +459,30 @@ TopkPlan plan_topk(int rows, int n_kv, int top_k, int path) {
   return p;
 }
 
-static void launch_rows(const float* vals, long row_stride, int seg_len, int n_total, int S, int rows,
-                        const int* cand, int top_k, int* out_idx, float* out_val, hipStream_t stream) {
+template <bool CAND>
+static void launch_rows_t(const float* vals, long row_stride, int seg_len, int n_total, int S, int rows,
+                          const int* cand, int top_k, int* out_idx, float* out_val, hipStream_t stream) {
   const int n = seg_len;  // longest segment
   dim3 grid(S, rows);
-  if (n <= 2048)
-    hipLaunchKernelGGL((topk_rows<256, 2048>), grid, dim3(256), 0, stream, vals, row_stride, seg_len,
-                       n_total, cand, top_k, out_idx, out_val);
-  else if (n <= 8192)
-    hipLaunchKernelGGL((topk_rows<512, 8192>), grid, dim3(512), 0, stream, vals, row_stride, seg_len,
-                       n_total, cand, top_k, out_idx, out_val);
-  else if (n <= kResidentMax)
-    hipLaunchKernelGGL((topk_rows<1024, kResidentMax>), grid, dim3(1024), 0, stream, vals, row_stride,
-                       seg_len, n_total, cand, top_k, out_idx, out_val);
+#define DSA_TOPK_REG(BL, IT)                                                                      \
+  hipLaunchKernelGGL((topk_rows_reg<BL, IT, CAND>), grid, dim3(BL), 0, stream, vals, row_stride, \
+                     seg_len, n_total, cand, top_k, out_idx, out_val)
+  if (n <= 256 * 8) DSA_TOPK_REG(256, 8);
+  else if (n <= 512 * 16) DSA_TOPK_REG(512, 16);
+  else if (n <= 512 * 32) DSA_TOPK_REG(512, 32);
+  else if (n <= 1024 * 32) DSA_TOPK_REG(1024, 32);
   else
-    hipLaunchKernelGGL((topk_rows<1024, 0>), grid, dim3(1024), 0, stream, vals, row_stride, seg_len,
+    hipLaunchKernelGGL((topk_rows<1024, 0, CAND>), grid, dim3(1024), 0, stream, vals, row_stride, seg_len,
                        n_total, cand, top_k, out_idx, out_val);
+#undef DSA_TOPK_REG
+}
+
+static void launch_rows(const float* vals, long row_stride, int seg_len, int n_total, int S, int rows,
+                        const int* cand, int top_k, int* out_idx, float* out_val, hipStream_t stream) {
+  if (cand)
+    launch_rows_t<true>(vals, row_stride, seg_len, n_total, S, rows, cand, top_k, out_idx, out_val, stream);
+  else
+    launch_rows_t<false>(vals, row_stride, seg_len, n_total, S, rows, cand, top_k, out_idx, out_val, stream);
 }
 
 hipError_t launch_topk(const float* scores, int* idx, int rows, int n_kv, int top_k,
