@@ -66,6 +66,11 @@ int dsa_set_tuning(const char* key, int value) {
     g_topk_path.store(value);
     return ok();
   }
+  if (std::strcmp(key, "score_chunks_per_wave") == 0) {
+    if (value < 0 || value > 64) return fail(DSA_ERR_SHAPE, "score_chunks_per_wave must be 0..64 (got %d)", value);
+    dsa::g_score_cpw = value;
+    return ok();
+  }
   return fail(DSA_ERR_SHAPE, "dsa_set_tuning: unknown key '%s'", key);
 }
 

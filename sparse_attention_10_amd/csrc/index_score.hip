@@ -18,6 +18,8 @@
 
 namespace dsa {
 
+int g_score_cpw = 0;  // 64-key chunks per wave of the decode kernel (0 automatic)
+
 // ---------------------------------------------------------------------------------------
 // plain kernel
 // ---------------------------------------------------------------------------------------
@@ -120,12 +122,15 @@ __device__ __forceinline__ float head_reduce(const f32x4& a0, const f32x4& a1, c
 
 // ---------------------------------------------------------------------------------------
 // decode: grid (key blocks, B * n_q), 4 waves; wave w of block x handles the 64-key chunks
-// ((x * iters + it) * 4 + w) for it < iters.
+// ((x * iters + it) * 4 + w) for it < iters. Each wave keeps two chunks of loads in flight
+// (statically indexed ping-pong registers, so the compiler's vmcnt waits count exactly): the
+// loads are unconditional, with rows past the scored range clamped to a valid row and the
+// boundary chunk zeroed afterwards.
 // ---------------------------------------------------------------------------------------
 constexpr int kDecWaves = 4;
 
 template <typename T16>
-__global__ __launch_bounds__(256) void index_score_decode_mfma(
+__global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
     int n_q, int H, int n_kv, int iters, float scale) {
@@ -138,44 +143,51 @@ __global__ __launch_bounds__(256) void index_score_decode_mfma(
   const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
   const int pos = q_pos ? q_pos[bi] : len - n_q + i;
   const int limit = min(len, pos + 1);  // keys [0, limit) are scored, the rest are -inf
-
-  i32x4 qa[2][4];
-  float wr[2][4];
-  load_q_operand(q + (long)bi * H * 128, H, lane, qa);
-  load_w_rows(w + (long)bi * H, H, lane, wr);
-
   const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k) + (long)b * n_kv * 256;
   float* out = scores + (long)bi * n_kv;
   uint8_t* my = lds[wave];
 
-  i32x4 pre[16];
-  auto issue = [&](int kb) {
+  // chunk it of this wave starts at key kb(it)
+  auto kb_of = [&](int it) { return ((blockIdx.x * iters + it) * kDecWaves + wave) * 64; };
+  auto fetch = [&](int kb, i32x4(&pre)[16]) {
+    if (kb >= limit) return;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int row = kb + 4 * j + g;
-      pre[j] = row < limit ? *reinterpret_cast<const i32x4*>(kseq + (long)row * 256 + r16 * 16)
-                           : i32x4{0, 0, 0, 0};
+      const int row = min(kb + 4 * j + g, limit - 1);
+      pre[j] = *reinterpret_cast<const i32x4*>(kseq + (long)row * 256 + r16 * 16);
     }
   };
-  const int first = ((blockIdx.x * iters) * kDecWaves + wave) * 64;
-  if (first < limit) issue(first);
-
-  for (int it = 0; it < iters; ++it) {
-    // block-uniform exit: every wave reaches the same barriers
-    if ((blockIdx.x * iters + it) * kDecWaves * 64 >= n_kv) break;
-    const int kb = ((blockIdx.x * iters + it) * kDecWaves + wave) * 64;
+  auto step = [&](int it, i32x4(&pre)[16], bool has_next2) {
+    const int kb = kb_of(it);
     const bool active = kb < limit;
     __syncthreads();
     if (active) {
+      if (kb + 64 > limit) {  // boundary chunk: rows past the scored range are zero
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (kb + 4 * j + g >= limit) pre[j] = i32x4{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = 4 * j + g;
         *reinterpret_cast<i32x4*>(my + key_lds_off(r, r16)) = pre[j];
       }
     }
-    const int kb_next = kb + kDecWaves * 64;
-    if (it + 1 < iters && kb_next < limit) issue(kb_next);
+    if (has_next2) fetch(kb_of(it + 2), pre);  // two chunks ahead, into the freed registers
     __syncthreads();
+    return active;
+  };
+
+  i32x4 qa[2][4];
+  float wr[2][4];
+  i32x4 pa[16], pb[16];
+  fetch(kb_of(0), pa);
+  if (iters > 1) fetch(kb_of(1), pb);
+  load_q_operand(q + (long)bi * H * 128, H, lane, qa);
+  load_w_rows(w + (long)bi * H, H, lane, wr);
+
+  auto compute = [&](int it, bool active) {
+    const int kb = kb_of(it);
     float v = -INFINITY;
     if (active) {
       float sc[4];
@@ -194,6 +206,16 @@ __global__ __launch_bounds__(256) void index_score_decode_mfma(
     }
     const int t = kb + lane;
     if (t < n_kv) out[t] = t < limit ? scale * v : -INFINITY;
+  };
+
+  for (int it = 0; it < iters; it += 2) {
+    // block-uniform exit: every wave reaches the same barriers
+    if ((blockIdx.x * iters + it) * kDecWaves * 64 >= n_kv) break;
+    const bool a0 = step(it, pa, it + 2 < iters);
+    compute(it, a0);
+    if (it + 1 >= iters || (blockIdx.x * iters + it + 1) * kDecWaves * 64 >= n_kv) break;
+    const bool a1 = step(it + 1, pb, it + 3 < iters);
+    compute(it + 1, a1);
   }
 }
 
@@ -343,9 +365,10 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
   } else {
     const long chunks = (n_kv + 255) / 256;  // 256-key block steps per query
     const long rows = (long)B * n_q;
-    // aim for about 1024 blocks, each wave walking up to 8 chunks of 64 keys
-    long iters = (chunks * rows) / 1024;
-    iters = iters < 1 ? 1 : (iters > 8 ? 8 : iters);
+    // about 2048 blocks: short-lived waves of two chunks each measured fastest (more
+    // independent streams in flight than a few long-lived waves)
+    long iters = g_score_cpw > 0 ? g_score_cpw : (chunks * rows) / 2048;
+    iters = iters < 1 ? 1 : (iters > 64 ? 64 : iters);
     const long xblocks = (chunks + iters - 1) / iters;
     dim3 grid((unsigned)xblocks, (unsigned)rows);
     hipLaunchKernelGGL(index_score_decode_mfma<T16>, grid, dim3(256), 0, stream,

@@ -137,6 +137,10 @@ def test_tuning_switch(lib):
     assert lib.dsa_set_tuning(b"topk_path", 2) == OK
     assert lib.dsa_set_tuning(b"topk_path", 0) == OK
     assert lib.dsa_set_tuning(b"topk_path", 5) == E_SHAPE
+    assert lib.dsa_set_tuning(b"score_chunks_per_wave", 4) == OK
+    assert lib.dsa_set_tuning(b"score_chunks_per_wave", 0) == OK
+    assert lib.dsa_set_tuning(b"score_chunks_per_wave", 65) == E_SHAPE
+    assert lib.dsa_set_tuning(b"score_chunks_per_wave", -1) == E_SHAPE
     assert lib.dsa_set_tuning(b"no_such_key", 1) == E_SHAPE
     assert lib.dsa_set_tuning(None, 1) == E_NULL
 
