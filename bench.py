@@ -81,6 +81,45 @@ def load_traffic(wl_name):
     return t.get("bytes_per_launch")
 
 
+def _counter_rows(path, counter):
+    """(dispatch id, kernel name, value in KiB) of one counter from a counter_collection.csv."""
+    import csv
+    rows = []
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def write_traffic(wl_name, fetch_csv, write_csv, copy_mib):
+    """HBM bytes per launch of the score kernel: its mean FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each divided by the factor the same counter reads for the calibration copy
+    (the last three copy-kernel dispatches, copy_mib MiB read and written)."""
+    if copy_mib <= 0:
+        sys.exit("--traffic-from needs --copy-calibration-mib (the size the counted runs copied)")
+    copy_bytes = copy_mib * 1024 * 1024
+    out = {"workload": wl_name, "kernel_sha": kernel_source_hash(), "copy_bytes": copy_bytes}
+    total = 0.0
+    for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _counter_rows(path, counter)
+        copies = [v for _, name, v in rows if "copyBuffer" in name][-3:]
+        score = [v for _, name, v in rows if "index_score_" in name]
+        if len(copies) < 3 or not score:
+            sys.exit(f"{path}: no calibration copies or score dispatches with {counter}")
+        factor = sum(copies) / len(copies) * 1024 / copy_bytes
+        per = sum(score) / len(score) * 1024 / factor
+        out[tag] = {"counter": counter, "copy_kib": sum(copies) / len(copies), "factor": round(factor, 4),
+                    "kernel_kib": sum(score) / len(score), "dispatches": len(score), "bytes_per_launch": round(per)}
+        total += per
+    out["bytes_per_launch"] = round(total)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
 def cpu_baseline(wl, inp, seconds_target=15.0):
     """The oracle chain on whole sequences of the workload until ~seconds_target of work."""
     import numpy as np
@@ -122,7 +161,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the bench, run 3 device-to-device copies of this many MiB (the known-size "
+                         "copy that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="read two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE run, WRITE_SIZE "
+                         "run of this script with --copy-calibration-mib) and write the score kernel's "
+                         "HBM bytes per launch to profiles/traffic_index_score.json; no GPU work")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], args.copy_calibration_mib)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every GPU box here has one GPU and this hot path is run "
@@ -284,6 +333,16 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+    if args.copy_calibration_mib > 0:
+        del q, k, w, qa, lat, scores, idx, out, lse, ws_t, ws_m
+        n = args.copy_calibration_mib * 1024 * 1024
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration: 3 copies of {args.copy_calibration_mib} MiB", file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":
