@@ -128,7 +128,10 @@ int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* id
 /*
  * Tuning switches. They choose between kernels that compute identical results and
  * change only speed. key "topk_path": 0 = automatic, 1 = one workgroup per row,
- * 2 = two-stage (segments, then candidates). key "score_chunks_per_wave": 64-key chunks
+ * 2 = two-stage (segments, then candidates), 3 = filtered (a sampled threshold picks
+ * candidates in many workgroups per row, one workgroup per row selects among them, with a
+ * whole-row select when the candidates cannot hold the answer). A path the shape does not
+ * allow falls back to the automatic choice. key "score_chunks_per_wave": 64-key chunks
  * each wave of the 16-bit decode scoring kernel walks (0 = automatic, else 1..64). Returns DSA_OK,
  * or DSA_ERR_SHAPE for an unknown key or value. Process-wide; set it before launching work.
  */

@@ -62,7 +62,7 @@ const char* dsa_last_error(void) { return g_err; }
 int dsa_set_tuning(const char* key, int value) {
   if (!key) return fail(DSA_ERR_NULL, "dsa_set_tuning: key is NULL");
   if (std::strcmp(key, "topk_path") == 0) {
-    if (value < 0 || value > 2) return fail(DSA_ERR_SHAPE, "topk_path must be 0, 1 or 2 (got %d)", value);
+    if (value < 0 || value > 3) return fail(DSA_ERR_SHAPE, "topk_path must be 0..3 (got %d)", value);
     g_topk_path.store(value);
     return ok();
   }
@@ -102,7 +102,7 @@ int dsa_index_score(const void* q, const void* k_cache, const float* w, const in
 
 size_t dsa_topk_workspace_size(int rows, int n_kv, int top_k) {
   if (rows < 1 || n_kv < 1 || top_k < 1) return 0;
-  return dsa::plan_topk(rows, n_kv, top_k, 2).ws_bytes;
+  return dsa::plan_topk(rows, n_kv, top_k, 0).ws_bytes;
 }
 
 int dsa_topk(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, void* workspace,

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace dsa {
 
@@ -14,12 +15,13 @@ hipError_t launch_index_score(const void* q, const void* k, const float* w, cons
                               const int* q_pos, float* scores, int B, int n_q, int H, int D,
                               int n_kv, int dtype, float scale, hipStream_t stream);
 
-// top-k: path 0 = automatic, 1 = one workgroup per row, 2 = two-stage
+// top-k: path 0 = automatic, 1 = one workgroup per row, 2 = two-stage, 3 = filtered
 struct TopkPlan {
-  int two_stage;   // 1 when segments + candidates are used
-  int segments;    // segments per row (two-stage)
-  int seg_len;     // elements per segment (two-stage)
-  size_t ws_bytes; // workspace the plan needs
+  int kind;        // 0 one workgroup per row, 1 two-stage (segments + candidates), 2 filtered
+  int segments;    // segments per row (two-stage, filtered)
+  int seg_len;     // elements per segment (two-stage, filtered)
+  uint32_t need;   // filtered: sampled keys the threshold must cover
+  size_t ws_bytes; // workspace any path of this shape may use
 };
 TopkPlan plan_topk(int rows, int n_kv, int top_k, int path);
 hipError_t launch_topk(const float* scores, int* idx, int rows, int n_kv, int top_k,

@@ -136,7 +136,8 @@ def test_sparse_mla_workspace_size(lib):
 def test_tuning_switch(lib):
     assert lib.dsa_set_tuning(b"topk_path", 2) == OK
     assert lib.dsa_set_tuning(b"topk_path", 0) == OK
-    assert lib.dsa_set_tuning(b"topk_path", 5) == E_SHAPE
+    assert lib.dsa_set_tuning(b"topk_path", 3) == OK
+    assert lib.dsa_set_tuning(b"topk_path", 4) == E_SHAPE
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", 4) == OK
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", 0) == OK
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", 65) == E_SHAPE

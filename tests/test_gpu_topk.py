@@ -1,5 +1,6 @@
 """dsa_topk on the GPU: bit-exact against the oracle when fed the same fp32 scores, on
-both paths (one workgroup per row, two-stage), with ties, signed zeros, NaN and -inf."""
+every path (one workgroup per row, two-stage, filtered), with ties, signed zeros, NaN and
+-inf, and inputs that push the filtered path into its whole-row fallback."""
 import numpy as np
 import pytest
 
@@ -11,7 +12,7 @@ pytestmark = pytest.mark.gpu
 import torch  # noqa: E402
 
 
-@pytest.fixture(params=[1, 2], ids=["one_pass", "two_stage"])
+@pytest.fixture(params=[1, 2, 3], ids=["one_pass", "two_stage", "filtered"])
 def path(request):
     L = binding()
     L.dsa_set_tuning("topk_path", request.param)
@@ -71,13 +72,13 @@ def test_paths_agree_bitwise():
     L = binding()
     s = workloads.random_scores(8, 131072, seed=14, tie_frac=0.01)
     outs = []
-    for p in (1, 2, 0):
+    for p in (1, 2, 3, 0):
         L.dsa_set_tuning("topk_path", p)
         idx = torch.empty((8, 2048), dtype=torch.int32, device="cuda")
         L.dsa_topk(dev(s), idx, 2048)
         outs.append(host(idx))
     L.dsa_set_tuning("topk_path", 0)
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
     assert np.array_equal(outs[0], oracle.topk(s, 2048))
 
 
@@ -86,3 +87,52 @@ def test_oracle_scores_of_a_workload(path):
     inp = workloads.gen_all(wl, 3, parts=("q", "k", "w"))
     S = oracle.index_score(inp["q"], inp["k"], inp["w"], None, None, 1.0, wl.idx_dtype, wl.idx_dtype)
     _run(S.reshape(-1, wl.n_kv), wl.top_k)
+
+
+# The filtered path takes its threshold from the entries at positions floor(i * n / 4096).
+def _sampled(n):
+    m = min(n, 4096)
+    return (np.arange(m, dtype=np.int64) * n) // m
+
+
+def test_filtered_sample_overestimates():
+    """Sampled positions hold the largest scores, so the sample's threshold admits fewer than
+    top_k entries of the row: the selection must come from the whole-row fallback."""
+    L = binding()
+    L.dsa_set_tuning("topk_path", 3)
+    try:
+        for n, top_k in [(32768, 2048), (131072, 2048), (20000, 1000)]:
+            s = workloads.random_scores(4, n, seed=n)
+            s[:, _sampled(n)] += 100.0
+            _run(s, top_k)
+    finally:
+        L.dsa_set_tuning("topk_path", 0)
+
+
+def test_filtered_sample_sees_no_valid():
+    """Only unsampled positions are valid: the threshold falls to "every valid key", which is
+    more candidates than one select holds, so the fallback runs; with few valid keys the
+    candidates fit and the filtered select itself answers."""
+    L = binding()
+    L.dsa_set_tuning("topk_path", 3)
+    try:
+        n = 32768
+        s = workloads.random_scores(3, n, seed=21, tie_frac=0.05)
+        s[:, _sampled(n)] = -np.inf
+        s[1, :] = -np.inf
+        s[1, 5::97] = 1.5  # 338 valid, all tied
+        s[2, 8000:] = np.nan
+        _run(s, 2048)
+    finally:
+        L.dsa_set_tuning("topk_path", 0)
+
+
+@pytest.mark.parametrize("rows,n,top_k", [(1, 8192, 2048), (32, 32768, 2048), (8, 131072, 2048),
+                                          (3, 4097, 64), (200, 12000, 4096), (2, 2047, 100)])
+def test_filtered_shapes(rows, n, top_k):
+    L = binding()
+    L.dsa_set_tuning("topk_path", 3)
+    try:
+        _run(workloads.random_scores(rows, n, seed=rows * n + top_k, tie_frac=0.01), top_k)
+    finally:
+        L.dsa_set_tuning("topk_path", 0)
