@@ -594,9 +594,9 @@ __global__ __launch_bounds__(BLOCK) void topk_rows_reg(const float* __restrict__
 // Stage 1 (topk_filter): workgroup (row, seg) takes a fixed sample of its row and picks a
 // key G that at least `need` sampled valid keys reach: the lower edge of the histogram bin
 // holding the need-th largest sampled key (G = 1, i.e. every valid key, when the sample holds
-// no more than `need` valid keys). The sample is the whole row up to 4096 entries, else 1024
+// no more than `need` valid keys). The sample is the whole row up to 2048 entries, else 512
 // runs of 4 consecutive entries spread evenly over the row (runs keep the reads to at most
-// 1024 cache lines whatever the row length). `need` exceeds the sample's expected share of
+// 512 cache lines whatever the row length). `need` exceeds the sample's expected share of
 // the top-k by several standard deviations, so the row usually holds at least top_k keys
 // >= G. Every workgroup of a row computes the same G from the same sample. It then copies its
 // segment's keys >= G with their indices, in index order, to the segment's slot of the
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(BLOCK) void topk_rows_reg(const float* __restrict__
 // unique result.
 // ---------------------------------------------------------------------------------------
 constexpr int kFilterBlock = 256, kFilterItems = 8, kFilterSeg = kFilterBlock * kFilterItems;
-constexpr int kFilterSample = 4096, kFilterRun = 4;
+constexpr int kFilterSample = 2048, kFilterRun = 4;
 constexpr int kSelectBlock = 1024, kSelectItems = 8, kFilterCap = kSelectBlock * kSelectItems;
 constexpr int kFilterMaxSeg = kSelectBlock;
 constexpr int kFilterMaxRows = 256;

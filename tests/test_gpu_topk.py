@@ -89,10 +89,13 @@ def test_oracle_scores_of_a_workload(path):
     _run(S.reshape(-1, wl.n_kv), wl.top_k)
 
 
-# The filtered path takes its threshold from the entries at positions floor(i * n / 4096).
+# The filtered path takes its threshold from a sample of the row: the whole row up to 2048
+# entries, else 512 runs of 4 consecutive entries starting at floor(r * (n - 4) / 511).
 def _sampled(n):
-    m = min(n, 4096)
-    return (np.arange(m, dtype=np.int64) * n) // m
+    if n <= 2048:
+        return np.arange(n)
+    r = np.arange(512, dtype=np.int64)
+    return ((r * (n - 4)) // 511)[:, None] + np.arange(4)[None, :]
 
 
 def test_filtered_sample_overestimates():
