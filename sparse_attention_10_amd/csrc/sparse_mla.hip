@@ -10,12 +10,11 @@
 // softmax, ds4 "Hy3 (295B)" PR, online-softmax commit); a merge pass combines the parts:
 //   M = max_s m_s,  L = sum_s e^{m_s - M} l_s,  out = sum_s e^{m_s - M} o_s / L,  lse = M + ln L.
 //
-// MFMA kernel (bf16, 16..64 heads, 512 + {0, 64} dims): 32 selected rows at a time are
-// gathered with coalesced 16-byte loads into LDS (row-major, padded rows). Each wave owns 16
-// heads. Scores are computed transposed, S^T = C Q^T, so a lane owns one head and eight rows:
-// the softmax statistics of a head live in one lane column and the probabilities are already
-// in the B-operand layout of the value product O^T = V^T P^T. V^T is read from the row-major
-// tile with ds_read_b64_tr_b16 (gfx950 transpose read), so no second copy is made.
+// MFMA kernel (bf16, 16..64 heads, 512 + {0, 64} dims): 16 selected rows at a time are
+// gathered into LDS by DMA. Score waves compute S^T = C Q^T for 16 heads each, so a lane owns
+// one head and four rows and the softmax needs no cross-lane work in the common case; value
+// waves accumulate O^T = V^T P^T for 128 output dims of all heads, reading V^T from the
+// row-major tile with ds_read_b64_tr_b16 (gfx950 transpose read), so no second copy is made.
 #include "common.h"
 #include "kernels.h"
 
@@ -160,7 +159,6 @@ __global__ __launch_bounds__(256) void sparse_mla_plain(
 // ---------------------------------------------------------------------------------------
 // MFMA kernel
 // ---------------------------------------------------------------------------------------
-constexpr int kMlaRows = 32;          // rows per LDS tile
 constexpr int kMlaMaxChunk = 2048;    // index slots per workgroup (LDS index buffer)
 
 __device__ __forceinline__ f32x4 mma_bf16(i32x4 a, i32x4 b, f32x4 c) {
@@ -168,14 +166,12 @@ __device__ __forceinline__ f32x4 mma_bf16(i32x4 a, i32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
 // ds_read_b64_tr_b16: within each 16-lane row, lane i receives element i%4 of the 8-byte
 // loads of lanes 4j + i/4 (j = 0..3), i.e. a 4x4 transpose of 16-bit values per lane quad.
 // Issued through inline asm: the compiler treats the intrinsic as possibly aliasing every
 // in-flight LDS DMA and would wait for all of them (draining the tile ring) before each read.
-// The caller orders the reads after the tile's barrier and consumes the results only after
-// tr_wait(), which ties the destination registers to an s_waitcnt lgkmcnt(0).
+// The caller orders the reads after the tile's barrier and consumes the results only after an
+// s_waitcnt lgkmcnt that has the destination registers tied to it.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
 }
@@ -191,6 +187,34 @@ __device__ __forceinline__ i16x4 ds_read_tr16_off(uint32_t base) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF) : "memory");
   return v;
 }
+// s_waitcnt lgkmcnt(0) with the destinations of earlier LDS reads tied to it, so that they
+// cannot be used before it (the reads are asm, invisible to the compiler's own waits).
+__device__ __forceinline__ void tie4(i32x4& a, i32x4& b, i32x4& c, i32x4& d) {
+  asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+template <int N>
+__device__ __forceinline__ void tie_rest(i32x4 (&a)[N]) {
+  static_assert(N >= 4 && N <= 12, "register groups");
+  if constexpr (N >= 8) tie4(a[4], a[5], a[6], a[7]);
+  if constexpr (N >= 12) tie4(a[8], a[9], a[10], a[11]);
+  if constexpr (N % 4 == 1) asm volatile("" : "+v"(a[N - 1]));
+  if constexpr (N % 4 == 2) asm volatile("" : "+v"(a[N - 2]), "+v"(a[N - 1]));
+  if constexpr (N % 4 == 3) asm volatile("" : "+v"(a[N - 3]), "+v"(a[N - 2]), "+v"(a[N - 1]));
+}
+// all LDS reads of this wave done
+template <int N>
+__device__ __forceinline__ void lds_wait_all(i32x4 (&a)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : : "memory");
+  tie_rest<N>(a);
+}
+// the reads into a[] done while the CNT reads issued after them may still be in flight (LDS
+// reads of one wave complete in order)
+template <int N, int CNT = N>
+__device__ __forceinline__ void lds_wait_first(i32x4 (&a)[N]) {
+  static_assert(CNT <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "n"(CNT) : "memory");
+  tie_rest<N>(a);
+}
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -199,33 +223,35 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
-// Tie 16-byte results to an lgkmcnt(0) wait: they cannot be used before it.
-__device__ __forceinline__ void lds_wait4(i32x4& a, i32x4& b, i32x4& c, i32x4& d) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : : "memory");
-}
-__device__ __forceinline__ void lds_wait6(i32x4& a, i32x4& b, i32x4& c, i32x4& d, i32x4& e, i32x4& f) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f) : : "memory");
-}
-
-// Tile staging. A tile is 32 selected rows, row-major, each row's 16-byte chunk c stored at
+// Tile staging. A tile is 16 selected rows, row-major, each row's 16-byte chunk c stored at
 // position c ^ (row & 7) (no padding; the XOR keeps both the score reads and the transpose
 // reads free of bank conflicts). Tiles arrive by LDS DMA (global_load_lds_dwordx4): every
 // instruction of a wave fills 64 consecutive 16-byte LDS slots, lane l the slot base + l, so
 // each lane fetches whatever global chunk belongs in its slot. Slots of padding rows fetch
 // from a zero row, so every wave always issues the same number of DMA instructions per tile
-// and the vmcnt bookkeeping below stays exact. A 3-deep ring keeps two tiles (72 KB) in flight
-// per workgroup while the third is consumed.
+// and the vmcnt bookkeeping below stays exact. A 7-deep ring: two tiles are being computed on
+// while five (90 KB) are in flight.
 //
-// Work split: 8 waves, two per group of 16 heads. The pair splits the score contraction (each
-// wave 288 of the 576 dims; partial scores are exchanged through LDS and summed) and the
-// value product (each wave 256 of the 512 output dims). Both waves of a pair then hold the
-// same scores and run the same softmax, and each keeps only half of the query and of the
-// output accumulators, so two waves fit per SIMD.
-constexpr int kStages = 3;
+// Work split: waves 0..3 are score waves, one per group of 16 heads; waves 4..7 are value
+// waves, one per 128 output dims, each for all heads. Wave w runs on SIMD w % 4, so every SIMD
+// holds one of each. In step i the score waves compute S^T = C Q^T for tile i + 1 over all 576
+// dims, run the online softmax and leave the probabilities (bf16 hi + lo parts, [head][row])
+// in LDS, while the value waves accumulate O^T += V^T P^T for tile i from the probabilities
+// left in the previous step (32x32x16 MFMA: 32 dims x 32 heads x the tile's 16 rows). The two
+// kinds of work overlap on each SIMD: one wave's exponentials and shuffles run while the other
+// keeps the matrix core busy. A barrier separates the steps.
+constexpr int kTileRows = 16;
+constexpr int kNst = 7;                // ring stages
 constexpr float kLazyRescale = 8.0f;  // natural-log units
 __device__ __attribute__((aligned(16))) const uint32_t g_zero_row[288] = {0};  // 1152 zero bytes
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+__device__ __forceinline__ f32x16 mma32_bf16(i32x4 a, i32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
@@ -233,15 +259,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-// Workgroup barrier without the release fence of __syncthreads (which would wait for every
-// outstanding DMA); the compiler-only fences keep LDS accesses on their side of it.
+// Workgroup barrier after this wave's own LDS accesses have completed (lgkmcnt(0)); unlike
+// __syncthreads it leaves the in-flight DMA (vmcnt) alone. The compiler-only fences keep LDS
+// accesses on their side of it.
 __device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-// The same after this wave's own LDS writes have completed (lgkmcnt(0), vmcnt untouched).
-__device__ __forceinline__ void lds_write_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // vmcnt 63 (no wait), lgkmcnt 0
   __builtin_amdgcn_s_barrier();
@@ -265,20 +286,26 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   constexpr int DC = DL + DR;
   constexpr int ROWB = DC * 2;                  // bytes per row
   constexpr int CPR = ROWB / 16;                // 16-byte chunks per row (72 or 64)
-  constexpr int TILE_BYTES = kMlaRows * ROWB;
-  constexpr int NBLK = kMlaRows * CPR / 64;     // 64-slot DMA blocks per tile (36 or 32)
-  constexpr int KSW = DC / 64;                  // score k-steps per wave (9 or 8)
-  constexpr int NTW = DL / 32;                  // 16-dim output tiles per wave (16)
+  constexpr int TILE_BYTES = kTileRows * ROWB;
+  constexpr int NBLK = kTileRows * CPR / 64;    // 64-slot DMA blocks per tile (18 or 16)
+  constexpr int KSW = DC / 32;                  // score k-steps (18 or 16)
   constexpr int SB = KSW % 3 == 0 ? 3 : 2;      // score k-steps per LDS batch
-  static_assert(kMlaRows * CPR % 64 == 0 && KSW % SB == 0, "tile shape");
+  constexpr int NJ = DmaShare<NBLK>::hi;
+  static_assert(kTileRows * CPR % 64 == 0 && KSW % SB == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kStages * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kNst * TILE_BYTES];
   __shared__ int s_idx[kMlaMaxChunk];
-  __shared__ __attribute__((aligned(16))) f32x4 s_xch[8][2][64];  // partial scores per wave
+  // probabilities of one tile: [buffer][hi, lo][head][row], bf16 bits
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[2][2][64 * kTileRows];
+  __shared__ __attribute__((aligned(16))) float s_alpha[2][64];   // rescale factor per head
+  __shared__ __attribute__((aligned(16))) uint32_t s_flag[2][4];  // score wave rescaled
+  __shared__ float s_ml[2][64];                                   // final m, l per head
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hg = wave & 3, hf = wave >> 2;      // head group, half
   const int g = lane >> 4, r16 = lane & 15;
+  const bool score_wave = wave < 4;
+  const int hg = wave;            // score waves: head group
+  const int pq = wave - 4;        // value waves: output dims 128 * pq ..
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bi = logical / n_split;
   const int sp = logical - bi * n_split;
@@ -286,33 +313,31 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
   const int s0 = sp * chunk, s1 = min(top_k, s0 + chunk);
   const int nslots = max(0, s1 - s0);
-  const bool computes = hg * 16 < Hm;
+  const bool scores = score_wave && hg * 16 < Hm;
   const int head = hg * 16 + r16;
 
   for (int j = tid; j < nslots; j += 512) {
     const int r = idx[(long)bi * top_k + s0 + j];
     s_idx[j] = (r >= 0 && r < len) ? r : -1;
   }
+  {  // heads without a score wave keep zero probabilities
+    uint4* p4 = reinterpret_cast<uint4*>(&s_p[0][0][0]);
+    for (int j = tid; j < (int)(sizeof(s_p) / 16); j += 512) p4[j] = make_uint4(0u, 0u, 0u, 0u);
+  }
 
-  // query operand (B of the score MFMA) for this wave's half of the dims:
-  // lane holds head, dims 32 * (hf * KSW + s) + 8 * g .. +8
+  // score waves: query operand (B of the score MFMA), lane holds head, dims 32 s + 8 g .. +8
   i32x4 qreg[KSW];
-  if (computes) {
+  if (scores) {
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(qa) + ((long)bi * Hm + head) * ROWB;
 #pragma unroll
-    for (int s = 0; s < KSW; ++s)
-      qreg[s] = *reinterpret_cast<const i32x4*>(qp + (4 * (hf * KSW + s) + g) * 16);
+    for (int s = 0; s < KSW; ++s) qreg[s] = *reinterpret_cast<const i32x4*>(qp + (4 * s + g) * 16);
   }
-  f32x4 o[NTW];
-#pragma unroll
-  for (int t = 0; t < NTW; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  const int n_ht = (Hm + 31) / 32;
   wait_vmcnt<0>();  // query registers ready before the first DMA, so later waits count DMAs only
   __syncthreads();
 
   const uint8_t* latb = reinterpret_cast<const uint8_t*>(lat) + (long)b * n_kv * ROWB;
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_row);
-  constexpr int NJ = DmaShare<NBLK>::hi;
   const int my_blocks = wave < (NBLK % 8 == 0 ? 8 : NBLK % 8) ? DmaShare<NBLK>::hi : DmaShare<NBLK>::lo;
   // per-lane DMA constants: block j of this wave fills LDS slots (j*8 + wave)*64 + lane, which
   // hold chunk dma_c[j] of tile row dma_r[j]
@@ -324,208 +349,279 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     dma_r[j] = r;
     dma_c[j] = ((slot - r * CPR) ^ (r & 7)) * 16;
   }
-  auto issue = [&](int tile) {
-    uint8_t* stage = s_ring + (tile % kStages) * TILE_BYTES;
+  const int ntiles = (nslots + kTileRows - 1) / kTileRows;
+  // The cache rows of a tile's DMA slots are read from s_idx one step before the tile is
+  // issued, so the DMA issue itself never waits for LDS.
+  auto tile_rows = [&](int tile, int (&rows)[NJ]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int ts = tile * kTileRows + dma_r[j];
+      rows[j] = (j * 8 + wave < NBLK && ts < nslots) ? s_idx[ts] : -1;
+    }
+  };
+  auto issue = [&](int tile, const int (&rows)[NJ]) {
+    uint8_t* stage = s_ring + (tile % kNst) * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int blk = j * 8 + wave;
       if (blk < NBLK) {
-        const int ts = tile * kMlaRows + dma_r[j];
-        const int row = ts < nslots ? s_idx[ts] : -1;
-        const uint8_t* src = (row >= 0 ? latb + (long)row * ROWB : zero) + dma_c[j];
+        const uint8_t* src = (rows[j] >= 0 ? latb + (long)rows[j] * ROWB : zero) + dma_c[j];
         __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + blk * 1024), 16, 0, 0);
       }
     }
   };
   // waits: at most `ahead` later tiles of this wave's DMA may still be in flight
-  auto wait_tile = [&](int ahead) {
+  auto wait_tiles = [&](int ahead) {
+    static_assert(kNst - 3 == 4, "wait cases");
     if (my_blocks == DmaShare<NBLK>::hi) {
-      if (ahead >= 1) wait_vmcnt<DmaShare<NBLK>::hi>();
+      constexpr int h = DmaShare<NBLK>::hi;
+      if (ahead >= 4) wait_vmcnt<4 * h>();
+      else if (ahead == 3) wait_vmcnt<3 * h>();
+      else if (ahead == 2) wait_vmcnt<2 * h>();
+      else if (ahead == 1) wait_vmcnt<h>();
       else wait_vmcnt<0>();
     } else {
-      if (ahead >= 1) wait_vmcnt<DmaShare<NBLK>::lo>();
+      constexpr int l = DmaShare<NBLK>::lo;
+      if (ahead >= 4) wait_vmcnt<4 * l>();
+      else if (ahead == 3) wait_vmcnt<3 * l>();
+      else if (ahead == 2) wait_vmcnt<2 * l>();
+      else if (ahead == 1) wait_vmcnt<l>();
       else wait_vmcnt<0>();
     }
   };
-  static_assert(kStages == 3, "wait_tile assumes one tile ahead");
+  __syncthreads();  // s_idx and the zeroed probabilities are visible
+  int next_rows[NJ];
+  for (int p = 0; p < kNst - 2; ++p)
+    if (p < ntiles) {
+      tile_rows(p, next_rows);
+      issue(p, next_rows);
+    }
+  tile_rows(kNst - 2, next_rows);
 
-  const int ntiles = (nslots + kMlaRows - 1) / kMlaRows;
-#pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < ntiles) issue(p);
-
-  // Per-lane LDS offsets inside a tile. Score reads: rows r16 and 16 + r16 (same r & 7), chunk
-  // 4 * S + g with S = hf * KSW + s stored at (4S + g) ^ (r & 7); for k-steps of one parity the
-  // offset grows by 128 bytes per two steps, so two bases cover all steps (immediates do the
-  // rest). Transpose reads: rows 4g + r16/4 (+16), chunk 2 * T + (r16 % 4) / 2 with
-  // T = 16 * hf + t; four bases by t % 4, 128 bytes per four tiles.
+  // Score reads: row r16, chunk 4 s + g stored at (4 s + g) ^ (r16 & 7); for k-steps of one
+  // parity the offset grows by 128 bytes per two steps, so two bases cover all steps.
   const int swz = r16 & 7;
-  const int sc_off0 = (((4 * (hf * KSW + 0) + g) ^ swz) << 4) + r16 * ROWB;
-  const int sc_off1 = (((4 * (hf * KSW + 1) + g) ^ swz) << 4) + r16 * ROWB;
-  const int tr_row = 4 * g + (r16 >> 2);
-  const int tr_x = tr_row & 7;
-  const int tr_c = (r16 & 3) >> 1;
-  int tr_off[4];
+  const int sc_off0 = ((g ^ swz) << 4) + r16 * ROWB;
+  const int sc_off1 = (((4 + g) ^ swz) << 4) + r16 * ROWB;
+  // Value reads (A operand of the 32x32x16 MFMA: lane holds dim 32 dt + l % 32, rows
+  // 8 (l / 32) .. +8): transpose reads, two per dim tile (rows +0..3 and +4..7). In the 16-lane
+  // group gg of lane l, lane i points at row 8 (gg / 2) + i / 4 (+4), dims d0 + 4 (i % 4) with
+  // d0 = 128 pq + 32 dt + 16 (gg % 2).
+  int tr_off[4][2];
+  {
+    const int gg = g, i = r16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) tr_off[j] = tr_row * ROWB + (((2 * (16 * hf + j) + tr_c) ^ tr_x) << 4) + (r16 & 1) * 8;
-
-  for (int tile = 0; tile < ntiles; ++tile) {
-    wait_tile(min(kStages - 2, ntiles - 1 - tile));
-    lds_barrier();
-    if (tile + kStages - 1 < ntiles) issue(tile + kStages - 1);
-    const uint32_t bufa = lds_addr(s_ring + (tile % kStages) * TILE_BYTES);
-    // row validity of this tile: bit r set when tile row r holds a selected cache row
-    int sv = -1;
-    if (lane < kMlaRows) {
-      const int ts = tile * kMlaRows + lane;
-      sv = ts < nslots ? s_idx[ts] : -1;
-    }
-    const uint32_t vbits = (uint32_t)__ballot(sv >= 0);
-    // partial S^T tiles over this wave's dims: rows 16 * rt + 4 * g + e, head r16
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (computes) {
-      const uint32_t sb0 = bufa + sc_off0, sb1 = bufa + sc_off1;
-      i32x4 sa[2][2 * SB];
-      auto s_issue = [&](auto KB, i32x4(&a)[2 * SB]) {
-        static_for<0, SB>([&](auto J) {
-          constexpr int st = decltype(KB)::value * SB + decltype(J)::value;
-          constexpr int off = 128 * (st >> 1);
-          const uint32_t bse = (st & 1) ? sb1 : sb0;
-          a[2 * J] = ds_read_b128_off<off>(bse);
-          a[2 * J + 1] = ds_read_b128_off<off + 16 * ROWB>(bse);
-        });
-      };
-      s_issue(std::integral_constant<int, 0>(), sa[0]);
-      static_for<0, KSW / SB>([&](auto KB) {
-        constexpr int kb = decltype(KB)::value;
-        constexpr int cur = kb & 1;
-        if constexpr (SB == 3)
-          lds_wait6(sa[cur][0], sa[cur][1], sa[cur][2], sa[cur][3], sa[cur][4], sa[cur][5]);
-        else
-          lds_wait4(sa[cur][0], sa[cur][1], sa[cur][2], sa[cur][3]);
-        if constexpr (kb + 1 < KSW / SB) s_issue(std::integral_constant<int, kb + 1>(), sa[cur ^ 1]);
-        static_for<0, SB>([&](auto J) {
-          sacc[0] = mma_bf16(sa[cur][2 * J], qreg[SB * kb + J], sacc[0]);
-          sacc[1] = mma_bf16(sa[cur][2 * J + 1], qreg[SB * kb + J], sacc[1]);
-        });
-      });
-      s_xch[wave][0][lane] = sacc[0];
-      s_xch[wave][1][lane] = sacc[1];
-    }
-    lds_write_barrier();  // partial scores of both waves of a pair are in LDS
-    if (computes) {
-      const f32x4 p0 = s_xch[wave ^ 4][0][lane], p1 = s_xch[wave ^ 4][1][lane];
-      // both waves of the pair add the halves in the same order, so they hold equal scores
-      const f32x4 a0 = hf == 0 ? sacc[0] : p0, b0 = hf == 0 ? p0 : sacc[0];
-      const f32x4 a1 = hf == 0 ? sacc[1] : p1, b1 = hf == 0 ? p1 : sacc[1];
-      const uint32_t vlo = vbits >> (4 * g), vhi = vbits >> (16 + 4 * g);
-      float z[8];
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        z[e] = (vlo >> e) & 1u ? (a0[e] + b0[e]) * sm_scale : -INFINITY;
-        z[4 + e] = (vhi >> e) & 1u ? (a1[e] + b1[e]) * sm_scale : -INFINITY;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 8 * (gg >> 1) + (i >> 2) + 4 * hh;
+        const int d = 128 * (pq & 3) + 32 * dt + 16 * (gg & 1) + 4 * (i & 3);
+        tr_off[dt][hh] = row * ROWB + (((d >> 3) ^ (row & 7)) << 4) + (d & 7) * 2;
       }
-      float mt = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      mt = fmaxf(mt, shfl_xor(mt, 16));
-      mt = fmaxf(mt, shfl_xor(mt, 32));
-      // m_run is a reference max, not the exact running max: weights are exp(z - m_run) and
-      // O, l are kept relative to it. It moves (and O, l are rescaled) only when a tile's max
-      // exceeds it by more than kLazyRescale, so weights stay below e^kLazyRescale (harmless
-      // in fp32 and for the bf16 hi + lo split) and the rescale branch is rarely taken. O / l
-      // and m_run + log(l) do not depend on the reference.
-      // Every head sees the same valid rows, so mt is -inf in all lanes or in none.
-      if (mt != -INFINITY) {
-        if (__ballot(mt > m_run + kLazyRescale) != 0) {
-          const float m_new = fmaxf(m_run, mt);
-          const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+  }
+
+  // One step: wait for this wave's DMA of the score tile, barrier, refill the freed stage.
+  // Both kinds of wave run the same steps (and barriers) in loops of their own, so each
+  // keeps only its own state in registers.
+  auto step = [&](int it) {
+    const int u = it + 1;  // score tile of this step
+    if (u < ntiles) wait_tiles(min(kNst - 3, ntiles - 1 - u));
+    lds_barrier();
+    if (it + kNst - 1 < ntiles) issue(it + kNst - 1, next_rows);
+    tile_rows(it + kNst, next_rows);
+  };
+
+  if (score_wave) {
+    float m_run = -INFINITY, l_run = 0.f;
+    constexpr int KH = KSW / 2;
+    auto score_step = [&](int it) {
+      step(it);
+      const int u = it + 1;
+      if (scores && u < ntiles) {
+        const int buf = u & 1;
+        const uint32_t bufa = lds_addr(s_ring + (u % kNst) * TILE_BYTES);
+        int sv = -1;
+        if (lane < kTileRows) {
+          const int ts = u * kTileRows + lane;
+          sv = ts < nslots ? s_idx[ts] : -1;
+        }
+        const uint32_t vbits = (uint32_t)__ballot(sv >= 0);
+        // S^T tile: rows 4 g + e, head r16. The k-step reads go out in two halves; the first
+        // half's products run while the second half is in flight, and the k-steps feed three
+        // accumulators in turn so consecutive MFMAs do not wait on each other.
+        const uint32_t sb0 = bufa + sc_off0, sb1 = bufa + sc_off1;
+        i32x4 ka[KH], kb[KH];
+        static_for<0, KH>([&](auto S) {
+          constexpr int st = decltype(S)::value;
+          ka[st] = ds_read_b128_off<128 * (st >> 1)>((st & 1) ? sb1 : sb0);
+        });
+        static_for<0, KH>([&](auto S) {
+          constexpr int st = KH + decltype(S)::value;
+          kb[st - KH] = ds_read_b128_off<128 * (st >> 1)>((st & 1) ? sb1 : sb0);
+        });
+        lds_wait_first<KH>(ka);
+        f32x4 sacc[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        static_for<0, KH>([&](auto S) {
+          constexpr int st = decltype(S)::value;
+          sacc[st % 3] = mma_bf16(ka[st], qreg[st], sacc[st % 3]);
+        });
+        lds_wait_all<KH>(kb);
+        static_for<0, KH>([&](auto S) {
+          constexpr int st = KH + decltype(S)::value;
+          sacc[st % 3] = mma_bf16(kb[st - KH], qreg[st], sacc[st % 3]);
+        });
+        const uint32_t vr = vbits >> (4 * g);
+        float z[4];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) {
-            o[t][0] *= alpha;
-            o[t][1] *= alpha;
-            o[t][2] *= alpha;
-            o[t][3] *= alpha;
-          }
+        for (int e = 0; e < 4; ++e)
+          z[e] = (vr >> e) & 1u ? ((sacc[0][e] + sacc[1][e]) + sacc[2][e]) * sm_scale : -INFINITY;
+        // m_run is a reference max, not the exact running max: weights are exp(z - m_run) and
+        // O, l are kept relative to it. It moves (and O, l are rescaled by alpha) only when a
+        // score exceeds it by more than kLazyRescale, so weights stay below e^kLazyRescale
+        // (harmless in fp32 and for the bf16 hi + lo split) and rescales are rare: the common
+        // path needs no cross-lane reduction. m_run is equal in the four lanes of a head; each
+        // lane sums the weights of its own rows (l_run) and the lanes are added at the end.
+        // O / l and m_run + log(l) do not depend on the reference.
+        const float zl = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        float alpha = 1.f;
+        const bool rescale = __ballot(zl > m_run + kLazyRescale) != 0;
+        if (rescale) {
+          float mt = fmaxf(zl, shfl_xor(zl, 16));
+          mt = fmaxf(mt, shfl_xor(mt, 32));
+          const float m_new = fmaxf(m_run, mt);
+          alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
           l_run *= alpha;
           m_run = m_new;
         }
-        // p = hi + lo with both parts bf16 (hardware round to nearest even): the value
-        // product runs once per part, so the weights keep about 16 significant bits.
-        float p[8];
+        float pr[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __expf(z[e] - m_run);  // exp(-inf) = 0
-        bf16x8 hi8, lo8;
+        for (int e = 0; e < 4; ++e) pr[e] = z[e] == -INFINITY ? 0.f : __expf(z[e] - m_run);
+        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        // p = hi + lo with both parts bf16 (round to nearest even): the value product runs
+        // once per part, so the weights keep about 16 significant bits.
+        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+        bf16x4 hi4, lo4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hi8[e] = (__bf16)p[e];
+        for (int e = 0; e < 4; ++e) hi4[e] = (__bf16)pr[e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lo8[e] = (__bf16)(p[e] - (float)hi8[e]);
-        float psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        psum += shfl_xor(psum, 16);
-        psum += shfl_xor(psum, 32);
-        l_run += psum;
-        // P^T operand: k slots 0..3 = rows 4g+e, slots 4..7 = rows 16+4g+e
-        const i32x4 pv_hi = __builtin_bit_cast(i32x4, hi8);
-        const i32x4 pv_lo = __builtin_bit_cast(i32x4, lo8);
-        // V^T operand through transpose reads of this wave's output dims: lane i of row-group
-        // g supplies the address of rows (4g + i/4) and (16 + 4g + i/4), dims 16T + 4*(i%4).
-        // Batches of four output tiles; batch k+1 is in flight during batch k.
-        uint32_t tb_[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tb_[j] = bufa + tr_off[j];
-        i16x4 lo[2][4], hi[2][4];
-        auto tr_issue = [&](auto TB, i16x4(&l)[4], i16x4(&h)[4]) {
-          static_for<0, 4>([&](auto J) {
-            constexpr int off = 128 * decltype(TB)::value;
-            l[J] = ds_read_tr16_off<off>(tb_[J]);
-            h[J] = ds_read_tr16_off<off + 16 * ROWB>(tb_[J]);
-          });
-        };
-        auto tr_wait = [&](i16x4(&l)[4], i16x4(&h)[4]) {
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(l[0]), "+v"(l[1]), "+v"(l[2]), "+v"(l[3]), "+v"(h[0]), "+v"(h[1]), "+v"(h[2]),
-                         "+v"(h[3])
-                       :
-                       : "memory");
-        };
-        tr_issue(std::integral_constant<int, 0>(), lo[0], hi[0]);
-        static_for<0, NTW / 4>([&](auto TB) {
-          constexpr int tb = decltype(TB)::value;
-          constexpr int cur = tb & 1;
-          tr_wait(lo[cur], hi[cur]);
-          if constexpr (tb + 1 < NTW / 4) tr_issue(std::integral_constant<int, tb + 1>(), lo[cur ^ 1], hi[cur ^ 1]);
-          static_for<0, 4>([&](auto J) {
-            constexpr int t = tb * 4 + decltype(J)::value;
-            const i32x4 av = __builtin_bit_cast(i32x4, __builtin_shufflevector(lo[cur][J], hi[cur][J], 0, 1, 2, 3, 4, 5, 6, 7));
-            o[t] = mma_bf16(av, pv_lo, mma_bf16(av, pv_hi, o[t]));
-          });
-        });
+        for (int e = 0; e < 4; ++e) lo4[e] = (__bf16)(pr[e] - (float)hi4[e]);
+        const int po = head * kTileRows + 4 * g;
+        *reinterpret_cast<bf16x4*>(&s_p[buf][0][po]) = hi4;
+        *reinterpret_cast<bf16x4*>(&s_p[buf][1][po]) = lo4;
+        if (lane < 16) s_alpha[buf][head] = alpha;
+        if (lane == 0) s_flag[buf][hg] = rescale ? 1u : 0u;
+      } else if (u < ntiles && lane == 0) {
+        s_flag[u & 1][hg] = 0u;
+      }
+    };
+    for (int it = -1; it < ntiles; ++it) score_step(it);
+    // final statistics of each head
+    if (scores) {
+      l_run += shfl_xor(l_run, 16);
+      l_run += shfl_xor(l_run, 32);
+      if (g == 0) {
+        s_ml[0][head] = m_run;
+        s_ml[1][head] = l_run;
       }
     }
-  }
-
-  if (!computes) return;
-  // lane holds O[head][256 * hf + 16t + 4g + e]
-  const long qh = (long)bi * Hm + head;
-  if (n_split == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* op = out + qh * DL + 256 * hf + 4 * g;
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      f32x4 v = o[t];
-      v[0] *= inv;
-      v[1] *= inv;
-      v[2] *= inv;
-      v[3] *= inv;
-      *reinterpret_cast<f32x4*>(op + 16 * t) = v;
-    }
-    if (lse && hf == 0 && g == 0) lse[qh] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
+    __syncthreads();
+    return;
   } else {
-    const long ph = ((long)bi * n_split + sp) * Hm + head;
-    float* op = ws_o + ph * DL + 256 * hf + 4 * g;
+    // O^T tiles [32 dims][32 heads], dims 128 pq + 32 dt, heads 32 ht
+    f32x16 o[4][2];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = o[t];
-    if (hf == 0 && g == 0) {
-      ws_ml[2 * ph] = m_run;
-      ws_ml[2 * ph + 1] = l_run;
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][ht][e] = 0.f;
+    // The value operands of tile it + 1 are read at the end of step it (that tile is in LDS
+    // for the score waves) into the registers the step's products have just consumed, so a
+    // step only waits for its probabilities.
+    i16x4 va[4][2];
+    auto read_v = [&](int tile) {
+      const uint32_t bufa = lds_addr(s_ring + (tile % kNst) * TILE_BYTES);
+      static_for<0, 4>([&](auto DT) {
+        constexpr int dt = decltype(DT)::value;
+        va[dt][0] = ds_read_tr16_off<0>(bufa + tr_off[dt][0]);
+        va[dt][1] = ds_read_tr16_off<0>(bufa + tr_off[dt][1]);
+      });
+    };
+    const uint32_t p_off = ((lane & 31) * kTileRows + 8 * (lane >> 5)) * 2;
+    for (int it = -1; it < ntiles; ++it) {
+      step(it);  // its lgkmcnt(0) wait completes the reads into va
+      if (it >= 0) {
+        const int buf = it & 1;
+        const uint4 fl = *reinterpret_cast<const uint4*>(s_flag[buf]);
+        if ((fl.x | fl.y | fl.z | fl.w) != 0u) {  // uniform: some head group moved its reference
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) {
+            const float a = s_alpha[buf][32 * ht + (lane & 31)];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) o[dt][ht][e] *= a;
+          }
+        }
+        // B operands: P^T [16 rows][32 heads], lane holds head 32 ht + l % 32, rows 8 (l / 32) ..
+        const uint32_t pbase = lds_addr(&s_p[buf][0][0]) + p_off;
+        constexpr int PHL = 64 * kTileRows * 2;  // bytes between the hi and lo parts
+        constexpr int PHT = 32 * kTileRows * 2;  // bytes between the two head tiles
+        i32x4 pb[4];
+        pb[0] = ds_read_b128_off<0>(pbase);
+        pb[1] = ds_read_b128_off<PHL>(pbase);
+        pb[2] = ds_read_b128_off<PHT>(pbase);
+        pb[3] = ds_read_b128_off<PHT + PHL>(pbase);
+        lds_wait_all<4>(pb);
+        asm volatile("" : "+v"(va[0][0]), "+v"(va[0][1]), "+v"(va[1][0]), "+v"(va[1][1]),
+                     "+v"(va[2][0]), "+v"(va[2][1]), "+v"(va[3][0]), "+v"(va[3][1]));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const i32x4 av = __builtin_bit_cast(i32x4, __builtin_shufflevector(va[dt][0], va[dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) {
+            if (ht < n_ht) {
+              o[dt][ht] = mma32_bf16(av, pb[2 * ht], o[dt][ht]);
+              o[dt][ht] = mma32_bf16(av, pb[2 * ht + 1], o[dt][ht]);
+            }
+          }
+        }
+      }
+      if (it + 1 < ntiles) read_v(it + 1);
+    }
+    __syncthreads();  // the score waves' statistics are in s_ml
+    // lane holds O^T[32 dt + 8 (i / 4) + 4 (l / 32) + i % 4][32 ht + l % 32], i < 16
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int h = 32 * ht + (lane & 31);
+    if (h >= Hm) continue;
+    const float m = s_ml[0][h], l = s_ml[1][h];
+    const long qh = (long)bi * Hm + h;
+    float* dst;
+    float scale;
+    if (n_split == 1) {
+      dst = out + qh * DL;
+      scale = l > 0.f ? 1.f / l : 0.f;
+    } else {
+      const long ph = ((long)bi * n_split + sp) * Hm + h;
+      dst = ws_o + ph * DL;
+      scale = 1.f;
+      if (pq == 0 && lane < 32) {
+        ws_ml[2 * ph] = m;
+        ws_ml[2 * ph + 1] = l;
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d = 128 * pq + 32 * dt + 8 * c + 4 * (lane >> 5);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = o[dt][ht][4 * c + e] * scale;
+        *reinterpret_cast<f32x4*>(dst + d) = v;
+      }
+      if (n_split == 1 && lse && pq == 0 && lane < 32) lse[qh] = l > 0.f ? m + __logf(l) : -INFINITY;
     }
   }
 }
