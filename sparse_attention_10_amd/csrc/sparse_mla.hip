@@ -575,17 +575,19 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
         lds_wait_all<4>(pb);
         asm volatile("" : "+v"(va[0][0]), "+v"(va[0][1]), "+v"(va[1][0]), "+v"(va[1][1]),
                      "+v"(va[2][0]), "+v"(va[2][1]), "+v"(va[3][0]), "+v"(va[3][1]));
+        // all hi-part products first, then the lo parts: the two products into one
+        // accumulator are eight MFMAs apart, so none waits for the previous one's result
+        i32x4 av[4];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const i32x4 av = __builtin_bit_cast(i32x4, __builtin_shufflevector(va[dt][0], va[dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int dt = 0; dt < 4; ++dt)
+          av[dt] = __builtin_bit_cast(i32x4, __builtin_shufflevector(va[dt][0], va[dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int ht = 0; ht < 2; ++ht) {
-            if (ht < n_ht) {
-              o[dt][ht] = mma32_bf16(av, pb[2 * ht], o[dt][ht]);
-              o[dt][ht] = mma32_bf16(av, pb[2 * ht + 1], o[dt][ht]);
-            }
-          }
-        }
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+              if (ht < n_ht) o[dt][ht] = mma32_bf16(av[dt], pb[2 * ht + hl], o[dt][ht]);
       }
       if (it + 1 < ntiles) read_v(it + 1);
     }
