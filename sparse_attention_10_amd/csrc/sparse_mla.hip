@@ -638,7 +638,9 @@ __global__ __launch_bounds__(256) void mla_merge(const float* __restrict__ ws_o,
                                                  float* __restrict__ out, float* __restrict__ lse,
                                                  int Hm, int n_split, int dv, long total) {
   typedef __attribute__((__vector_size__(VEC * sizeof(float)))) float fv;
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;  // over (query, head, dims / VEC)
+  // over (query, head, dims / VEC); XCD-aware order, so a query's merge runs on the XCD whose
+  // L2 received that query's partial outputs from the attention kernel
+  const long gid = (long)xcd_remap(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   if (gid >= total) return;
   const long qh = gid / dv;
   const int dq = (int)(gid - qh * dv);
