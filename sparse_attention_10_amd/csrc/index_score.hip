@@ -125,9 +125,17 @@ __device__ __forceinline__ float head_reduce(const f32x4& a0, const f32x4& a1, c
 // ((x * iters + it) * 4 + w) for it < iters. Each wave keeps two chunks of loads in flight
 // (statically indexed ping-pong registers, so the compiler's vmcnt waits count exactly): the
 // loads are unconditional, with rows past the scored range clamped to a valid row and the
-// boundary chunk zeroed afterwards.
+// boundary chunk zeroed afterwards. A wave only reads the LDS tile it wrote itself, so waves
+// never wait for each other: LDS operations of one wave execute in issue order, and a
+// compiler-only fence keeps that order in the code.
 // ---------------------------------------------------------------------------------------
 constexpr int kDecWaves = 4;
+
+__device__ __forceinline__ void wave_lds_order() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 template <typename T16>
 __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
   auto step = [&](int it, i32x4(&pre)[16], bool has_next2) {
     const int kb = kb_of(it);
     const bool active = kb < limit;
-    __syncthreads();
+    wave_lds_order();  // the previous chunk's tile reads stay before these writes
     if (active) {
       if (kb + 64 > limit) {  // boundary chunk: rows past the scored range are zero
 #pragma unroll
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
       }
     }
     if (has_next2) fetch(kb_of(it + 2), pre);  // two chunks ahead, into the freed registers
-    __syncthreads();
+    wave_lds_order();
     return active;
   };
 
@@ -209,11 +217,10 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
   };
 
   for (int it = 0; it < iters; it += 2) {
-    // block-uniform exit: every wave reaches the same barriers
-    if ((blockIdx.x * iters + it) * kDecWaves * 64 >= n_kv) break;
+    if (kb_of(it) >= n_kv) break;
     const bool a0 = step(it, pa, it + 2 < iters);
     compute(it, a0);
-    if (it + 1 >= iters || (blockIdx.x * iters + it + 1) * kDecWaves * 64 >= n_kv) break;
+    if (it + 1 >= iters || kb_of(it + 1) >= n_kv) break;
     const bool a1 = step(it + 1, pb, it + 3 < iters);
     compute(it + 1, a1);
   }
