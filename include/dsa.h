@@ -62,7 +62,7 @@ enum {
  *          (NULL: q_pos[b][i] = kv_len[b] - n_q + i, the queries are the last n_q rows)
  * scores   device, [B][n_q][n_kv] fp32, written in full
  * scale    factor applied after the head sum
- * Sizes: B, n_q, H, D, n_kv >= 1. q_dtype must equal k_dtype (F32, BF16 or F16).
+ * Sizes: B, n_q, H, D, n_kv >= 1, n_kv <= 2^30. q_dtype must equal k_dtype (F32, BF16 or F16).
  * bf16/f16 with D = 128 and H <= 32 run on MFMA; other shapes run a plain kernel that
  * needs H * D <= 16384.
  */
@@ -132,7 +132,8 @@ int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* id
  * candidates in many workgroups per row, one workgroup per row selects among them, with a
  * whole-row select when the candidates cannot hold the answer). A path the shape does not
  * allow falls back to the automatic choice. key "score_chunks_per_wave": 64-key chunks
- * each wave of the 16-bit decode scoring kernel walks (0 = automatic, else 1..64). Returns DSA_OK,
+ * each wave of the 16-bit decode scoring kernel walks (0 = automatic, else 1..64, taken
+ * down to 1, 2, 4 or 8). Returns DSA_OK,
  * or DSA_ERR_SHAPE for an unknown key or value. Process-wide; set it before launching work.
  */
 int dsa_set_tuning(const char* key, int value);

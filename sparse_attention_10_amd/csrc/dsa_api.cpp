@@ -82,8 +82,8 @@ int dsa_index_score(const void* q, const void* k_cache, const float* w, const in
   if (B < 1 || n_q < 1 || H < 1 || D < 1 || n_kv < 1)
     return fail(DSA_ERR_SHAPE, "dsa_index_score: B=%d n_q=%d H=%d D=%d n_kv=%d must all be >= 1", B, n_q,
                 H, D, n_kv);
-  if ((long long)B * n_q > INT_MAX || (long long)B * n_q * n_kv > (1LL << 40))
-    return fail(DSA_ERR_SHAPE, "dsa_index_score: B*n_q*n_kv too large");
+  if ((long long)B * n_q > INT_MAX || (long long)B * n_q * n_kv > (1LL << 40) || n_kv > (1 << 30))
+    return fail(DSA_ERR_SHAPE, "dsa_index_score: n_kv (at most 2^30) or B*n_q*n_kv too large");
   if (!valid_dtype(q_dtype) || !valid_dtype(k_dtype))
     return fail(DSA_ERR_DTYPE, "dsa_index_score: unknown dtype (q %d, k %d)", q_dtype, k_dtype);
   if (q_dtype != k_dtype)

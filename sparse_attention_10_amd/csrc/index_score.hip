@@ -78,42 +78,42 @@ template <> struct Mma16<f16_t> {
 __device__ __forceinline__ int key_lds_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
 // Query operand of one wave: heads 16*mt + (lane%16), k-step s covers dims 32*s + 8*(lane/16) .. +8.
+// Heads past H load head H-1 (the loads stay unconditional); their products are dropped in
+// head_reduce.
 template <typename T16>
 __device__ __forceinline__ void load_q_operand(const T16* q_bi, int H, int lane, i32x4 (&qa)[2][4]) {
   const int g = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const int head = 16 * mt + r16;
+    const int head = min(16 * mt + r16, H - 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (head < H)
-        qa[mt][s] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(q_bi) +
-                                                    head * 256 + (4 * s + g) * 16);
-      else
-        qa[mt][s] = i32x4{0, 0, 0, 0};
-    }
+    for (int s = 0; s < 4; ++s)
+      qa[mt][s] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(q_bi) +
+                                                  head * 256 + (4 * s + g) * 16);
   }
 }
 
-// Weights of the accumulator rows a lane holds: heads 16*mt + 4*(lane/16) + e.
+// Weights of the accumulator rows a lane holds: heads 16*mt + 4*(lane/16) + e (clamped to
+// H-1 like the query; head_reduce drops the rows past H).
 __device__ __forceinline__ void load_w_rows(const float* w_bi, int H, int lane, float (&wr)[2][4]) {
   const int g = lane >> 4;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int head = 16 * mt + 4 * g + e;
-      wr[mt][e] = head < H ? w_bi[head] : 0.f;
-    }
+    for (int e = 0; e < 4; ++e) wr[mt][e] = w_bi[min(16 * mt + 4 * g + e, H - 1)];
 }
 
-// relu, head weight and head sum of one 16-key N tile; every lane of a column ends with the sum.
-__device__ __forceinline__ float head_reduce(const f32x4& a0, const f32x4& a1, const float (&wr)[2][4]) {
+// relu, head weight and head sum of one 16-key N tile over the heads below H; every lane of
+// a column ends with the sum.
+__device__ __forceinline__ float head_reduce(const f32x4& a0, const f32x4& a1, const float (&wr)[2][4],
+                                             int H, int g) {
   float p = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    p = fmaf(wr[0][e], fmaxf(a0[e], 0.f), p);
-    p = fmaf(wr[1][e], fmaxf(a1[e], 0.f), p);
+    const float t0 = wr[0][e] * fmaxf(a0[e], 0.f);
+    const float t1 = wr[1][e] * fmaxf(a1[e], 0.f);
+    p += 4 * g + e < H ? t0 : 0.f;
+    p += 16 + 4 * g + e < H ? t1 : 0.f;
   }
   p += shfl_xor(p, 16);
   p += shfl_xor(p, 32);
@@ -122,10 +122,14 @@ __device__ __forceinline__ float head_reduce(const f32x4& a0, const f32x4& a1, c
 
 // ---------------------------------------------------------------------------------------
 // decode: grid (key blocks, B * n_q), 4 waves; wave w of block x handles the 64-key chunks
-// ((x * iters + it) * 4 + w) for it < iters. Each wave keeps two chunks of loads in flight
-// (statically indexed ping-pong registers, so the compiler's vmcnt waits count exactly): the
-// loads are unconditional, with rows past the scored range clamped to a valid row and the
-// boundary chunk zeroed afterwards. A wave only reads the LDS tile it wrote itself, so waves
+// ((x * ITERS + it) * 4 + w) for it < ITERS. Each wave keeps two chunks of loads in flight in
+// ping-pong registers. The code between the loads and their use has no branches: the chunk
+// loop is fully unrolled (ITERS is a template argument) and every load is unconditional,
+// because at a join of paths with different loads in flight the compiler's wait counting
+// falls back to waiting for all of them, the next chunk's included. Rows past the scored
+// range are clamped to the last scored row (row 0 when nothing is scored), so every load
+// reads real data and chunks past the range cost no extra HBM traffic; their scores are
+// replaced by -inf at the store. A wave only reads the LDS tile it wrote itself, so waves
 // never wait for each other: LDS operations of one wave execute in issue order, and a
 // compiler-only fence keeps that order in the code.
 // ---------------------------------------------------------------------------------------
@@ -137,14 +141,14 @@ __device__ __forceinline__ void wave_lds_order() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename T16>
+template <typename T16, int ITERS>
 __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
-    int n_q, int H, int n_kv, int iters, float scale) {
+    int n_q, int H, int n_kv, float scale) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDecWaves][64 * 256];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int bi = blockIdx.y;
   const int b = bi / n_q, i = bi - b * n_q;
@@ -156,73 +160,66 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
   uint8_t* my = lds[wave];
 
   // chunk it of this wave starts at key kb(it)
-  auto kb_of = [&](int it) { return ((blockIdx.x * iters + it) * kDecWaves + wave) * 64; };
+  auto kb_of = [&](int it) { return ((int)(blockIdx.x * ITERS + it) * kDecWaves + wave) * 64; };
+  const int last = max(limit - 1, 0);
   auto fetch = [&](int kb, i32x4(&pre)[16]) {
-    if (kb >= limit) return;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int row = min(kb + 4 * j + g, limit - 1);
+      const int row = min(kb + 4 * j + g, last);
       pre[j] = *reinterpret_cast<const i32x4*>(kseq + (long)row * 256 + r16 * 16);
     }
   };
-  auto step = [&](int it, i32x4(&pre)[16], bool has_next2) {
-    const int kb = kb_of(it);
-    const bool active = kb < limit;
-    wave_lds_order();  // the previous chunk's tile reads stay before these writes
-    if (active) {
-      if (kb + 64 > limit) {  // boundary chunk: rows past the scored range are zero
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (kb + 4 * j + g >= limit) pre[j] = i32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = 4 * j + g;
-        *reinterpret_cast<i32x4*>(my + key_lds_off(r, r16)) = pre[j];
-      }
-    }
-    if (has_next2) fetch(kb_of(it + 2), pre);  // two chunks ahead, into the freed registers
-    wave_lds_order();
-    return active;
-  };
 
+  // query and weights first: loads complete in issue order, so the first chunk's MFMAs
+  // wait for that chunk only
   i32x4 qa[2][4];
   float wr[2][4];
-  i32x4 pa[16], pb[16];
-  fetch(kb_of(0), pa);
-  if (iters > 1) fetch(kb_of(1), pb);
+  i32x4 pre[2][16];
   load_q_operand(q + (long)bi * H * 128, H, lane, qa);
   load_w_rows(w + (long)bi * H, H, lane, wr);
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order: query, weights, chunk 0, chunk 1
+  fetch(kb_of(0), pre[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (ITERS > 1) fetch(kb_of(1), pre[1]);
+  __builtin_amdgcn_sched_barrier(0);
 
-  auto compute = [&](int it, bool active) {
-    const int kb = kb_of(it);
-    float v = -INFINITY;
-    if (active) {
-      float sc[4];
+  // chunks past n_kv (in the last block) compute on clamped rows and store nothing
+  float res[ITERS];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < ITERS; ++it) {
+    i32x4(&p)[16] = pre[it & 1];
+    wave_lds_order();  // the previous chunk's tile reads stay before these writes
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const i32x4 kv = *reinterpret_cast<const i32x4*>(my + key_lds_off(nt * 16 + r16, 4 * s + g));
-          a0 = Mma16<T16>::run(qa[0][s], kv, a0);
-          a1 = Mma16<T16>::run(qa[1][s], kv, a1);
-        }
-        sc[nt] = head_reduce(a0, a1, wr);
-      }
-      v = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+    for (int j = 0; j < 16; ++j) {
+      const int r = 4 * j + g;
+      *reinterpret_cast<i32x4*>(my + key_lds_off(r, r16)) = p[j];
     }
-    const int t = kb + lane;
-    if (t < n_kv) out[t] = t < limit ? scale * v : -INFINITY;
-  };
-
-  for (int it = 0; it < iters; it += 2) {
-    if (kb_of(it) >= n_kv) break;
-    const bool a0 = step(it, pa, it + 2 < iters);
-    compute(it, a0);
-    if (it + 1 >= iters || kb_of(it + 1) >= n_kv) break;
-    const bool a1 = step(it + 1, pb, it + 3 < iters);
-    compute(it + 1, a1);
+    if (it + 2 < ITERS) fetch(kb_of(it + 2), p);  // two chunks ahead, into the freed registers
+    __builtin_amdgcn_sched_barrier(0);
+    wave_lds_order();
+    float sc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const i32x4 kv = *reinterpret_cast<const i32x4*>(my + key_lds_off(nt * 16 + r16, 4 * s + g));
+        a0 = Mma16<T16>::run(qa[0][s], kv, a0);
+        a1 = Mma16<T16>::run(qa[1][s], kv, a1);
+      }
+      sc[nt] = head_reduce(a0, a1, wr, H, g);
+    }
+    // lane group g keeps tile g (bit tests, which the compiler keeps as selects)
+    const float v01 = (g & 1) ? sc[1] : sc[0];
+    const float v23 = (g & 1) ? sc[3] : sc[2];
+    res[it] = (g & 2) ? v23 : v01;
+  }
+  // stores last: a store guard is a branch, and the code-sinking pass would move the loads
+  // of a later chunk past it, next to their use
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int t = kb_of(it) + lane;
+    if (t < n_kv) out[t] = t < limit ? scale * res[it] : -INFINITY;
   }
 }
 
@@ -330,7 +327,7 @@ __global__ __launch_bounds__(256) void index_score_prefill_mfma(
         }
       }
 #pragma unroll
-      for (int qq = 0; qq < kPreQPW; ++qq) sc[qq][nt] = head_reduce(acc[qq][0], acc[qq][1], wr[qq]);
+      for (int qq = 0; qq < kPreQPW; ++qq) sc[qq][nt] = head_reduce(acc[qq][0], acc[qq][1], wr[qq], H, g);
     }
     const int t = kb + lane;
 #pragma unroll
@@ -374,13 +371,20 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
     const long rows = (long)B * n_q;
     // about 2048 blocks: short-lived waves of two chunks each measured fastest (more
     // independent streams in flight than a few long-lived waves)
-    long iters = g_score_cpw > 0 ? g_score_cpw : (chunks * rows) / 2048;
-    iters = iters < 1 ? 1 : (iters > 64 ? 64 : iters);
+    long want = g_score_cpw > 0 ? g_score_cpw : (chunks * rows) / 2048;
+    const int iters = want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
     const long xblocks = (chunks + iters - 1) / iters;
     dim3 grid((unsigned)xblocks, (unsigned)rows);
-    hipLaunchKernelGGL(index_score_decode_mfma<T16>, grid, dim3(256), 0, stream,
-                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv,
-                       (int)iters, scale);
+#define DSA_DECODE_LAUNCH(N)                                                                  \
+  hipLaunchKernelGGL((index_score_decode_mfma<T16, N>), grid, dim3(256), 0, stream,             \
+                     (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale)
+    switch (iters) {
+      case 8: DSA_DECODE_LAUNCH(8); break;
+      case 4: DSA_DECODE_LAUNCH(4); break;
+      case 2: DSA_DECODE_LAUNCH(2); break;
+      default: DSA_DECODE_LAUNCH(1); break;
+    }
+#undef DSA_DECODE_LAUNCH
   }
   return hipGetLastError();
 }

@@ -42,6 +42,21 @@ def test_decode_bf16_shapes(B, n_kv, H):
     _run(DEC.scaled(B=B, n_kv=n_kv, H=H), 1)
 
 
+@pytest.mark.parametrize("cpw", [1, 2, 4, 8])
+def test_decode_chunks_per_wave(cpw):
+    """Every unrolled variant of the decode kernel: ragged kv_len (a chunk straddles the end
+    of the scored range, whole chunks lie past it), n_kv not a multiple of a block's keys
+    (waves of the last block run past n_kv), a second query per sequence."""
+    L = binding()
+    L.dsa_set_tuning("score_chunks_per_wave", cpw)
+    try:
+        _run(DEC.scaled(B=3, n_kv=5000), 5, kv_len=[5000, 3001, 70])
+        _run(DEC.scaled(B=2, n_q=2, n_kv=2113), 6, kv_len=[2113, 1500])
+        _run(workloads.LONG_DECODE_128K.scaled(B=2, n_kv=4099), 7)
+    finally:
+        L.dsa_set_tuning("score_chunks_per_wave", 0)
+
+
 @pytest.mark.parametrize("B,n_kv", [(1, 77), (2, 2100)])
 def test_decode_f16(B, n_kv):
     _run(workloads.LONG_DECODE_128K.scaled(B=B, n_kv=n_kv), 2)
