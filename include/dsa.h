@@ -133,7 +133,9 @@ int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* id
  * whole-row select when the candidates cannot hold the answer). A path the shape does not
  * allow falls back to the automatic choice. key "score_chunks_per_wave": 64-key chunks
  * each wave of the 16-bit decode scoring kernel walks (0 = automatic, else 1..64, taken
- * down to 1, 2, 4 or 8). Returns DSA_OK,
+ * down to 1, 2, 4 or 8). key "score_prefill_waves": waves per workgroup of the 16-bit
+ * scoring kernel for 8 or more queries per sequence, each wave taking 2 queries (0 =
+ * automatic, else 4 or 8). Returns DSA_OK,
  * or DSA_ERR_SHAPE for an unknown key or value. Process-wide; set it before launching work.
  */
 int dsa_set_tuning(const char* key, int value);

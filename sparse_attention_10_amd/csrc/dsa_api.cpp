@@ -71,6 +71,12 @@ int dsa_set_tuning(const char* key, int value) {
     dsa::g_score_cpw = value;
     return ok();
   }
+  if (std::strcmp(key, "score_prefill_waves") == 0) {
+    if (value != 0 && value != 4 && value != 8)
+      return fail(DSA_ERR_SHAPE, "score_prefill_waves must be 0, 4 or 8 (got %d)", value);
+    dsa::g_score_prefill_waves = value;
+    return ok();
+  }
   return fail(DSA_ERR_SHAPE, "dsa_set_tuning: unknown key '%s'", key);
 }
 

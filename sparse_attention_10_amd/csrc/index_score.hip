@@ -18,7 +18,9 @@
 
 namespace dsa {
 
-int g_score_cpw = 0;  // 64-key chunks per wave of the decode kernel (0 automatic)
+int g_score_cpw = 0;            // 64-key chunks per wave of the decode kernel (0 automatic)
+int g_score_prefill_waves = 0;  // waves per block of the prefill kernel (0 automatic)
+constexpr int kPrefillWaves = 8;
 
 // ---------------------------------------------------------------------------------------
 // plain kernel
@@ -78,8 +80,7 @@ template <> struct Mma16<f16_t> {
 __device__ __forceinline__ int key_lds_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
 // Query operand of one wave: heads 16*mt + (lane%16), k-step s covers dims 32*s + 8*(lane/16) .. +8.
-// Heads past H load head H-1 (the loads stay unconditional); their products are dropped in
-// head_reduce.
+// Heads past H load head H-1, so that the loads stay unconditional.
 template <typename T16>
 __device__ __forceinline__ void load_q_operand(const T16* q_bi, int H, int lane, i32x4 (&qa)[2][4]) {
   const int g = lane >> 4, r16 = lane & 15;
@@ -94,7 +95,7 @@ __device__ __forceinline__ void load_q_operand(const T16* q_bi, int H, int lane,
 }
 
 // Weights of the accumulator rows a lane holds: heads 16*mt + 4*(lane/16) + e (clamped to
-// H-1 like the query; head_reduce drops the rows past H).
+// H-1 like the query).
 __device__ __forceinline__ void load_w_rows(const float* w_bi, int H, int lane, float (&wr)[2][4]) {
   const int g = lane >> 4;
 #pragma unroll
@@ -103,21 +104,47 @@ __device__ __forceinline__ void load_w_rows(const float* w_bi, int H, int lane, 
     for (int e = 0; e < 4; ++e) wr[mt][e] = w_bi[min(16 * mt + 4 * g + e, H - 1)];
 }
 
-// relu, head weight and head sum of one 16-key N tile over the heads below H; every lane of
-// a column ends with the sum.
-__device__ __forceinline__ float head_reduce(const f32x4& a0, const f32x4& a1, const float (&wr)[2][4],
+// relu on the bit pattern: a set sign bit (negative values, -0.0, negative NaNs) gives +0.0,
+// everything else passes unchanged. One integer max, where fmaxf would first quiet both
+// operands.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// relu, head weight and the in-lane part of the head sum of one 16-key N tile: the lane's
+// 8 accumulator rows (heads 4*(lane/16) + e and 16 + 4*(lane/16) + e) of key column lane%16.
+// With fewer than 32 heads, rows past H (which hold copies of head H-1) are left out.
+template <bool FULLH>
+__device__ __forceinline__ float head_partial(const f32x4& a0, const f32x4& a1, const float (&wr)[2][4],
                                              int H, int g) {
   float p = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float t0 = wr[0][e] * fmaxf(a0[e], 0.f);
-    const float t1 = wr[1][e] * fmaxf(a1[e], 0.f);
-    p += 4 * g + e < H ? t0 : 0.f;
-    p += 16 + 4 * g + e < H ? t1 : 0.f;
+    if (FULLH) {
+      p = fmaf(wr[0][e], relu(a0[e]), p);
+      p = fmaf(wr[1][e], relu(a1[e]), p);
+    } else {
+      p += 4 * g + e < H ? wr[0][e] * relu(a0[e]) : 0.f;
+      p += 16 + 4 * g + e < H ? wr[1][e] * relu(a1[e]) : 0.f;
+    }
   }
-  p += shfl_xor(p, 16);
-  p += shfl_xor(p, 32);
   return p;
+}
+
+// Finishes the head sums of four N tiles at once: p[nt] holds lane row g = lane/16's part of
+// tile nt. Afterwards lane (g, c) holds the full sum of tile g at column c. Two exchanges
+// between the wave halves give the lower half tiles 0 and 1 and the upper half tiles 2 and
+// 3 summed over both halves; one exchange between neighbouring 16-lane rows finishes them.
+__device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float tile_reduce(float p0, float p1, float p2, float p3) {
+  // v_permlane32_swap: lanes 32..63 of the first operand trade places with lanes 0..31 of
+  // the second, so x[0] + x[1] sums lane i with lane i ^ 32 of the pair (p0 | p2).
+  const auto x = __builtin_amdgcn_permlane32_swap(fbits(p0), fbits(p2), false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(fbits(p1), fbits(p3), false, false);
+  const float a = __uint_as_float(x[0]) + __uint_as_float(x[1]);  // rows 0,1: tile 0; rows 2,3: tile 2
+  const float c = __uint_as_float(y[0]) + __uint_as_float(y[1]);  // rows 0,1: tile 1; rows 2,3: tile 3
+  // v_permlane16_swap: odd 16-lane rows of the first operand trade places with even rows
+  // of the second.
+  const auto z = __builtin_amdgcn_permlane16_swap(fbits(a), fbits(c), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -141,7 +168,7 @@ __device__ __forceinline__ void wave_lds_order() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename T16, int ITERS>
+template <typename T16, int ITERS, bool FULLH>
 __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
@@ -207,12 +234,9 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
         a0 = Mma16<T16>::run(qa[0][s], kv, a0);
         a1 = Mma16<T16>::run(qa[1][s], kv, a1);
       }
-      sc[nt] = head_reduce(a0, a1, wr, H, g);
+      sc[nt] = head_partial<FULLH>(a0, a1, wr, H, g);
     }
-    // lane group g keeps tile g (bit tests, which the compiler keeps as selects)
-    const float v01 = (g & 1) ? sc[1] : sc[0];
-    const float v23 = (g & 1) ? sc[3] : sc[2];
-    res[it] = (g & 2) ? v23 : v01;
+    res[it] = tile_reduce(sc[0], sc[1], sc[2], sc[3]);  // lane l: key kb + l
   }
   // stores last: a store guard is a branch, and the code-sinking pass would move the loads
   // of a later chunk past it, next to their use
@@ -228,14 +252,15 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
 // span in 64-key tiles held in two LDS buffers; the next tile is fetched into registers while
 // the current one feeds the MFMAs.
 // ---------------------------------------------------------------------------------------
-constexpr int kPreQPW = 2;
-constexpr int kPreQB = 4 * kPreQPW;
+constexpr int kPreQPW = 2;  // queries per wave
 
-template <typename T16>
-__global__ __launch_bounds__(256) void index_score_prefill_mfma(
+template <typename T16, int NWV, bool FULLH>
+__global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
     int n_q, int H, int n_kv, int key_span, float scale) {
+  constexpr int kPreQB = NWV * kPreQPW;     // queries per block
+  constexpr int kCPT = 1024 / (NWV * 64);  // 16-byte tile chunks each thread stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][64 * 256];
   __shared__ int s_limit[kPreQB];
   const int tid = threadIdx.x;
@@ -288,12 +313,13 @@ __global__ __launch_bounds__(256) void index_score_prefill_mfma(
   }
 
   const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k) + (long)b * n_kv * 256;
-  // tile staging: thread tid copies chunks (j * 256 + tid), j < 4, of the 64 x 16 chunk tile
-  i32x4 pre[4];
+  // tile staging: thread tid copies chunks (j * NWV * 64 + tid), j < kCPT, of the 64 x 16
+  // chunk tile
+  i32x4 pre[kCPT];
   auto issue = [&](int kb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = j * 16 + (tid >> 4);
+    for (int j = 0; j < kCPT; ++j) {
+      const int r = j * (NWV * 4) + (tid >> 4);
       const int row = kb + r;
       pre[j] = row < kc_end ? *reinterpret_cast<const i32x4*>(kseq + (long)row * 256 + (tid & 15) * 16)
                             : i32x4{0, 0, 0, 0};
@@ -305,8 +331,8 @@ __global__ __launch_bounds__(256) void index_score_prefill_mfma(
     const int kb = kbeg + tile * 64;
     uint8_t* buf = lds[tile & 1];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = j * 16 + (tid >> 4);
+    for (int j = 0; j < kCPT; ++j) {
+      const int r = j * (NWV * 4) + (tid >> 4);
       *reinterpret_cast<i32x4*>(buf + key_lds_off(r, tid & 15)) = pre[j];
     }
     __syncthreads();
@@ -327,15 +353,15 @@ __global__ __launch_bounds__(256) void index_score_prefill_mfma(
         }
       }
 #pragma unroll
-      for (int qq = 0; qq < kPreQPW; ++qq) sc[qq][nt] = head_reduce(acc[qq][0], acc[qq][1], wr[qq], H, g);
+      for (int qq = 0; qq < kPreQPW; ++qq) sc[qq][nt] = head_partial<FULLH>(acc[qq][0], acc[qq][1], wr[qq], H, g);
     }
     const int t = kb + lane;
 #pragma unroll
     for (int qq = 0; qq < kPreQPW; ++qq) {
-      if (qi[qq] < n_q && t < kend) {
-        const float v = g == 0 ? sc[qq][0] : g == 1 ? sc[qq][1] : g == 2 ? sc[qq][2] : sc[qq][3];
+      // cross-lane, so outside the store guard: every lane takes part
+      const float v = tile_reduce(sc[qq][0], sc[qq][1], sc[qq][2], sc[qq][3]);
+      if (qi[qq] < n_q && t < kend)
         scores[((long)b * n_q + qi[qq]) * n_kv + t] = t < lim[qq] ? scale * v : -INFINITY;
-      }
     }
   }
   // keys of the span past every query's limit are masked for all of them
@@ -355,17 +381,28 @@ template <typename T16>
 static hipError_t launch_mfma(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int n_kv,
                               float scale, hipStream_t stream) {
-  if (n_q >= kPreQB) {
-    const int qblocks = (n_q + kPreQB - 1) / kPreQB;
+  if (n_q >= 8) {
+    const int nwv = g_score_prefill_waves > 0 ? g_score_prefill_waves : kPrefillWaves;
+    const int qb = nwv * kPreQPW;
+    const int qblocks = (n_q + qb - 1) / qb;
     int spans = 2048 / max(1, qblocks * B);
     spans = max(1, min(spans, (n_kv + 255) / 256));
     int key_span = (n_kv + spans - 1) / spans;
     key_span = (key_span + 63) / 64 * 64;
     spans = (n_kv + key_span - 1) / key_span;
     dim3 grid(qblocks, spans, B);
-    hipLaunchKernelGGL(index_score_prefill_mfma<T16>, grid, dim3(256), 0, stream,
-                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv,
-                       key_span, scale);
+#define DSA_PREFILL_LAUNCH(N, FH)                                                              \
+  hipLaunchKernelGGL((index_score_prefill_mfma<T16, N, FH>), grid, dim3(N * 64), 0, stream,      \
+                     (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, key_span, scale)
+    const bool full = H == 32;
+    if (nwv == 8) {
+      if (full) DSA_PREFILL_LAUNCH(8, true);
+      else DSA_PREFILL_LAUNCH(8, false);
+    } else {
+      if (full) DSA_PREFILL_LAUNCH(4, true);
+      else DSA_PREFILL_LAUNCH(4, false);
+    }
+#undef DSA_PREFILL_LAUNCH
   } else {
     const long chunks = (n_kv + 255) / 256;  // 256-key block steps per query
     const long rows = (long)B * n_q;
@@ -376,8 +413,12 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
     const long xblocks = (chunks + iters - 1) / iters;
     dim3 grid((unsigned)xblocks, (unsigned)rows);
 #define DSA_DECODE_LAUNCH(N)                                                                  \
-  hipLaunchKernelGGL((index_score_decode_mfma<T16, N>), grid, dim3(256), 0, stream,             \
-                     (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale)
+  if (H == 32)                                                                                \
+    hipLaunchKernelGGL((index_score_decode_mfma<T16, N, true>), grid, dim3(256), 0, stream,     \
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale); \
+  else                                                                                        \
+    hipLaunchKernelGGL((index_score_decode_mfma<T16, N, false>), grid, dim3(256), 0, stream,    \
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale)
     switch (iters) {
       case 8: DSA_DECODE_LAUNCH(8); break;
       case 4: DSA_DECODE_LAUNCH(4); break;

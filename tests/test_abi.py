@@ -142,6 +142,10 @@ def test_tuning_switch(lib):
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", 0) == OK
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", 65) == E_SHAPE
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", -1) == E_SHAPE
+    for v in (4, 8, 0):
+        assert lib.dsa_set_tuning(b"score_prefill_waves", v) == OK
+    for v in (1, 2, 12, 16, -4):
+        assert lib.dsa_set_tuning(b"score_prefill_waves", v) == E_SHAPE
     assert lib.dsa_set_tuning(b"no_such_key", 1) == E_SHAPE
     assert lib.dsa_set_tuning(None, 1) == E_NULL
 

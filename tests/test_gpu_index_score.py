@@ -77,6 +77,19 @@ def test_prefill_causal_bf16(n_q, n_kv, start):
     _run(DEC.scaled(n_q=n_q, n_kv=n_kv, q_pos_start=start), 5)
 
 
+@pytest.mark.parametrize("waves", [4, 8])
+def test_prefill_waves_per_block(waves):
+    """Each workgroup shape of the prefill kernel: a query count that leaves the last block
+    partly empty, causal limits inside and across tiles, a second sequence."""
+    L = binding()
+    L.dsa_set_tuning("score_prefill_waves", waves)
+    try:
+        _run(DEC.scaled(B=2, n_q=45, n_kv=1100, q_pos_start=1100 - 45 - 300), 10)
+        _run(DEC.scaled(n_q=33, n_kv=700, q_pos_start=0), 11)
+    finally:
+        L.dsa_set_tuning("score_prefill_waves", 0)
+
+
 def test_prefill_kv_len_shorter_than_cache():
     wl = DEC.scaled(B=2, n_q=16, n_kv=400, q_pos_start=380)
     _run(wl, 6, kv_len=[390, 200])
