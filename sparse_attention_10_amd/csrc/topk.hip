@@ -750,7 +750,9 @@ __global__ __launch_bounds__(BLOCK) void topk_filtered_select(const float* __res
   __shared__ uint32_t s_cnt[BLOCK];
   __shared__ uint32_t s_tv[3];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long row = blockIdx.x;
+  // the same row -> XCD grouping as the filter workgroups, so the candidates they wrote are
+  // read from this XCD's L2
+  const long row = xcd_remap(blockIdx.x, gridDim.x);
   int* o_idx = out_idx + row * top_k;
   const long row_base = row * S * (long)seg_len;
 
