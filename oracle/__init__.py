@@ -264,6 +264,98 @@ def sparse_mla_split_merge_f64(qa, latent, idx, sm_scale: float, d_latent: int, 
 
 
 # ----------------------------------------------------------------------------
+# 4. indexer-input preparation: RoPE, Hadamard rotation, cache append
+# ----------------------------------------------------------------------------
+def encode(x64: np.ndarray, dtype: int) -> np.ndarray:
+    """float64 -> storage: float32, or bf16 / f16 bit patterns (uint16), each by rounding
+    to float32 first and then to the 16-bit format, to nearest even."""
+    x32 = np.asarray(x64, np.float64).astype(np.float32)
+    if dtype == F32:
+        return x32
+    if dtype == F16:
+        return x32.astype(np.float16).view(np.uint16)
+    if dtype == BF16:
+        u = x32.view(np.uint32).astype(np.uint64)
+        out = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+        out[np.isnan(x32)] = 0x7FC0
+        return out
+    raise ValueError(f"unknown dtype code {dtype}")
+
+
+def rope_neox_f64(x: np.ndarray, pos: np.ndarray, rope_base: float, n_rope: int = 64) -> np.ndarray:
+    """NeoX rotary embedding of the first n_rope dims of the last axis (ik_llama_opt log,
+    "Add GLM-5.2/DeepSeek-V3.2 DSA lightning indexer": the indexer q and k are split into a
+    64-dim rope part and a 64-dim nope part, the rope part is NeoX-roped, the two are
+    concatenated again). NeoX pairs dim i with dim i + n_rope/2 (rotate-half):
+        theta_i = pos * rope_base^(-2 i / n_rope),  i < n_rope / 2
+        y_i = x_i cos theta_i - x_{i+h} sin theta_i,  y_{i+h} = x_{i+h} cos theta_i + x_i sin theta_i
+    pos broadcasts against x[..., 0]; dims from n_rope on pass through."""
+    x = np.asarray(x, np.float64)
+    h = n_rope // 2
+    i = np.arange(h, dtype=np.float64)
+    theta = np.asarray(pos, np.float64)[..., None] * np.power(float(rope_base), -2.0 * i / n_rope)
+    c, s = np.cos(theta), np.sin(theta)
+    a, b = x[..., :h], x[..., h:n_rope]
+    y = x.copy()
+    y[..., :h] = a * c - b * s
+    y[..., h:n_rope] = b * c + a * s
+    return y
+
+
+def hadamard_f64(x: np.ndarray) -> np.ndarray:
+    """Orthonormal Walsh-Hadamard rotation of the last axis (ik_llama_opt log, "decode-correct
+    via persistent indexer-K cache": the indexer q and k are Hadamard-rotated, which keeps
+    (Hq).(Hk) = q.k). The matrix is Sylvester's, H_1 = [1], H_2n = [[H, H], [H, -H]], scaled
+    by 1/sqrt(n); it is symmetric, so x H = H x per row."""
+    x = np.asarray(x, np.float64)
+    n = x.shape[-1]
+    H = np.ones((1, 1))
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    assert H.shape[0] == n, "length must be a power of two"
+    return x @ (H / math.sqrt(n))
+
+
+def indexer_prep_f64(q_in, k_in, pos, rope_base: float, hadamard: bool = True):
+    """Indexer inputs of the new tokens, before scoring: RoPE on the rope part, then the
+    Hadamard rotation (same two log entries as above; the rotation acts on the roped vector).
+    q_in [B][n][H][128], k_in [B][n][128] (either may be None), pos [B][n] the new tokens'
+    positions. Returns (q, k) in float64."""
+    pos = np.asarray(pos)
+    q = k = None
+    if q_in is not None:
+        q = rope_neox_f64(q_in, pos[:, :, None], rope_base)
+        if hadamard:
+            q = hadamard_f64(q)
+    if k_in is not None:
+        k = rope_neox_f64(k_in, pos, rope_base)
+        if hadamard:
+            k = hadamard_f64(k)
+    return q, k
+
+
+def indexer_prep(q_in, k_in, pos, rope_base: float, out_dtype: int, hadamard: bool = True):
+    """indexer_prep_f64 rounded to the cache dtype (see encode)."""
+    q, k = indexer_prep_f64(q_in, k_in, pos, rope_base, hadamard)
+    return (None if q is None else encode(q, out_dtype)), (None if k is None else encode(k, out_dtype))
+
+
+def cache_append(cache: np.ndarray, rows: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """A copy of cache [B][n_kv][...] with row pos[b][i] replaced by rows[b][i] (ik_llama_opt
+    log, "decode-correct via persistent indexer-K cache": the batch's indexer keys are
+    written to the cache at kv_head; the same holds for the latent rows of the MLA cache).
+    Positions outside [0, n_kv) write nothing."""
+    out = np.array(cache, copy=True)
+    pos = np.asarray(pos)
+    for b in range(pos.shape[0]):
+        for i in range(pos.shape[1]):
+            p = int(pos[b, i])
+            if 0 <= p < out.shape[1]:
+                out[b, p] = rows[b, i]
+    return out
+
+
+# ----------------------------------------------------------------------------
 # the whole chain, as one decode/prefill step of one DSA layer
 # ----------------------------------------------------------------------------
 def dsa_step(inp: dict, wl) -> dict:

@@ -299,3 +299,88 @@ def pins_mla(fn, dense_fn=None, split_fn=None):
             o2, l2 = split_fn(qs, ls3, idx, 0.3, dl, F64, n_split, None)
             _close(o2, o1, 1e-12, f"split merge {n_split}")
             _close(l2, l1, 1e-12, f"split merge lse {n_split}")
+
+
+# ----------------------------------------------------------------------------
+# indexer-input preparation: rope(x, pos, base) -> [..., 128]; had(x) -> [..., 128];
+# prep(q_in, k_in, pos, base, hadamard) -> (q, k); append(cache, rows, pos) -> cache
+# ----------------------------------------------------------------------------
+def pins_rope(rope):
+    rng = _rng(11)
+    base = 10000.0
+    x = rng.standard_normal((5, 128))
+    # position 0 is the identity
+    _close(rope(x, np.zeros(5), base), x, 1e-15, "rope at position 0")
+    # NeoX pairing and sign: e_0 turns towards e_32 by the position itself (frequency 1)
+    for p in (1.0, 3.0, 1000.0):
+        e0 = np.zeros((1, 128)); e0[0, 0] = 1.0
+        e32 = np.zeros((1, 128)); e32[0, 32] = 1.0
+        y0 = rope(e0, np.array([p]), base)[0]
+        y32 = rope(e32, np.array([p]), base)[0]
+        want0 = np.zeros(128); want0[0] = math.cos(p); want0[32] = math.sin(p)
+        want32 = np.zeros(128); want32[32] = math.cos(p); want32[0] = -math.sin(p)
+        _close(y0, want0, 1e-12, f"e_0 at {p}")
+        _close(y32, want32, 1e-12, f"e_32 at {p}")
+    # frequencies: at position 1 pair i turns by base^(-2i/64); pair 31 by base^(-62/64)
+    for i in (1, 7, 31):
+        e = np.zeros((1, 128)); e[0, i] = 1.0
+        y = rope(e, np.array([1.0]), base)[0]
+        ang = math.atan2(y[i + 32], y[i])
+        assert abs(ang - base ** (-2.0 * i / 64.0)) < 1e-12, f"frequency of pair {i}"
+        assert np.count_nonzero(np.abs(y) > 1e-15) == 2, f"pair {i} leaks"
+    # the nope half passes through; every pair keeps its length
+    pos = rng.integers(0, 200000, size=5).astype(np.float64)
+    y = rope(x, pos, base)
+    _close(y[:, 64:], x[:, 64:], 0.0, "nope half unchanged")
+    _close(np.hypot(y[:, :32], y[:, 32:64]), np.hypot(x[:, :32], x[:, 32:64]), 1e-12, "pair lengths")
+    # rotations compose, and a score depends on the position difference only
+    a, b = 37.0, 1234.0
+    _close(rope(rope(x, np.full(5, a), base), np.full(5, b), base), rope(x, np.full(5, a + b), base),
+           1e-9, "R_a R_b = R_(a+b)")
+    q = rng.standard_normal((3, 128)); k = rng.standard_normal((3, 128))
+    for t in (5.0, 777.0):
+        d1 = np.sum(rope(q, np.full(3, 100.0), base) * rope(k, np.full(3, 40.0), base), axis=-1)
+        d2 = np.sum(rope(q, np.full(3, 100.0 + t), base) * rope(k, np.full(3, 40.0 + t), base), axis=-1)
+        _close(d1, d2, 1e-9, "relative position")
+
+
+def pins_hadamard(had):
+    rng = _rng(12)
+    x = rng.standard_normal((4, 128))
+    H = scipy.linalg.hadamard(128).astype(np.float64) / math.sqrt(128.0)
+    _close(had(x), x @ H, 1e-12, "scipy Hadamard")
+    _close(had(had(x)), x, 1e-12, "H H = I")
+    e0 = np.zeros((1, 128)); e0[0, 0] = 1.0
+    _close(had(e0), np.full((1, 128), 1.0 / math.sqrt(128.0)), 1e-15, "H e_0")
+
+
+def pins_prep(prep, rope, append):
+    rng = _rng(13)
+    base = 10000.0
+    B, n, H = 2, 3, 4
+    q_in = rng.standard_normal((B, n, H, 128))
+    k_in = rng.standard_normal((B, n, 128))
+    pos = rng.integers(0, 5000, size=(B, n))
+    q, k = prep(q_in, k_in, pos, base, True)
+    # scores are those of the roped vectors: the rotation keeps dot products, and it acts
+    # after the rope
+    qr = rope(q_in, pos[:, :, None].astype(np.float64), base)
+    kr = rope(k_in, pos.astype(np.float64), base)
+    _close(np.einsum("bnhd,bmd->bnhm", q, k), np.einsum("bnhd,bmd->bnhm", qr, kr), 1e-10,
+           "prep keeps rope scores")
+    # without the rotation, prep is the rope; at position 0 the rotation alone
+    q0, k0 = prep(q_in, k_in, np.zeros((B, n), np.int64), base, False)
+    _close(q0, q_in, 1e-15, "prep at position 0 without rotation")
+    q1, _ = prep(q_in, None, pos, base, False)
+    _close(q1, qr, 1e-12, "prep without rotation is the rope")
+    qh, kh = prep(q_in, k_in, np.zeros((B, n), np.int64), base, True)
+    Hm = scipy.linalg.hadamard(128).astype(np.float64) / math.sqrt(128.0)
+    _close(kh, k_in @ Hm, 1e-12, "prep at position 0 is the rotation")
+    # cache append: rows land at their positions, the rest stays, out of range is dropped
+    cache = rng.standard_normal((B, 10, 6))
+    rows = rng.standard_normal((B, 3, 6))
+    pp = np.array([[0, 9, 4], [7, -1, 10]])
+    out = append(cache, rows, pp)
+    want = cache.copy()
+    want[0, 0], want[0, 9], want[0, 4], want[1, 7] = rows[0, 0], rows[0, 1], rows[0, 2], rows[1, 0]
+    _close(out, want, 0.0, "cache append")

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads
-from oracle_pins import F64, pins_mla, pins_scores, pins_topk
+from oracle_pins import F64, pins_hadamard, pins_mla, pins_prep, pins_rope, pins_scores, pins_topk
 
 
 def test_score_pins():
@@ -189,3 +189,103 @@ def test_generator_is_per_tensor_and_seeded():
     # the rotation keeps the indexer statistics: std of q entries ~ 1/sqrt(128)
     q = oracle.decode(a["q"], workloads.BF16)
     assert abs(q.std() * math.sqrt(128) - 1.0) < 0.1
+
+
+# ---------------------------------------------------------------------------
+# indexer-input preparation
+# ---------------------------------------------------------------------------
+def test_prep_pins():
+    pins_rope(oracle.rope_neox_f64)
+    pins_hadamard(oracle.hadamard_f64)
+    pins_prep(oracle.indexer_prep_f64, oracle.rope_neox_f64, oracle.cache_append)
+
+
+def _rope_mutant(kind):
+    def fn(x, pos, base, n_rope=64):
+        x = np.asarray(x, np.float64)
+        h = n_rope // 2
+        i = np.arange(h, dtype=np.float64)
+        expo = -1.0 * i / n_rope if kind == "half_freq" else -2.0 * i / n_rope
+        p = np.asarray(pos, np.float64) + (1.0 if kind == "pos_plus_one" else 0.0)
+        th = p[..., None] * np.power(base, expo)
+        c, s = np.cos(th), np.sin(th)
+        y = x.copy()
+        if kind == "interleaved":  # GPT-J pairing (2i, 2i + 1)
+            a, b = x[..., 0:n_rope:2], x[..., 1:n_rope:2]
+            y[..., 0:n_rope:2] = a * c - b * s
+            y[..., 1:n_rope:2] = b * c + a * s
+            return y
+        lo = 64 if kind == "rope_on_nope" else 0
+        a, b = x[..., lo:lo + h], x[..., lo + h:lo + n_rope]
+        sg = -1.0 if kind == "sign" else 1.0
+        y[..., lo:lo + h] = a * c - sg * b * s
+        y[..., lo + h:lo + n_rope] = b * c + sg * a * s
+        return y
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["half_freq", "pos_plus_one", "interleaved", "rope_on_nope", "sign"])
+def test_rope_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_rope(_rope_mutant(kind))
+
+
+def test_rope_mutant_harness_is_faithful():
+    pins_rope(_rope_mutant("none"))
+
+
+def _had_mutant(kind):
+    def fn(x):
+        x = np.asarray(x, np.float64)
+        n = x.shape[-1]
+        H = np.ones((1, 1))
+        while H.shape[0] < n:
+            H = np.block([[H, H], [H, -H]]) if kind != "kron_order" else np.block([[H, -H], [H, H]])
+        if kind == "sequency":  # rows sorted by number of sign changes (Walsh order)
+            H = H[np.argsort(np.sum(H[:, 1:] != H[:, :-1], axis=1), kind="stable")]
+        scale = 1.0 if kind == "no_scale" else 1.0 / math.sqrt(n)
+        return x @ (H * scale)
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["kron_order", "sequency", "no_scale"])
+def test_hadamard_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_hadamard(_had_mutant(kind))
+
+
+def test_hadamard_mutant_harness_is_faithful():
+    pins_hadamard(_had_mutant("none"))
+
+
+def _prep_mutant(kind):
+    def fn(q_in, k_in, pos, base, hadamard=True):
+        pos = np.asarray(pos)
+        def one(x, p):
+            if kind == "hadamard_first" and hadamard:
+                return oracle.rope_neox_f64(oracle.hadamard_f64(x), p, base)
+            y = oracle.rope_neox_f64(x, p, base)
+            if hadamard:
+                y = oracle.hadamard_f64(y) * (math.sqrt(128.0) if kind == "unscaled" else 1.0)
+            return y
+        q = None if q_in is None else one(q_in, pos[:, :, None] + (1 if kind == "q_pos_shift" else 0))
+        k = None if k_in is None else one(k_in, pos)
+        return q, k
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["hadamard_first", "unscaled", "q_pos_shift"])
+def test_prep_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_prep(_prep_mutant(kind), oracle.rope_neox_f64, oracle.cache_append)
+
+
+def test_prep_mutant_harness_is_faithful():
+    pins_prep(_prep_mutant("none"), oracle.rope_neox_f64, oracle.cache_append)
+
+
+def test_cache_append_catches_off_by_one():
+    def bad(cache, rows, pos):
+        return oracle.cache_append(cache, rows, np.asarray(pos) + 1)
+    with pytest.raises(AssertionError):
+        pins_prep(oracle.indexer_prep_f64, oracle.rope_neox_f64, bad)
