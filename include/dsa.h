@@ -126,6 +126,42 @@ int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* id
                         int n_split, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Indexer inputs of newly appended tokens (ik_llama_opt "DSA lightning indexer" sub-commit:
+ * the indexer q and k split into a 64-dim rope part and a 64-dim nope part, NeoX rope on the
+ * rope part, concatenated again; "persistent indexer-K cache" sub-commit: q and k are
+ * Hadamard-rotated and the batch's keys are written into the key cache at their positions).
+ * For each new token n at position p = pos[b][n]:
+ *
+ *   rope:      y[i]    = x[i] cos(a_i) - x[i+32] sin(a_i),   y[i+32] = x[i+32] cos(a_i) + x[i] sin(a_i),
+ *              a_i = p * rope_base^(-i/32) for i < 32; dims 64..127 pass through
+ *   rotation:  z = H y / sqrt(128), H the 128 x 128 Sylvester Hadamard matrix (if hadamard != 0)
+ *   outputs:   q_out[b][n][h][:] = z(q_in[b][n][h][:]);  k_cache[b][p][:] = z(k_in[b][n][:]);
+ *              latent_cache[b][p][:] = latent_in[b][n][:] (copied unchanged)
+ *
+ * q_in          device, [B][n_new][H][128] fp32, or NULL (no query output)
+ * q_out         device, [B][n_new][H][128] out_dtype; NULL exactly when q_in is NULL
+ * k_in          device, [B][n_new][128] fp32, or NULL (no key appended)
+ * k_cache       device, [B][n_kv][128] out_dtype; rows pos[b][n] are written, no others;
+ *               NULL exactly when k_in is NULL
+ * latent_in     device, [B][n_new][row_bytes] raw rows (the 576-wide latent rows, any dtype),
+ *               or NULL (no latent row appended)
+ * latent_cache  device, [B][n_kv][row_bytes]; rows pos[b][n] are written; NULL exactly when
+ *               latent_in is NULL
+ * pos           device, [B][n_new] int32. A position outside [0, n_kv) writes no cache row
+ *               (the query is still roped with it). Two new tokens of one sequence with the
+ *               same position race.
+ * out_dtype     F32, BF16 or F16 (rounded to nearest even from fp32)
+ * row_bytes     bytes per latent row, a multiple of 16 (1152 for 576 bf16); ignored when
+ *               latent_in is NULL
+ * rope_base     the rope frequency base (> 0, finite)
+ * Sizes: B, n_new, n_kv >= 1; H >= 1 when q_in is given; head dim 128 with 64 rope dims.
+ * Pointers to 16-byte aligned memory. At least one of q_in, k_in, latent_in is non-NULL.
+ */
+int dsa_indexer_prep(const float* q_in, const float* k_in, const void* latent_in, const int32_t* pos,
+                     void* q_out, void* k_cache, void* latent_cache, int B, int n_new, int H, int n_kv,
+                     int row_bytes, int out_dtype, float rope_base, int hadamard, hipStream_t stream);
+
+/*
  * Tuning switches. They choose between kernels that compute identical results and
  * change only speed. key "topk_path": 0 = automatic, 1 = one workgroup per row,
  * 2 = two-stage (segments, then candidates), 3 = filtered (a sampled threshold picks

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 
 #include "kernels.h"
@@ -176,6 +177,33 @@ int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* id
   return hip_status(dsa::launch_sparse_mla(q_abs, latent, idx, kv_len, out, lse, B, n_q, Hm, n_kv, top_k,
                                            d_latent, d_rope, sm_scale, dtype, n_split, workspace, stream),
                     "dsa_sparse_mla_attn launch");
+}
+
+int dsa_indexer_prep(const float* q_in, const float* k_in, const void* latent_in, const int32_t* pos,
+                     void* q_out, void* k_cache, void* latent_cache, int B, int n_new, int H, int n_kv,
+                     int row_bytes, int out_dtype, float rope_base, int hadamard, hipStream_t stream) {
+  if (!pos) return fail(DSA_ERR_NULL, "dsa_indexer_prep: pos must be non-NULL");
+  if (!q_in && !k_in && !latent_in)
+    return fail(DSA_ERR_NULL, "dsa_indexer_prep: one of q_in, k_in, latent_in must be non-NULL");
+  if (!q_in != !q_out || !k_in != !k_cache || !latent_in != !latent_cache)
+    return fail(DSA_ERR_NULL, "dsa_indexer_prep: q_in/q_out, k_in/k_cache and latent_in/latent_cache "
+                              "must be given in pairs");
+  if (B < 1 || n_new < 1 || n_kv < 1 || (q_in && H < 1))
+    return fail(DSA_ERR_SHAPE, "dsa_indexer_prep: B=%d n_new=%d H=%d n_kv=%d out of range", B, n_new, H, n_kv);
+  if ((long long)B * n_new * (q_in ? H + 1 : 1) > INT_MAX || (long long)B * n_kv > (1LL << 34))
+    return fail(DSA_ERR_SHAPE, "dsa_indexer_prep: too many rows");
+  if (latent_in && (row_bytes < 16 || row_bytes % 16 != 0))
+    return fail(DSA_ERR_SHAPE, "dsa_indexer_prep: row_bytes=%d must be a positive multiple of 16", row_bytes);
+  if (!valid_dtype(out_dtype)) return fail(DSA_ERR_DTYPE, "dsa_indexer_prep: unknown out_dtype %d", out_dtype);
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return fail(DSA_ERR_SHAPE, "dsa_indexer_prep: rope_base must be positive and finite");
+  const void* ptrs[] = {q_in, k_in, latent_in, q_out, k_cache, latent_cache};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(DSA_ERR_UNSUPPORTED, "dsa_indexer_prep: pointers must be 16-byte aligned");
+  return hip_status(dsa::launch_indexer_prep(q_in, k_in, latent_in, pos, q_out, k_cache, latent_cache, B, n_new,
+                                             q_in ? H : 1, n_kv, row_bytes, out_dtype, std::log2((double)rope_base),
+                                             hadamard != 0, stream),
+                    "dsa_indexer_prep launch");
 }
 
 }  // extern "C"

@@ -37,4 +37,10 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
                              int n_kv, int top_k, int d_latent, int d_rope, float sm_scale,
                              int dtype, int n_split, void* workspace, hipStream_t stream);
 
+// indexer-input preparation (rope + Hadamard + cache append)
+hipError_t launch_indexer_prep(const float* q_in, const float* k_in, const void* latent_in, const int* pos,
+                               void* q_out, void* k_cache, void* latent_cache, int B, int n_new, int H,
+                               int n_kv, int row_bytes, int out_dtype, double log2_base, int hadamard,
+                               hipStream_t stream);
+
 }  // namespace dsa

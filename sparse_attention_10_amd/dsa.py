@@ -21,7 +21,7 @@ DSA_F32, DSA_BF16, DSA_F16 = 0, 1, 2
 _DTYPE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.float16: DSA_F16}
 
 EXPORTED = ("dsa_index_score", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
-            "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_set_tuning",
+            "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_indexer_prep", "dsa_set_tuning",
             "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -49,6 +49,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_sparse_mla_workspace_size.restype = S
     lib.dsa_sparse_mla_attn.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, S, P]
     lib.dsa_sparse_mla_attn.restype = I
+    lib.dsa_indexer_prep.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
+    lib.dsa_indexer_prep.restype = I
     lib.dsa_set_tuning.argtypes = [ctypes.c_char_p, I]
     lib.dsa_set_tuning.restype = I
     lib.dsa_status_string.argtypes = [I]
@@ -169,6 +171,55 @@ def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, idx: torch.Te
                                    Dc - d_latent, float(sm_scale), _DTYPE[q_abs.dtype], int(n_split),
                                    _ptr(workspace), wbytes, _stream(stream)), "dsa_sparse_mla_attn")
     return out
+
+
+def dsa_indexer_prep(pos: torch.Tensor, q_in: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
+                     k_in: Optional[torch.Tensor] = None, k_cache: Optional[torch.Tensor] = None,
+                     latent_in: Optional[torch.Tensor] = None, latent_cache: Optional[torch.Tensor] = None,
+                     rope_base: float = 10000.0, hadamard: bool = True, stream=None) -> None:
+    """pos [B][n_new] int32; q_in [B][n_new][H][128] fp32 -> q_out (same shape, bf16/f16/fp32);
+    k_in [B][n_new][128] fp32 -> rows pos of k_cache [B][n_kv][128]; latent_in [B][n_new][R]
+    -> rows pos of latent_cache [B][n_kv][R] (copied)."""
+    _dev(pos, "pos")
+    if pos.dtype != torch.int32 or pos.dim() != 2:
+        raise ValueError("pos must be int32 [B][n_new]")
+    B, n_new = pos.shape
+    H, n_kv, row_bytes, out_dtype = 1, None, 0, None
+    if (q_in is None) != (q_out is None) or (k_in is None) != (k_cache is None) \
+            or (latent_in is None) != (latent_cache is None):
+        raise ValueError("dsa_indexer_prep: inputs and outputs come in pairs")
+    if q_in is not None:
+        _dev(q_in, "q_in"); _dev(q_out, "q_out")
+        if q_in.dtype != torch.float32 or tuple(q_in.shape[:2]) != (B, n_new) or q_in.shape[-1] != 128 \
+                or q_in.dim() != 4 or tuple(q_out.shape) != tuple(q_in.shape):
+            raise ValueError("q_in must be fp32 [B][n_new][H][128] and q_out of the same shape")
+        H = q_in.shape[2]
+        out_dtype = _DTYPE[q_out.dtype]
+    if k_in is not None:
+        _dev(k_in, "k_in"); _dev(k_cache, "k_cache")
+        if k_in.dtype != torch.float32 or tuple(k_in.shape) != (B, n_new, 128) or k_cache.dim() != 3 \
+                or k_cache.shape[0] != B or k_cache.shape[2] != 128:
+            raise ValueError("k_in must be fp32 [B][n_new][128], k_cache [B][n_kv][128]")
+        if out_dtype is not None and _DTYPE[k_cache.dtype] != out_dtype:
+            raise ValueError("q_out and k_cache must share a dtype")
+        out_dtype = _DTYPE[k_cache.dtype]
+        n_kv = k_cache.shape[1]
+    if latent_in is not None:
+        _dev(latent_in, "latent_in"); _dev(latent_cache, "latent_cache")
+        if latent_in.dim() != 3 or tuple(latent_in.shape[:2]) != (B, n_new) or latent_cache.dim() != 3 \
+                or latent_cache.shape[0] != B or latent_cache.shape[2] != latent_in.shape[2] \
+                or latent_cache.dtype != latent_in.dtype:
+            raise ValueError("latent_in [B][n_new][R] and latent_cache [B][n_kv][R] of one dtype")
+        if n_kv is not None and latent_cache.shape[1] != n_kv:
+            raise ValueError("k_cache and latent_cache must have the same n_kv")
+        n_kv = latent_cache.shape[1]
+        row_bytes = latent_in.shape[2] * latent_in.element_size()
+    if n_kv is None:
+        n_kv = 1
+    _check(lib.dsa_indexer_prep(_ptr(q_in), _ptr(k_in), _ptr(latent_in), pos.data_ptr(), _ptr(q_out),
+                                _ptr(k_cache), _ptr(latent_cache), B, n_new, H, n_kv, row_bytes,
+                                DSA_BF16 if out_dtype is None else out_dtype, float(rope_base),
+                                1 if hadamard else 0, _stream(stream)), "dsa_indexer_prep")
 
 
 def dsa_set_tuning(key: str, value: int) -> None:

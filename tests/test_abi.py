@@ -162,3 +162,24 @@ def test_last_error_is_per_thread(lib):
     t.join()
     assert seen["err"] == b""
     assert lib.dsa_last_error() != b""
+
+
+def _prep(lib, q_in=FAKE, k_in=FAKE, lat=None, pos=FAKE, q_out=FAKE, k_cache=FAKE, lat_cache=None,
+          B=1, n_new=1, H=32, n_kv=64, row_bytes=1152, od=1, base=10000.0, had=1):
+    return lib.dsa_indexer_prep(q_in, k_in, lat, pos, q_out, k_cache, lat_cache, B, n_new, H, n_kv,
+                                row_bytes, od, base, had, None)
+
+
+def test_indexer_prep_rejects_on_host(lib):
+    assert _prep(lib, pos=None) == E_NULL
+    assert _prep(lib, q_in=None, k_in=None) == E_NULL               # nothing to do
+    assert _prep(lib, q_out=None) == E_NULL                         # unpaired
+    assert _prep(lib, k_cache=None) == E_NULL
+    assert _prep(lib, lat=FAKE) == E_NULL                           # latent without its cache
+    for kw in ({"B": 0}, {"n_new": 0}, {"H": 0}, {"n_kv": 0}):
+        assert _prep(lib, **kw) == E_SHAPE, kw
+    assert _prep(lib, lat=FAKE, lat_cache=FAKE, row_bytes=1000) == E_SHAPE
+    assert _prep(lib, od=9) == E_DTYPE
+    for base in (0.0, -1.0, float("inf"), float("nan")):
+        assert _prep(lib, base=base) == E_SHAPE, base
+    assert _prep(lib, k_cache=FAKE + 8) == E_UNSUP

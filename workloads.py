@@ -43,6 +43,7 @@ DTYPE_NAMES = {F32: "f32", BF16: "bf16", F16: "f16"}
 
 # tensor tags for the per-tensor streams
 _TAG_Q, _TAG_K, _TAG_W, _TAG_QA, _TAG_LAT = 1, 2, 3, 4, 5
+_TAG_PQ, _TAG_PK, _TAG_PLAT = 6, 7, 8
 
 
 @dataclasses.dataclass(frozen=True)
@@ -186,6 +187,21 @@ def gen_all(wl: Workload, seed: int, parts=("q", "k", "w", "qa", "latent")) -> D
     out["kv_len"] = wl.kv_len()
     out["q_pos"] = wl.q_pos()
     return out
+
+
+def gen_prep(wl: Workload, seed: int) -> Dict[str, np.ndarray]:
+    """Inputs of the indexer-input preparation for the workload's new tokens (its queries):
+    fp32 indexer query and key rows before rope and rotation, drawn like the cached ones
+    (N(0, 1) / sqrt(128)); the new 576-wide latent rows in the MLA dtype; the positions
+    (the queries' cache positions). q_in [B][n_q][H][128], k_in [B][n_q][128],
+    latent_in [B][n_q][Dc], pos [B][n_q] int32."""
+    s = 1.0 / math.sqrt(wl.D)
+    q = np.stack([_draw_normal(_rng(seed, wl.wid, b, _TAG_PQ), (wl.n_q, wl.H, wl.D), s) for b in range(wl.B)])
+    k = np.stack([_draw_normal(_rng(seed, wl.wid, b, _TAG_PK), (wl.n_q, wl.D), s) for b in range(wl.B)])
+    lat = np.stack([_draw_normal(_rng(seed, wl.wid, b, _TAG_PLAT), (wl.n_q, wl.Dc), wl.latent_std)
+                    for b in range(wl.B)])
+    return {"q_in": q.astype(np.float32), "k_in": k.astype(np.float32),
+            "latent_in": round_to(lat, wl.mla_dtype), "pos": wl.q_pos()}
 
 
 def random_scores(rows: int, n: int, seed: int, tie_frac: float = 0.0, neg_inf_frac: float = 0.0,
