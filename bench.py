@@ -52,6 +52,15 @@ def algorithmic_bytes(wl):
     }
 
 
+def prep_bytes(wl):
+    """Bytes of the indexer-input preparation of the step's new tokens: fp32 q and k in, q
+    out and the k row in the indexer dtype, the latent row in and out, the positions."""
+    isz = 4 if wl.idx_dtype == 0 else 2
+    msz = 4 if wl.mla_dtype == 0 else 2
+    tok = wl.B * wl.n_q
+    return tok * (wl.H * wl.D * (4 + isz) + wl.D * (4 + isz) + 2 * wl.Dc * msz + 4)
+
+
 def score_flops(wl, causal=True):
     """Indexer contraction flops (2 * H * D per scored (query, key) pair)."""
     import numpy as np
@@ -161,6 +170,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--scrub-mib", type=int, default=0,
+                    help="also time eager steps with a buffer of this many MiB written between them "
+                         "(steps that start with cold caches)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the bench, run 3 device-to-device copies of this many MiB (the known-size "
                          "copy that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -283,6 +295,72 @@ def main():
         torch.cuda.synchronize()
         step_s = (time.perf_counter() - t0) / args.steps
 
+    # indexer-input preparation of the step's new tokens (the stage upstream of the scores):
+    # timed on its own with HIP events, after the timed region, writing the same cache rows
+    prep_in = workloads.gen_prep(wl, args.seed)
+    p_q = to_dev(prep_in["q_in"])
+    p_k = to_dev(prep_in["k_in"])
+    p_lat = to_dev(prep_in["latent_in"], wl.mla_dtype)
+    p_pos = to_dev(prep_in["pos"])
+    p_qout = torch.empty(q.shape, dtype=q.dtype, device=dev)
+
+    def call_prep():
+        dsa.dsa_indexer_prep(p_pos, q_in=p_q, q_out=p_qout, k_in=p_k, k_cache=k, latent_in=p_lat,
+                             latent_cache=lat)
+
+    for _ in range(5):
+        call_prep()
+    torch.cuda.synchronize()
+    # a few microseconds of GPU work per call: the host cannot queue single calls fast enough,
+    # so a graph of 20 calls is replayed and the time per call taken from that
+    pg = torch.cuda.CUDAGraph()
+    pside = torch.cuda.Stream()
+    pside.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(pside):
+        call_prep()
+    torch.cuda.current_stream().wait_stream(pside)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(pg):
+        for _ in range(20):
+            call_prep()
+    pg.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // 20)
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe0.record(stream)
+    for _ in range(reps):
+        pg.replay()
+    pe1.record(stream)
+    torch.cuda.synchronize()
+    prep_ms = pe0.elapsed_time(pe1) / (reps * 20)
+
+    # a plain device-to-device copy of 1 GiB: the bandwidth a streaming kernel reaches here
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record(stream)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    ce1.record(stream)
+    ce1.synchronize()
+    copy_gbs = 3 * 2 * (1 << 30) / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    del csrc, cdst
+
+    scrub = None
+    if args.scrub_mib > 0:
+        buf = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device=dev)
+        se = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):  # the fill runs between the event pairs, outside them
+            buf.fill_(i & 255)
+            se[i][0].record(stream)
+            step()
+            se[i][1].record(stream)
+        torch.cuda.synchronize()
+        tot = sum(a.elapsed_time(b) for a, b in se)
+        scrub = {"scrub_mib": args.scrub_mib, "ms_per_step": round(tot / args.steps, 4)}
+        del buf
+
     ab = algorithmic_bytes(wl)
     tokens = rows
     value = tokens / step_s
@@ -326,15 +404,23 @@ def main():
         "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
         "kernels_gbs": {k_: round(ab[k_] / (per[k_] * 1e-3) / 1e9, 1) for k_ in per},
         "roofline": roof,
+        "copy_gbs": round(copy_gbs, 1),
+        "score_frac_of_copy": round(achieved / copy_gbs, 4) if not prefill else None,
+        "indexer_prep": {"ms": round(prep_ms, 4), "bytes": prep_bytes(wl),
+                         "gbs": round(prep_bytes(wl) / (prep_ms * 1e-3) / 1e9, 1),
+                         "frac": round(prep_bytes(wl) / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "tokens": rows},
         "context": "whole-model figures on other hardware (not comparable): GLM-5.2 IQ2_XXS greedy decode "
                    "~0.3-0.4 tokens/s and 200-token prefill ~3.2 tokens/s on an RTX 4060 Ti 16GB with SSD "
                    "expert streaming",
     }
+    if scrub is not None:
+        result["cold_cache_eager"] = scrub
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     if args.copy_calibration_mib > 0:
-        del q, k, w, qa, lat, scores, idx, out, lse, ws_t, ws_m
+        del q, k, w, qa, lat, scores, idx, out, lse, ws_t, ws_m, p_q, p_k, p_lat, p_qout
         n = args.copy_calibration_mib * 1024 * 1024
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -25,6 +25,11 @@ namespace dsa {
 
 constexpr int kPrepThreads = 256;  // 16 rows of 128 dims per workgroup
 
+// base^(-i/32) / (2 pi) for the 32 rope pairs, in double (passed by value with the launch)
+struct RopeTurns {
+  double turns[32];
+};
+
 __device__ __forceinline__ uint32_t pack2_f16(float a, float b) {
   const _Float16 ha = (_Float16)a, hb = (_Float16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
@@ -52,7 +57,7 @@ __device__ __forceinline__ void store8(uint8_t* dst, const float (&v)[8], int ou
 __global__ __launch_bounds__(kPrepThreads) void indexer_prep_rows(
     const float* __restrict__ q_in, const float* __restrict__ k_in, const int* __restrict__ pos,
     uint8_t* __restrict__ q_out, uint8_t* __restrict__ k_cache, int q_rows, int k_rows, int H,
-    int n_new, int n_kv, int out_dtype, double log2_base, int hadamard) {
+    int n_new, int n_kv, int out_dtype, RopeTurns freq, int hadamard) {
   const int t = threadIdx.x & 15;
   const long r = (long)blockIdx.x * (kPrepThreads / 16) + (threadIdx.x >> 4);
   if (r >= (long)q_rows + k_rows) return;  // whole 16-lane groups leave together
@@ -69,18 +74,16 @@ __global__ __launch_bounds__(kPrepThreads) void indexer_prep_rows(
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
 
-  // NeoX rope on dims 0..63. The angle is formed and reduced modulo 2 pi in double (positions
-  // reach 2^17 and more, where a float angle would be off by 1e-2 rad), then turned into
-  // cos / sin in float.
+  // NeoX rope on dims 0..63. The angle in turns, p * base^(-i/32) / (2 pi), is formed in double
+  // and its fractional part taken there (positions reach 2^17 and more, where a float angle
+  // would be off by 1e-2 rad); cos / sin then run in float on an angle in [-pi, pi].
   {
     float c[8], s[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int f = 8 * (t & 3) + j;  // pair index i of dims (i, i + 32)
-      const double inv = exp2(-(double)f * (1.0 / 32.0) * log2_base);
-      const double ang = (double)p * inv;
-      const double twopi = 6.283185307179586476925287;
-      const float red = (float)(ang - twopi * rint(ang / twopi));
+      const double turns = (double)p * freq.turns[f];
+      const float red = (float)((turns - rint(turns)) * 6.283185307179586476925287);
       sincosf(red, &s[j], &c[j]);
     }
     float y[8];
@@ -144,6 +147,8 @@ hipError_t launch_indexer_prep(const float* q_in, const float* k_in, const void*
                                void* q_out, void* k_cache, void* latent_cache, int B, int n_new, int H,
                                int n_kv, int row_bytes, int out_dtype, double log2_base, int hadamard,
                                hipStream_t stream) {
+  RopeTurns freq;
+  for (int i = 0; i < 32; ++i) freq.turns[i] = exp2(-(double)i / 32.0 * log2_base) / 6.283185307179586476925287;
   const long n_tok = (long)B * n_new;
   const long q_rows = q_in ? n_tok * H : 0;
   const long k_rows = k_in ? n_tok : 0;
@@ -151,7 +156,7 @@ hipError_t launch_indexer_prep(const float* q_in, const float* k_in, const void*
     const long blocks = (q_rows + k_rows + 15) / 16;
     hipLaunchKernelGGL(indexer_prep_rows, dim3((unsigned)blocks), dim3(kPrepThreads), 0, stream, q_in, k_in, pos,
                        (uint8_t*)q_out, (uint8_t*)k_cache, (int)q_rows, (int)k_rows, H, n_new, n_kv, out_dtype,
-                       log2_base, hadamard);
+                       freq, hadamard);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
