@@ -71,6 +71,25 @@ int dsa_index_score(const void* q, const void* k_cache, const float* w, const in
                     int q_dtype, int k_dtype, float scale, hipStream_t stream);
 
 /*
+ * dsa_index_score with the attention-sink boost (ik_llama_opt log: "DSA_SINK" force-inclusion
+ * in the persistent-cache sub-commit, "per-sequence attention sink" and "UPDATE 6"
+ * sub-commits: the first n_sink keys of the query's own sequence, counted from the sequence's
+ * first present position, get a large additive boost so that top-k always keeps them):
+ *
+ *   scores[b][i][t] += sink_boost  for sink_start[b] <= t < sink_start[b] + n_sink, t not masked
+ *
+ * (the addition is a float32 add to the finished score; masked keys stay -inf). sink_start:
+ * device [B] int32, each sequence's first present position, or NULL for 0 in every sequence.
+ * n_sink >= 0 (0: same as dsa_index_score); sink_boost finite (the pages use 1e20, far above
+ * any score, so the boosted keys tie and top-k keeps the lower positions first). Every other
+ * argument and rule is that of dsa_index_score.
+ */
+int dsa_index_score_sink(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
+                         const int32_t* q_pos, const int32_t* sink_start, int n_sink, float sink_boost,
+                         float* scores, int B, int n_q, int H, int D, int n_kv, int q_dtype, int k_dtype,
+                         float scale, hipStream_t stream);
+
+/*
  * Top-k selection (ik_llama_opt "DSA lightning indexer" sub-commit: top_k of
  * min(top_k, n_tokens), used as a set; "persistent indexer-K cache" sub-commit: the same
  * set from a descending argsort).

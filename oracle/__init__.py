@@ -109,6 +109,27 @@ def index_score(q, k, w, kv_len=None, q_pos=None, scale: float = 1.0,
     return index_score_f64(q, k, w, kv_len, q_pos, scale, q_dtype, k_dtype).astype(np.float32)
 
 
+def index_score_sink(q, k, w, kv_len=None, q_pos=None, scale: float = 1.0, q_dtype: int = F32,
+                     k_dtype: int = F32, sink_start=None, n_sink: int = 0, sink_boost: float = 1e20) -> np.ndarray:
+    """index_score with the attention-sink boost: the float32 boost is added (in float32) to the
+    float32 scores of keys sink_start[b] <= t < sink_start[b] + n_sink that are not masked
+    (ik_llama_opt log: "DSA_SINK" force-inclusion, a boost so the sink always survives top-k;
+    "per-sequence attention sink": only the query's own sequence's sink, as an additive F32
+    input; "UPDATE 6": anchored on the sequence's first present position). sink_start [B] or
+    None (0 for every sequence)."""
+    S = index_score(q, k, w, kv_len, q_pos, scale, q_dtype, k_dtype)
+    if n_sink <= 0:
+        return S
+    B, n_q, n_kv = S.shape
+    start = np.zeros(B, np.int64) if sink_start is None else np.asarray(sink_start, np.int64)
+    t = np.arange(n_kv)
+    for b in range(B):
+        in_sink = (t >= start[b]) & (t < start[b] + n_sink)
+        # masked keys are -inf, and -inf + boost stays -inf
+        S[b][:, in_sink] = S[b][:, in_sink] + np.float32(sink_boost)
+    return S
+
+
 # ----------------------------------------------------------------------------
 # 2. top-k selection
 # ----------------------------------------------------------------------------

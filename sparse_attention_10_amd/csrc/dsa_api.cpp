@@ -81,30 +81,46 @@ int dsa_set_tuning(const char* key, int value) {
   return fail(DSA_ERR_SHAPE, "dsa_set_tuning: unknown key '%s'", key);
 }
 
+static int index_score_checked(const char* fn, const void* q, const void* k_cache, const float* w,
+                               const int32_t* kv_len, const int32_t* q_pos, float* scores, int B, int n_q,
+                               int H, int D, int n_kv, int q_dtype, int k_dtype, float scale,
+                               dsa::SinkArgs sink, hipStream_t stream) {
+  if (!q || !k_cache || !w || !scores)
+    return fail(DSA_ERR_NULL, "%s: q, k_cache, w and scores must be non-NULL", fn);
+  if (B < 1 || n_q < 1 || H < 1 || D < 1 || n_kv < 1)
+    return fail(DSA_ERR_SHAPE, "%s: B=%d n_q=%d H=%d D=%d n_kv=%d must all be >= 1", fn, B, n_q, H, D, n_kv);
+  if ((long long)B * n_q > INT_MAX || (long long)B * n_q * n_kv > (1LL << 40) || n_kv > (1 << 30))
+    return fail(DSA_ERR_SHAPE, "%s: n_kv (at most 2^30) or B*n_q*n_kv too large", fn);
+  if (!valid_dtype(q_dtype) || !valid_dtype(k_dtype))
+    return fail(DSA_ERR_DTYPE, "%s: unknown dtype (q %d, k %d)", fn, q_dtype, k_dtype);
+  if (q_dtype != k_dtype)
+    return fail(DSA_ERR_DTYPE, "%s: q_dtype (%d) must equal k_dtype (%d)", fn, q_dtype, k_dtype);
+  const bool mfma = D == 128 && H <= 32 && q_dtype != DSA_F32;
+  if (mfma && (!aligned16(q) || !aligned16(k_cache)))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: q and k_cache must be 16-byte aligned", fn);
+  if (!mfma && (long long)H * D > 16384)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: H*D = %lld exceeds 16384 outside the MFMA shape (16-bit, D=128, H<=32)",
+                fn, (long long)H * D);
+  return hip_status(dsa::launch_index_score(q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv, q_dtype,
+                                            scale, sink, stream),
+                    fn);
+}
+
 int dsa_index_score(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
                     const int32_t* q_pos, float* scores, int B, int n_q, int H, int D, int n_kv,
                     int q_dtype, int k_dtype, float scale, hipStream_t stream) {
-  if (!q || !k_cache || !w || !scores)
-    return fail(DSA_ERR_NULL, "dsa_index_score: q, k_cache, w and scores must be non-NULL");
-  if (B < 1 || n_q < 1 || H < 1 || D < 1 || n_kv < 1)
-    return fail(DSA_ERR_SHAPE, "dsa_index_score: B=%d n_q=%d H=%d D=%d n_kv=%d must all be >= 1", B, n_q,
-                H, D, n_kv);
-  if ((long long)B * n_q > INT_MAX || (long long)B * n_q * n_kv > (1LL << 40) || n_kv > (1 << 30))
-    return fail(DSA_ERR_SHAPE, "dsa_index_score: n_kv (at most 2^30) or B*n_q*n_kv too large");
-  if (!valid_dtype(q_dtype) || !valid_dtype(k_dtype))
-    return fail(DSA_ERR_DTYPE, "dsa_index_score: unknown dtype (q %d, k %d)", q_dtype, k_dtype);
-  if (q_dtype != k_dtype)
-    return fail(DSA_ERR_DTYPE, "dsa_index_score: q_dtype (%d) must equal k_dtype (%d)", q_dtype, k_dtype);
-  const bool mfma = D == 128 && H <= 32 && q_dtype != DSA_F32;
-  if (mfma && (!aligned16(q) || !aligned16(k_cache)))
-    return fail(DSA_ERR_UNSUPPORTED, "dsa_index_score: q and k_cache must be 16-byte aligned");
-  if (!mfma && (long long)H * D > 16384)
-    return fail(DSA_ERR_UNSUPPORTED,
-                "dsa_index_score: H*D = %lld exceeds 16384 outside the MFMA shape (16-bit, D=128, H<=32)",
-                (long long)H * D);
-  return hip_status(dsa::launch_index_score(q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv,
-                                            q_dtype, scale, stream),
-                    "dsa_index_score launch");
+  return index_score_checked("dsa_index_score", q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv,
+                             q_dtype, k_dtype, scale, dsa::SinkArgs{nullptr, 0, 0.f}, stream);
+}
+
+int dsa_index_score_sink(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
+                         const int32_t* q_pos, const int32_t* sink_start, int n_sink, float sink_boost,
+                         float* scores, int B, int n_q, int H, int D, int n_kv, int q_dtype, int k_dtype,
+                         float scale, hipStream_t stream) {
+  if (n_sink < 0) return fail(DSA_ERR_SHAPE, "dsa_index_score_sink: n_sink=%d must be >= 0", n_sink);
+  if (!std::isfinite(sink_boost)) return fail(DSA_ERR_SHAPE, "dsa_index_score_sink: sink_boost must be finite");
+  return index_score_checked("dsa_index_score_sink", q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv,
+                             q_dtype, k_dtype, scale, dsa::SinkArgs{sink_start, n_sink, sink_boost}, stream);
 }
 
 size_t dsa_topk_workspace_size(int rows, int n_kv, int top_k) {

@@ -14,6 +14,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <limits.h>
 #include <math.h>
 
 namespace dsa {
@@ -22,6 +23,23 @@ int g_score_cpw = 0;            // 64-key chunks per wave of the decode kernel (
 int g_score_prefill_waves = 0;  // waves per block of the prefill kernel (0 automatic)
 constexpr int kPrefillWaves = 8;
 
+// Attention-sink range [lo, hi) of sequence b (ik_llama_opt log, "per-sequence attention sink"
+// and "UPDATE 6" sub-commits: the first n_sink keys of the query's own sequence, counted from
+// its first present position, get a large additive boost so that top-k always keeps them).
+struct SinkRange {
+  int lo, hi;
+  float boost;
+  __device__ __forceinline__ float add(int t, float v) const { return t >= lo && t < hi ? v + boost : v; }
+};
+__device__ __forceinline__ SinkRange sink_range(const SinkArgs& s, int b) {
+  SinkRange r{0, 0, s.boost};
+  if (s.n > 0) {
+    r.lo = s.start ? s.start[b] : 0;
+    r.hi = (int)min((long)r.lo + s.n, (long)INT_MAX);
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------------------
 // plain kernel
 // ---------------------------------------------------------------------------------------
@@ -29,7 +47,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void index_score_plain(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
-    int n_q, int H, int D, int n_kv, float scale) {
+    int n_q, int H, int D, int n_kv, float scale, SinkArgs sink) {
   extern __shared__ float qs[];  // [H][D] of this query
   const int bi = blockIdx.y;
   const int b = bi / n_q, i = bi - b * n_q;
@@ -53,7 +71,7 @@ __global__ __launch_bounds__(256) void index_score_plain(
     for (int d = 0; d < D; ++d) dot = fmaf(qs[h * D + d], load_as_f32(kp, d), dot);
     s = fmaf(wp[h], fmaxf(dot, 0.f), s);
   }
-  out[t] = scale * s;
+  out[t] = sink_range(sink, b).add(t, scale * s);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -172,7 +190,7 @@ template <typename T16, int ITERS, bool FULLH>
 __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
-    int n_q, int H, int n_kv, float scale) {
+    int n_q, int H, int n_kv, float scale, SinkArgs sink) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDecWaves][64 * 256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -240,10 +258,11 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
   }
   // stores last: a store guard is a branch, and the code-sinking pass would move the loads
   // of a later chunk past it, next to their use
+  const SinkRange sk = sink_range(sink, b);
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int t = kb_of(it) + lane;
-    if (t < n_kv) out[t] = t < limit ? scale * res[it] : -INFINITY;
+    if (t < n_kv) out[t] = t < limit ? sk.add(t, scale * res[it]) : -INFINITY;
   }
 }
 
@@ -258,7 +277,7 @@ template <typename T16, int NWV, bool FULLH>
 __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
-    int n_q, int H, int n_kv, int key_span, float scale) {
+    int n_q, int H, int n_kv, int key_span, float scale, SinkArgs sink) {
   constexpr int kPreQB = NWV * kPreQPW;     // queries per block
   constexpr int kCPT = 1024 / (NWV * 64);  // 16-byte tile chunks each thread stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][64 * 256];
@@ -285,6 +304,7 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
   for (int j = 0; j < kPreQB; ++j) kmax = max(kmax, s_limit[j]);
 
   const int kbeg = blockIdx.y * key_span;
+  const SinkRange sk = sink_range(sink, b);
   const int kend = min(n_kv, kbeg + key_span);
   const int kc_end = min(kend, kmax);  // keys [kbeg, kc_end) need the contraction
 
@@ -395,7 +415,7 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
       // cross-lane, so outside the store guard: every lane takes part
       const float v = tile_reduce(sc[qq][0], sc[qq][1], sc[qq][2], sc[qq][3]);
       if (qi[qq] < n_q && t < kend)
-        scores[((long)b * n_q + qi[qq]) * n_kv + t] = t < lim[qq] ? scale * v : -INFINITY;
+        scores[((long)b * n_q + qi[qq]) * n_kv + t] = t < lim[qq] ? sk.add(t, scale * v) : -INFINITY;
     }
   }
   // keys of the span past every query's limit are masked for all of them
@@ -414,7 +434,7 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
 template <typename T16>
 static hipError_t launch_mfma(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int n_kv,
-                              float scale, hipStream_t stream) {
+                              float scale, SinkArgs sink, hipStream_t stream) {
   if (n_q >= 8) {
     const int nwv = g_score_prefill_waves > 0 ? g_score_prefill_waves : kPrefillWaves;
     const int qb = nwv * kPreQPW;
@@ -427,7 +447,7 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
     dim3 grid(qblocks, spans, B);
 #define DSA_PREFILL_LAUNCH(N, FH)                                                              \
   hipLaunchKernelGGL((index_score_prefill_mfma<T16, N, FH>), grid, dim3(N * 64), 0, stream,      \
-                     (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, key_span, scale)
+                     (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, key_span, scale, sink)
     const bool full = H == 32;
     if (nwv == 8) {
       if (full) DSA_PREFILL_LAUNCH(8, true);
@@ -449,10 +469,10 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
 #define DSA_DECODE_LAUNCH(N)                                                                  \
   if (H == 32)                                                                                \
     hipLaunchKernelGGL((index_score_decode_mfma<T16, N, true>), grid, dim3(256), 0, stream,     \
-                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale); \
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, sink); \
   else                                                                                        \
     hipLaunchKernelGGL((index_score_decode_mfma<T16, N, false>), grid, dim3(256), 0, stream,    \
-                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale)
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, sink)
     switch (iters) {
       case 8: DSA_DECODE_LAUNCH(8); break;
       case 4: DSA_DECODE_LAUNCH(4); break;
@@ -466,24 +486,24 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
 
 hipError_t launch_index_score(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int D,
-                              int n_kv, int dtype, float scale, hipStream_t stream) {
+                              int n_kv, int dtype, float scale, SinkArgs sink, hipStream_t stream) {
   const bool mfma_ok = D == 128 && H <= 32 && (dtype == kBF16 || dtype == kF16);
   if (mfma_ok) {
     if (dtype == kBF16)
-      return launch_mfma<bf16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, stream);
-    return launch_mfma<f16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, stream);
+      return launch_mfma<bf16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, sink, stream);
+    return launch_mfma<f16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, sink, stream);
   }
   dim3 grid((n_kv + 255) / 256, (unsigned)((long)B * n_q));
   const size_t shm = (size_t)H * D * sizeof(float);
   if (dtype == kF32)
     hipLaunchKernelGGL(index_score_plain<float>, grid, dim3(256), shm, stream, (const float*)q,
-                       (const float*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale);
+                       (const float*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale, sink);
   else if (dtype == kBF16)
     hipLaunchKernelGGL(index_score_plain<bf16_t>, grid, dim3(256), shm, stream, (const bf16_t*)q,
-                       (const bf16_t*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale);
+                       (const bf16_t*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale, sink);
   else
     hipLaunchKernelGGL(index_score_plain<f16_t>, grid, dim3(256), shm, stream, (const f16_t*)q,
-                       (const f16_t*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale);
+                       (const f16_t*)k, w, kv_len, q_pos, scores, n_q, H, D, n_kv, scale, sink);
   return hipGetLastError();
 }
 

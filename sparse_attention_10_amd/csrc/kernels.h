@@ -10,11 +10,19 @@ namespace dsa {
 
 constexpr int kF32 = 0, kBF16 = 1, kF16 = 2;
 
+// Attention-sink boost: scores of keys [start[b], start[b] + n) of sequence b get + boost
+// (start NULL: 0; n = 0: off). Masked keys stay -inf.
+struct SinkArgs {
+  const int* start;
+  int n;
+  float boost;
+};
+
 extern int g_score_cpw;  // 64-key chunks per wave of the decode scoring kernel, 0 automatic
 extern int g_score_prefill_waves;  // waves per block of the prefill scoring kernel (4 or 8), 0 automatic
 hipError_t launch_index_score(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int D,
-                              int n_kv, int dtype, float scale, hipStream_t stream);
+                              int n_kv, int dtype, float scale, SinkArgs sink, hipStream_t stream);
 
 // top-k: path 0 = automatic, 1 = one workgroup per row, 2 = two-stage, 3 = filtered
 struct TopkPlan {

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 DSA_F32, DSA_BF16, DSA_F16 = 0, 1, 2
 _DTYPE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.float16: DSA_F16}
 
-EXPORTED = ("dsa_index_score", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
+EXPORTED = ("dsa_index_score", "dsa_index_score_sink", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
             "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_indexer_prep", "dsa_set_tuning",
             "dsa_status_string", "dsa_last_error", "dsa_version")
 
@@ -39,6 +39,8 @@ def _load() -> ctypes.CDLL:
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.dsa_index_score.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     lib.dsa_index_score.restype = I
+    lib.dsa_index_score_sink.argtypes = [P, P, P, P, P, P, I, F, P, I, I, I, I, I, I, I, F, P]
+    lib.dsa_index_score_sink.restype = I
     lib.dsa_topk_workspace_size.argtypes = [I, I, I]
     lib.dsa_topk_workspace_size.restype = S
     lib.dsa_topk.argtypes = [P, P, I, I, I, P, S, P]
@@ -89,9 +91,11 @@ def _stream(stream) -> int:
 
 def dsa_index_score(q: torch.Tensor, k_cache: torch.Tensor, w: torch.Tensor, scores: torch.Tensor,
                     kv_len: Optional[torch.Tensor] = None, q_pos: Optional[torch.Tensor] = None,
-                    scale: float = 1.0, stream=None) -> torch.Tensor:
+                    scale: float = 1.0, stream=None, n_sink: int = 0,
+                    sink_start: Optional[torch.Tensor] = None, sink_boost: float = 1e20) -> torch.Tensor:
     """q [B][n_q][H][D], k_cache [B][n_kv][D] (same dtype), w [B][n_q][H] fp32,
-    scores [B][n_q][n_kv] fp32 (output); kv_len [B] / q_pos [B][n_q] int32 or None."""
+    scores [B][n_q][n_kv] fp32 (output); kv_len [B] / q_pos [B][n_q] int32 or None.
+    n_sink > 0 adds sink_boost to the first n_sink keys from sink_start [B] int32 (or 0)."""
     B, n_q, H, D = q.shape
     n_kv = k_cache.shape[1]
     for t, n in ((q, "q"), (k_cache, "k_cache"), (w, "w"), (scores, "scores")):
@@ -106,6 +110,16 @@ def dsa_index_score(q: torch.Tensor, k_cache: torch.Tensor, w: torch.Tensor, sco
             _dev(t, n)
             if t.dtype != torch.int32:
                 raise ValueError(f"{n} must be int32")
+    if n_sink:
+        if sink_start is not None:
+            _dev(sink_start, "sink_start")
+            if sink_start.dtype != torch.int32 or tuple(sink_start.shape) != (B,):
+                raise ValueError("sink_start must be int32 [B]")
+        _check(lib.dsa_index_score_sink(q.data_ptr(), k_cache.data_ptr(), w.data_ptr(), _ptr(kv_len),
+                                        _ptr(q_pos), _ptr(sink_start), int(n_sink), float(sink_boost),
+                                        scores.data_ptr(), B, n_q, H, D, n_kv, _DTYPE[q.dtype],
+                                        _DTYPE[k_cache.dtype], float(scale), _stream(stream)), "dsa_index_score_sink")
+        return scores
     _check(lib.dsa_index_score(q.data_ptr(), k_cache.data_ptr(), w.data_ptr(), _ptr(kv_len), _ptr(q_pos),
                                scores.data_ptr(), B, n_q, H, D, n_kv, _DTYPE[q.dtype], _DTYPE[k_cache.dtype],
                                float(scale), _stream(stream)), "dsa_index_score")

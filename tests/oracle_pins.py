@@ -384,3 +384,51 @@ def pins_prep(prep, rope, append):
     want = cache.copy()
     want[0, 0], want[0, 9], want[0, 4], want[1, 7] = rows[0, 0], rows[0, 1], rows[0, 2], rows[1, 0]
     _close(out, want, 0.0, "cache append")
+
+
+# ----------------------------------------------------------------------------
+# attention sink: fn(q, k, w, kv_len, q_pos, scale, q_dtype, k_dtype, sink_start, n_sink, boost)
+# -> float32 scores; plain(q, k, w, kv_len, q_pos, scale, q_dtype, k_dtype) -> float32; topk
+# ----------------------------------------------------------------------------
+def pins_sink(fn, plain, topk):
+    rng = _rng(14)
+    B, n_q, H, D, n_kv = 3, 2, 4, 16, 40
+    q = rng.standard_normal((B, n_q, H, D)).astype(np.float32)
+    k = rng.standard_normal((B, n_kv, D)).astype(np.float32)
+    w = rng.random((B, n_q, H)).astype(np.float32)
+    kv_len = np.array([40, 25, 9])
+    q_pos = np.array([[30, 39], [10, 24], [3, 8]])
+    base = plain(q, k, w, kv_len, q_pos, 1.0, 0, 0)
+    # no sink: the plain scores
+    assert np.array_equal(fn(q, k, w, kv_len, q_pos, 1.0, 0, 0, None, 0, 1e20), base), "n_sink 0"
+    # one contiguous sequence from position 0: exactly the keys below n_sink, float32 sums
+    got = fn(q, k, w, kv_len, q_pos, 1.0, 0, 0, None, 4, 1e20)
+    for b in range(B):
+        for i in range(n_q):
+            for t in range(n_kv):
+                want = base[b, i, t]
+                if t < 4 and np.isfinite(want):
+                    want = np.float32(np.float32(want) + np.float32(1e20))
+                assert got[b, i, t] == want or (np.isneginf(want) and np.isneginf(got[b, i, t])), (b, i, t)
+    # per sequence: each sequence's own first present position; masked keys stay -inf
+    start = np.array([5, 20, 7])
+    got = fn(q, k, w, kv_len, q_pos, 1.0, 0, 0, start, 3, 1e20)
+    for b in range(B):
+        boosted = np.nonzero(got[b] > 1e19)
+        assert set(boosted[1].tolist()) <= set(range(start[b], start[b] + 3)), f"sink of sequence {b}"
+        for i in range(n_q):
+            lim = min(kv_len[b], q_pos[b, i] + 1)
+            for t in range(start[b], start[b] + 3):
+                if t < lim:
+                    assert got[b, i, t] > 1e19, (b, i, t)
+                else:
+                    assert np.isneginf(got[b, i, t]), (b, i, t)
+    # force-inclusion: top-k keeps every visible sink key even where its plain score is lowest
+    wneg = -w  # all plain scores <= 0, so the boost decides
+    got = fn(q, k, wneg, kv_len, q_pos, 1.0, 0, 0, start, 3, 1e20)
+    sel = topk(got.reshape(-1, n_kv), 5).reshape(B, n_q, 5)
+    for b in range(B):
+        for i in range(n_q):
+            lim = min(kv_len[b], q_pos[b, i] + 1)
+            must = {t for t in range(start[b], start[b] + 3) if t < lim}
+            assert must <= set(sel[b, i].tolist()), (b, i, must, sel[b, i])

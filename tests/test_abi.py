@@ -183,3 +183,14 @@ def test_indexer_prep_rejects_on_host(lib):
     for base in (0.0, -1.0, float("inf"), float("nan")):
         assert _prep(lib, base=base) == E_SHAPE, base
     assert _prep(lib, k_cache=FAKE + 8) == E_UNSUP
+
+
+def test_index_score_sink_rejects_on_host(lib):
+    def call(n_sink=2, boost=1e20, q=FAKE):
+        return lib.dsa_index_score_sink(q, FAKE, FAKE, None, None, None, n_sink, boost, FAKE, 1, 1, 32, 128, 64,
+                                        1, 1, 1.0, None)
+    assert call(n_sink=-1) == E_SHAPE
+    assert call(boost=float("inf")) == E_SHAPE
+    assert call(boost=float("nan")) == E_SHAPE
+    assert call(q=None) == E_NULL
+    assert b"dsa_index_score_sink" in lib.dsa_last_error()

@@ -111,3 +111,53 @@ def test_deterministic():
     a, _ = _run(wl, 9)
     b, _ = _run(wl, 9)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def _run_sink(wl, seed, sink_start, n_sink, kv_len=None):
+    L = binding()
+    inp = workloads.gen_all(wl, seed, parts=("q", "k", "w"))
+    kv = inp["kv_len"] if kv_len is None else np.asarray(kv_len, np.int32)
+    qp = inp["q_pos"] if wl.q_pos_start is not None else None
+    out = torch.full((wl.B, wl.n_q, wl.n_kv), 7.0, dtype=torch.float32, device="cuda")
+    L.dsa_index_score(dev(inp["q"], wl.idx_dtype), dev(inp["k"], wl.idx_dtype), dev(inp["w"]), out,
+                      kv_len=dev(kv) if kv_len is not None else None,
+                      q_pos=dev(np.asarray(qp, np.int32)) if qp is not None else None, scale=wl.scale,
+                      n_sink=n_sink, sink_start=dev(np.asarray(sink_start, np.int32)) if sink_start is not None else None)
+    torch.cuda.synchronize()
+    want = oracle.index_score_sink(inp["q"], inp["k"], inp["w"], kv, qp, wl.scale, wl.idx_dtype, wl.idx_dtype,
+                                   sink_start, n_sink, 1e20)
+    got = host(out)
+    boosted = want > 1e19
+    assert boosted.any()
+    assert np.array_equal(got[boosted], want[boosted]), "boosted scores"
+    assert np.array_equal(got > 1e19, boosted), "boosted positions"
+    g2, w2 = got.copy(), want.copy()
+    g2[boosted] = 0.0
+    w2[boosted] = 0.0
+    assert_rowwise(g2, w2, RTOL[wl.idx_dtype], wl.name + " with sink")
+    # the sink survives top-k (n_sink <= top_k)
+    rows = wl.B * wl.n_q
+    k_sel = min(wl.top_k, 16)
+    idx = torch.empty((rows, k_sel), dtype=torch.int32, device="cuda")
+    L.dsa_topk(out.view(rows, wl.n_kv), idx, k_sel)
+    sel = host(idx).reshape(wl.B, wl.n_q, k_sel)
+    for b in range(wl.B):
+        for i in range(wl.n_q):
+            must = set(np.nonzero(boosted[b, i])[0].tolist())
+            assert must <= set(sel[b, i].tolist()), (b, i)
+
+
+def test_sink_decode_mfma():
+    _run_sink(DEC.scaled(B=3, n_kv=3000), 21, [0, 100, 2990], 4, kv_len=[3000, 2000, 2995])
+
+
+def test_sink_default_start_and_f16():
+    _run_sink(workloads.LONG_DECODE_128K.scaled(B=2, n_kv=1500), 22, None, 2)
+
+
+def test_sink_prefill():
+    _run_sink(DEC.scaled(B=2, n_q=20, n_kv=700, q_pos_start=650), 23, [0, 640], 4)
+
+
+def test_sink_plain_fp32():
+    _run_sink(workloads.TINY_FP32.scaled(B=2), 24, [3, 0], 2)

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads
-from oracle_pins import F64, pins_hadamard, pins_mla, pins_prep, pins_rope, pins_scores, pins_topk
+from oracle_pins import F64, pins_hadamard, pins_mla, pins_prep, pins_rope, pins_scores, pins_sink, pins_topk
 
 
 def test_score_pins():
@@ -289,3 +289,39 @@ def test_cache_append_catches_off_by_one():
         return oracle.cache_append(cache, rows, np.asarray(pos) + 1)
     with pytest.raises(AssertionError):
         pins_prep(oracle.indexer_prep_f64, oracle.rope_neox_f64, bad)
+
+
+# ---------------------------------------------------------------------------
+# attention sink
+# ---------------------------------------------------------------------------
+def test_sink_pins():
+    pins_sink(oracle.index_score_sink, oracle.index_score, oracle.topk)
+
+
+def _sink_mutant(kind):
+    def fn(q, k, w, kv_len, q_pos, scale, qd, kd, sink_start, n_sink, boost):
+        S = oracle.index_score(q, k, w, kv_len, q_pos, scale, qd, kd)
+        if n_sink <= 0:
+            return S
+        B, n_q, n_kv = S.shape
+        start = np.zeros(B, np.int64) if (sink_start is None or kind == "global") else np.asarray(sink_start)
+        t = np.arange(n_kv)
+        for b in range(B):
+            hi = start[b] + n_sink + (1 if kind == "one_more" else 0)
+            in_sink = (t >= start[b]) & (t < hi)
+            if kind == "boost_masked":
+                S[b][:, in_sink] = np.float32(boost)
+            else:
+                S[b][:, in_sink] = S[b][:, in_sink] + np.float32(boost)
+        return S
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["global", "one_more", "boost_masked"])
+def test_sink_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_sink(_sink_mutant(kind), oracle.index_score, oracle.topk)
+
+
+def test_sink_mutant_harness_is_faithful():
+    pins_sink(_sink_mutant("none"), oracle.index_score, oracle.topk)
