@@ -288,12 +288,29 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         step_s = (time.perf_counter() - t0) / args.steps
+        # a layer that shares the previous full layer's indices runs the attention only
+        gm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gm):
+            call_mla()
+        for _ in range(max(1, args.warmup)):
+            gm.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            gm.replay()
+        torch.cuda.synchronize()
+        shared_s = (time.perf_counter() - t0) / args.steps
     else:
         t0 = time.perf_counter()
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
         step_s = (time.perf_counter() - t0) / args.steps
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            call_mla()
+        torch.cuda.synchronize()
+        shared_s = (time.perf_counter() - t0) / args.steps
 
     # indexer-input preparation of the step's new tokens (the stage upstream of the scores):
     # timed on its own with HIP events, after the timed region, writing the same cache rows
@@ -363,6 +380,10 @@ def main():
 
     ab = algorithmic_bytes(wl)
     tokens = rows
+    # IndexShare over GLM-5.2's 78 DSA layers: full layers run the whole step, shared layers
+    # reuse the last full layer's indices and run the attention only
+    n_full = sum(dsa.dsa_layer_computes_topk(l) for l in range(78))
+    per_layer_s = (n_full * step_s + (78 - n_full) * shared_s) / 78
     value = tokens / step_s
     score_ms = per["index_score"]
     achieved = ab["index_score"] / (score_ms * 1e-3) / 1e9
@@ -404,6 +425,10 @@ def main():
         "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
         "kernels_gbs": {k_: round(ab[k_] / (per[k_] * 1e-3) / 1e9, 1) for k_ in per},
         "roofline": roof,
+        "indexshare": {"full_layers": n_full, "shared_layers": 78 - n_full,
+                       "shared_layer_ms": round(shared_s * 1e3, 4),
+                       "ms_per_layer": round(per_layer_s * 1e3, 4),
+                       "tokens_per_s_per_layer": round(tokens / per_layer_s, 1)},
         "copy_gbs": round(copy_gbs, 1),
         "score_frac_of_copy": round(achieved / copy_gbs, 4) if not prefill else None,
         "indexer_prep": {"ms": round(prep_ms, 4), "bytes": prep_bytes(wl),

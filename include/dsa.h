@@ -181,6 +181,17 @@ int dsa_indexer_prep(const float* q_in, const float* k_in, const void* latent_in
                      int row_bytes, int out_dtype, float rope_base, int hadamard, hipStream_t stream);
 
 /*
+ * IndexShare layer map (ik_llama_opt log, "GLM-5.2 DSA: IndexShare" sub-commit): in a model
+ * with n_layer DSA layers, "full" layers compute their own scores and top-k, and every
+ * "shared" layer reuses the indices of the most recent full layer (pass the same idx array to
+ * dsa_sparse_mla_attn). A layer is full iff layer <= 1 or layer % 4 == 2 (21 of GLM-5.2's 78).
+ * Returns 1 for a full layer, 0 for a shared one, DSA_ERR_SHAPE for layer < 0.
+ */
+int dsa_layer_computes_topk(int layer);
+/* The full layer whose indices layer `layer` uses (itself when full), or DSA_ERR_SHAPE. */
+int dsa_topk_source_layer(int layer);
+
+/*
  * Tuning switches. They choose between kernels that compute identical results and
  * change only speed. key "topk_path": 0 = automatic, 1 = one workgroup per row,
  * 2 = two-stage (segments, then candidates), 3 = filtered (a sampled threshold picks

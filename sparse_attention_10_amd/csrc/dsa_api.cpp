@@ -60,6 +60,17 @@ const char* dsa_status_string(int status) {
 
 const char* dsa_last_error(void) { return g_err; }
 
+int dsa_layer_computes_topk(int layer) {
+  if (layer < 0) return fail(DSA_ERR_SHAPE, "dsa_layer_computes_topk: layer=%d must be >= 0", layer);
+  return (layer <= 1 || layer % 4 == 2) ? 1 : 0;
+}
+
+int dsa_topk_source_layer(int layer) {
+  if (layer < 0) return fail(DSA_ERR_SHAPE, "dsa_topk_source_layer: layer=%d must be >= 0", layer);
+  if (layer <= 1) return layer;
+  return 4 * ((layer - 2) / 4) + 2;  // the most recent layer 4m + 2 at or below `layer`
+}
+
 int dsa_set_tuning(const char* key, int value) {
   if (!key) return fail(DSA_ERR_NULL, "dsa_set_tuning: key is NULL");
   if (std::strcmp(key, "topk_path") == 0) {

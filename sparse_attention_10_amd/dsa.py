@@ -21,7 +21,7 @@ DSA_F32, DSA_BF16, DSA_F16 = 0, 1, 2
 _DTYPE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.float16: DSA_F16}
 
 EXPORTED = ("dsa_index_score", "dsa_index_score_sink", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
-            "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_indexer_prep", "dsa_set_tuning",
+            "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_indexer_prep", "dsa_layer_computes_topk", "dsa_topk_source_layer", "dsa_set_tuning",
             "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -53,6 +53,10 @@ def _load() -> ctypes.CDLL:
     lib.dsa_sparse_mla_attn.restype = I
     lib.dsa_indexer_prep.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.dsa_indexer_prep.restype = I
+    lib.dsa_layer_computes_topk.argtypes = [I]
+    lib.dsa_layer_computes_topk.restype = I
+    lib.dsa_topk_source_layer.argtypes = [I]
+    lib.dsa_topk_source_layer.restype = I
     lib.dsa_set_tuning.argtypes = [ctypes.c_char_p, I]
     lib.dsa_set_tuning.restype = I
     lib.dsa_status_string.argtypes = [I]
@@ -234,6 +238,20 @@ def dsa_indexer_prep(pos: torch.Tensor, q_in: Optional[torch.Tensor] = None, q_o
                                 _ptr(k_cache), _ptr(latent_cache), B, n_new, H, n_kv, row_bytes,
                                 DSA_BF16 if out_dtype is None else out_dtype, float(rope_base),
                                 1 if hadamard else 0, _stream(stream)), "dsa_indexer_prep")
+
+
+def dsa_layer_computes_topk(layer: int) -> bool:
+    r = lib.dsa_layer_computes_topk(int(layer))
+    if r < 0:
+        _check(r, "dsa_layer_computes_topk")
+    return r == 1
+
+
+def dsa_topk_source_layer(layer: int) -> int:
+    r = lib.dsa_topk_source_layer(int(layer))
+    if r < 0:
+        _check(r, "dsa_topk_source_layer")
+    return r
 
 
 def dsa_set_tuning(key: str, value: int) -> None:

@@ -194,3 +194,18 @@ def test_index_score_sink_rejects_on_host(lib):
     assert call(boost=float("nan")) == E_SHAPE
     assert call(q=None) == E_NULL
     assert b"dsa_index_score_sink" in lib.dsa_last_error()
+
+
+def test_indexshare_layer_map(lib):
+    # GLM-5.2: 21 full and 57 shared layers among 78 (the IndexShare sub-commit's counts)
+    full = [l for l in range(78) if lib.dsa_layer_computes_topk(l) == 1]
+    assert len(full) == 21 and 78 - len(full) == 57
+    assert full[:3] == [0, 1, 2]
+    for l in range(200):
+        src = lib.dsa_topk_source_layer(l)
+        assert lib.dsa_layer_computes_topk(src) == 1
+        assert src <= l
+        # no full layer lies strictly between the source and the layer
+        assert all(lib.dsa_layer_computes_topk(m) == 0 for m in range(src + 1, l + 1))
+    assert lib.dsa_layer_computes_topk(-1) == E_SHAPE
+    assert lib.dsa_topk_source_layer(-3) == E_SHAPE

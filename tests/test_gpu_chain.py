@@ -109,3 +109,25 @@ def test_full_chunked_prefill():
 
 def test_full_tiny():
     _full("tiny_fp32_decode_256", [0], [0])
+
+
+def test_indexshare_shared_layer_reuses_indices():
+    """A shared layer (IndexShare) attends over the indices of the last full layer: its own
+    queries and latent cache, the full layer's selection."""
+    L = binding()
+    wl = workloads.GLM_DECODE_8K.scaled(B=2, n_kv=3000, top_k=512)
+    full = workloads.gen_all(wl, 0)
+    shared = workloads.gen_all(wl, 1, parts=("qa", "latent"))
+    d = to_device_inputs(wl, full)
+    _, idx, _, _ = run_chain(wl, d)
+    out = torch.empty((wl.B, wl.n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((wl.B, wl.n_q, wl.Hm), dtype=torch.float32, device="cuda")
+    src = L.dsa_topk_source_layer(5)
+    assert L.dsa_layer_computes_topk(src) and not L.dsa_layer_computes_topk(5)
+    L.dsa_sparse_mla_attn(dev(shared["qa"], wl.mla_dtype), dev(shared["latent"], wl.mla_dtype), idx, out,
+                          wl.d_latent, wl.sm_scale, lse=lse, kv_len=d["kv_len"])
+    torch.cuda.synchronize()
+    o_out, o_lse = oracle.sparse_mla(shared["qa"], shared["latent"], host(idx), wl.sm_scale, wl.d_latent,
+                                     wl.mla_dtype, full["kv_len"])
+    assert_rowwise(host(out), o_out, RTOL[wl.mla_dtype], "shared layer out")
+    assert_rowwise(host(lse), o_lse, RTOL[wl.mla_dtype], "shared layer lse")
