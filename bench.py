@@ -168,6 +168,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--pipelines", type=int, default=1,
+                    help="run the step as this many chains over equal slices of the batch, each on its "
+                         "own stream, so one slice's latency-bound stages overlap another's streaming")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--scrub-mib", type=int, default=0,
@@ -242,6 +245,42 @@ def main():
         call_topk()
         call_mla()
 
+    # the step as P chains over batch slices on P streams (default priority), joined at the end
+    P = args.pipelines
+    if P < 1 or wl.B % P != 0:
+        print(f"--pipelines must divide B={wl.B}", file=sys.stderr)
+        sys.exit(2)
+    parts = []
+    if P > 1:
+        hb = wl.B // P
+        for p_ in range(P):
+            sl = slice(p_ * hb, (p_ + 1) * hb)
+            ns_p = dsa.dsa_sparse_mla_num_splits(hb, wl.n_q, wl.top_k)
+            parts.append({
+                "sl": sl, "ns": ns_p, "stream": torch.cuda.Stream(),
+                "ws_t": torch.empty(max(1, dsa.dsa_topk_workspace_size(hb * wl.n_q, wl.n_kv, wl.top_k)),
+                                    dtype=torch.uint8, device=dev),
+                "ws_m": torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(hb, wl.n_q, wl.Hm, wl.top_k,
+                                                                             wl.d_latent, ns_p)),
+                                    dtype=torch.uint8, device=dev)})
+
+    def pstep():
+        if P == 1:
+            step()
+            return
+        cur = torch.cuda.current_stream()
+        for part in parts:
+            sl, st = part["sl"], part["stream"]
+            st.wait_stream(cur)
+            with torch.cuda.stream(st):
+                dsa.dsa_index_score(q[sl], k[sl], w[sl], scores[sl], kv_len=kv_len[sl],
+                                    q_pos=q_pos[sl] if q_pos is not None else None, scale=wl.scale)
+                dsa.dsa_topk(scores[sl], idx[sl], wl.top_k, workspace=part["ws_t"])
+                dsa.dsa_sparse_mla_attn(qa[sl], lat[sl], idx[sl], out[sl], wl.d_latent, wl.sm_scale, lse=lse[sl],
+                                        kv_len=kv_len[sl], n_split=part["ns"], workspace=part["ws_m"])
+        for part in parts:
+            cur.wait_stream(part["stream"])
+
     # warmup (also the eager reference of one step)
     for _ in range(max(1, args.warmup)):
         step()
@@ -275,11 +314,11 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()  # first call outside capture
+            pstep()  # first call outside capture
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            step()
+            pstep()
         for _ in range(max(1, args.warmup)):
             g.replay()
         torch.cuda.synchronize()
@@ -303,7 +342,7 @@ def main():
     else:
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            step()
+            pstep()
         torch.cuda.synchronize()
         step_s = (time.perf_counter() - t0) / args.steps
         t0 = time.perf_counter()
@@ -417,7 +456,7 @@ def main():
                    "top_k": wl.top_k, "Hm": wl.Hm, "d_latent": wl.d_latent, "d_rope": wl.d_rope,
                    "indexer_dtype": workloads.DTYPE_NAMES[wl.idx_dtype],
                    "latent_dtype": workloads.DTYPE_NAMES[wl.mla_dtype], "mode": args.mode,
-                   "mla_splits": n_split, "parallelism": "single GPU"},
+                   "mla_splits": n_split, "pipelines": P, "parallelism": "single GPU"},
         "step_hbm_gbs": round(ab["step"] / step_s / 1e9, 1),
         "step_hbm_frac": round(ab["step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": ab["step"],
