@@ -173,7 +173,7 @@ int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* id
  * row_bytes     bytes per latent row, a multiple of 16 (1152 for 576 bf16); ignored when
  *               latent_in is NULL
  * rope_base     the rope frequency base (> 0, finite)
- * Sizes: B, n_new, n_kv >= 1; H >= 1 when q_in is given; head dim 128 with 64 rope dims.
+ * Sizes: B, n_new, n_kv >= 1; 1 <= H <= 65536 when q_in is given; head dim 128 with 64 rope dims.
  * Pointers to 16-byte aligned memory. At least one of q_in, k_in, latent_in is non-NULL.
  */
 int dsa_indexer_prep(const float* q_in, const float* k_in, const void* latent_in, const int32_t* pos,

@@ -215,7 +215,7 @@ int dsa_indexer_prep(const float* q_in, const float* k_in, const void* latent_in
   if (!q_in != !q_out || !k_in != !k_cache || !latent_in != !latent_cache)
     return fail(DSA_ERR_NULL, "dsa_indexer_prep: q_in/q_out, k_in/k_cache and latent_in/latent_cache "
                               "must be given in pairs");
-  if (B < 1 || n_new < 1 || n_kv < 1 || (q_in && H < 1))
+  if (B < 1 || n_new < 1 || n_kv < 1 || (q_in && (H < 1 || H > 65536)))
     return fail(DSA_ERR_SHAPE, "dsa_indexer_prep: B=%d n_new=%d H=%d n_kv=%d out of range", B, n_new, H, n_kv);
   if ((long long)B * n_new * (q_in ? H + 1 : 1) > INT_MAX || (long long)B * n_kv > (1LL << 34))
     return fail(DSA_ERR_SHAPE, "dsa_indexer_prep: too many rows");

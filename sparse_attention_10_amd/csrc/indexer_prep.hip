@@ -12,10 +12,11 @@
 // over sqrt(128), applied as a butterfly (x_j, x_{j+h}) -> (x_j + x_{j+h}, x_j - x_{j+h}) for
 // h = 1, 2, ..., 64.
 //
-// Layout: 16 threads per 128-dim row, thread t holding dims 8t .. 8t+7 (two 16-byte loads of
-// fp32 input, one 16-byte store of 16-bit output). The rope partner of dim i sits in thread
-// t ^ 4; the butterflies with h >= 8 exchange with thread t ^ (h / 8). All exchanges stay
-// inside the row's 16 lanes.
+// Layout: 8 threads per 128-dim row, thread t holding dims 16t .. 16t+15 (four 16-byte loads of
+// fp32 input, two 16-byte stores of 16-bit output). The rope partner of dim i sits in thread
+// t ^ 2; the butterflies with h <= 8 stay in the thread, those with h = 16, 32, 64 exchange
+// with thread t ^ 1, t ^ 2, t ^ 4. All exchanges are DPP lane moves inside the row's 8 lanes
+// (quad permutes for ^1 and ^2, a row shift either way for ^4), so no LDS traffic is involved.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,7 +24,8 @@
 
 namespace dsa {
 
-constexpr int kPrepThreads = 256;  // 16 rows of 128 dims per workgroup
+constexpr int kPrepThreads = 256;  // 32 rows of 128 dims per workgroup
+constexpr int kPrepTpr = 8;        // threads per row
 
 // base^(-i/32) / (2 pi) for the 32 rope pairs, in double (passed by value with the launch)
 struct RopeTurns {
@@ -39,7 +41,7 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
 }
 
 // 8 consecutive values to dst (out_dtype: F32 two 16-byte stores, else one)
-__device__ __forceinline__ void store8(uint8_t* dst, const float (&v)[8], int out_dtype) {
+__device__ __forceinline__ void store8(uint8_t* dst, const float* v, int out_dtype) {
   if (out_dtype == kF32) {
     reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
     reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -52,80 +54,113 @@ __device__ __forceinline__ void store8(uint8_t* dst, const float (&v)[8], int ou
   }
 }
 
-// Rows [0, q_rows) are query rows (token r / H, head r % H); rows [q_rows, q_rows + k_rows)
-// are key rows (token r - q_rows). pos[token] is the token's position and cache row.
+// DPP lane moves within 4-lane quads (lane ^ 1, lane ^ 2) and 8-lane groups (lane ^ 4)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float lane_xor1(float x) { return dpp<0xB1>(x); }  // quad_perm [1,0,3,2]
+__device__ __forceinline__ float lane_xor2(float x) { return dpp<0x4E>(x); }  // quad_perm [2,3,0,1]
+__device__ __forceinline__ float lane_xor4(float x, bool hi) {
+  const float up = dpp<0x104>(x);    // row_shl:4, the value of lane + 4
+  const float down = dpp<0x114>(x);  // row_shr:4, the value of lane - 4
+  return hi ? down : up;
+}
+
+// Workgroup (token, chunk): rows 32 * chunk .. + 31 of the token's rows, which are its nq
+// query heads followed by its key (nk = 0 or 1). The rope angles depend on the token only, so
+// 32 threads compute the 32 (cos, sin) pairs once into LDS for all the token's rows.
 __global__ __launch_bounds__(kPrepThreads) void indexer_prep_rows(
     const float* __restrict__ q_in, const float* __restrict__ k_in, const int* __restrict__ pos,
-    uint8_t* __restrict__ q_out, uint8_t* __restrict__ k_cache, int q_rows, int k_rows, int H,
-    int n_new, int n_kv, int out_dtype, RopeTurns freq, int hadamard) {
-  const int t = threadIdx.x & 15;
-  const long r = (long)blockIdx.x * (kPrepThreads / 16) + (threadIdx.x >> 4);
-  if (r >= (long)q_rows + k_rows) return;  // whole 16-lane groups leave together
-  const bool is_q = r < q_rows;
-  const long token = is_q ? r / H : r - q_rows;
-  const float* src = (is_q ? q_in + r * 128 : k_in + token * 128) + 8 * t;
+    uint8_t* __restrict__ q_out, uint8_t* __restrict__ k_cache, int nq, int nk, int n_new, int n_kv,
+    int out_dtype, RopeTurns freq, int hadamard) {
+  __shared__ float s_cos[32], s_sin[32];
+  const int t = threadIdx.x & (kPrepTpr - 1);
+  const long token = blockIdx.x;
   const int p = pos[token];
+  if (threadIdx.x < 32) {
+    // the angle in turns, p * base^(-i/32) / (2 pi), is formed in double and its fractional
+    // part taken there (positions reach 2^17 and more, where a float angle would be off by
+    // 1e-2 rad); cos / sin then run in float on an angle in [-pi, pi]
+    const double turns = (double)p * freq.turns[threadIdx.x];
+    const float red = (float)((turns - rint(turns)) * 6.283185307179586476925287);
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    s_cos[threadIdx.x] = cs;
+    s_sin[threadIdx.x] = sn;
+  }
+  __syncthreads();
+  const int j_row = blockIdx.y * (kPrepThreads / kPrepTpr) + (int)(threadIdx.x / kPrepTpr);
+  // Rows past the token's last compute on its first row and store nothing: every lane of a
+  // row group stays active for the lane moves.
+  const bool live = j_row < nq + nk;
+  const int jr = live ? j_row : 0;
+  const bool is_q = jr < nq;
+  const float* src = (is_q ? q_in + (token * nq + jr) * 128 : k_in + token * 128) + 16 * t;
 
-  float x[8];
-  {
-    const float4 a = reinterpret_cast<const float4*>(src)[0];
-    const float4 b = reinterpret_cast<const float4*>(src)[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  float x[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float4 v = reinterpret_cast<const float4*>(src)[c];
+    x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
   }
 
-  // NeoX rope on dims 0..63. The angle in turns, p * base^(-i/32) / (2 pi), is formed in double
-  // and its fractional part taken there (positions reach 2^17 and more, where a float angle
-  // would be off by 1e-2 rad); cos / sin then run in float on an angle in [-pi, pi].
+  // NeoX rope on dims 0..63 (threads 0..3; thread t pairs with t ^ 2)
   {
-    float c[8], s[8];
+    const bool rope = t < 4;
+    const bool upper = (t & 2) != 0;  // holds dims i + 32
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int f = 8 * (t & 3) + j;  // pair index i of dims (i, i + 32)
-      const double turns = (double)p * freq.turns[f];
-      const float red = (float)((turns - rint(turns)) * 6.283185307179586476925287);
-      sincosf(red, &s[j], &c[j]);
+    for (int j = 0; j < 16; ++j) {
+      const float partner = lane_xor2(x[j]);
+      const int f = 16 * (t & 1) + j;
+      const float c = s_cos[f], sn = s_sin[f];
+      const float y = upper ? x[j] * c + partner * sn : x[j] * c - partner * sn;
+      x[j] = rope ? y : x[j];
     }
-    float y[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float partner = __shfl_xor(x[j], 4, 64);
-      if (t < 4) y[j] = x[j] * c[j] - partner * s[j];
-      else if (t < 8) y[j] = x[j] * c[j] + partner * s[j];
-      else y[j] = x[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = y[j];
   }
 
   if (hadamard) {
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
+    for (int h = 1; h < 16; h <<= 1)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 16; ++j)
         if ((j & h) == 0) {
           const float a = x[j], b = x[j + h];
           x[j] = a + b;
           x[j + h] = a - b;
         }
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
+    for (int j = 0; j < 16; ++j) {
+      const float o = lane_xor1(x[j]);
+      x[j] = (t & 1) ? o - x[j] : x[j] + o;
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float o = __shfl_xor(x[j], m, 64);
-        x[j] = (t & m) ? o - x[j] : x[j] + o;
-      }
+    for (int j = 0; j < 16; ++j) {
+      const float o = lane_xor2(x[j]);
+      x[j] = (t & 2) ? o - x[j] : x[j] + o;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float o = lane_xor4(x[j], (t & 4) != 0);
+      x[j] = (t & 4) ? o - x[j] : x[j] + o;
+    }
     const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] *= scale;
+    for (int j = 0; j < 16; ++j) x[j] *= scale;
   }
 
+  if (!live) return;
   const int esz = out_dtype == kF32 ? 4 : 2;
+  uint8_t* dst = nullptr;
   if (is_q) {
-    store8(q_out + (r * 128 + 8 * t) * esz, x, out_dtype);
+    dst = q_out + ((token * nq + jr) * 128 + 16 * t) * esz;
   } else if (p >= 0 && p < n_kv) {
     const long b = token / n_new;
-    store8(k_cache + (((long)b * n_kv + p) * 128 + 8 * t) * esz, x, out_dtype);
+    dst = k_cache + (((long)b * n_kv + p) * 128 + 16 * t) * esz;
+  }
+  if (dst) {
+    store8(dst, x, out_dtype);
+    store8(dst + 8 * esz, x + 8, out_dtype);
   }
 }
 
@@ -150,13 +185,12 @@ hipError_t launch_indexer_prep(const float* q_in, const float* k_in, const void*
   RopeTurns freq;
   for (int i = 0; i < 32; ++i) freq.turns[i] = exp2(-(double)i / 32.0 * log2_base) / 6.283185307179586476925287;
   const long n_tok = (long)B * n_new;
-  const long q_rows = q_in ? n_tok * H : 0;
-  const long k_rows = k_in ? n_tok : 0;
-  if (q_rows + k_rows > 0) {
-    const long blocks = (q_rows + k_rows + 15) / 16;
-    hipLaunchKernelGGL(indexer_prep_rows, dim3((unsigned)blocks), dim3(kPrepThreads), 0, stream, q_in, k_in, pos,
-                       (uint8_t*)q_out, (uint8_t*)k_cache, (int)q_rows, (int)k_rows, H, n_new, n_kv, out_dtype,
-                       freq, hadamard);
+  const int nq = q_in ? H : 0, nk = k_in ? 1 : 0;
+  if (nq + nk > 0) {
+    const int rows_per_block = kPrepThreads / kPrepTpr;
+    dim3 grid((unsigned)n_tok, (unsigned)((nq + nk + rows_per_block - 1) / rows_per_block));
+    hipLaunchKernelGGL(indexer_prep_rows, grid, dim3(kPrepThreads), 0, stream, q_in, k_in, pos, (uint8_t*)q_out,
+                       (uint8_t*)k_cache, nq, nk, n_new, n_kv, out_dtype, freq, hadamard);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
