@@ -168,6 +168,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
+                    help="dsa_set_tuning before the run (repeatable)")
     ap.add_argument("--pipelines", type=int, default=1,
                     help="run the step as this many chains over equal slices of the batch, each on its "
                          "own stream, so one slice's latency-bound stages overlap another's streaming")
@@ -198,6 +200,9 @@ def main():
     import workloads
     from sparse_attention_10_amd import dsa
 
+    for kv_ in args.tune:
+        key_, val_ = kv_.split("=")
+        dsa.dsa_set_tuning(key_, int(val_))
     wl = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
@@ -456,7 +461,7 @@ def main():
                    "top_k": wl.top_k, "Hm": wl.Hm, "d_latent": wl.d_latent, "d_rope": wl.d_rope,
                    "indexer_dtype": workloads.DTYPE_NAMES[wl.idx_dtype],
                    "latent_dtype": workloads.DTYPE_NAMES[wl.mla_dtype], "mode": args.mode,
-                   "mla_splits": n_split, "pipelines": P, "parallelism": "single GPU"},
+                   "mla_splits": n_split, "pipelines": P, "tuning": args.tune, "parallelism": "single GPU"},
         "step_hbm_gbs": round(ab["step"] / step_s / 1e9, 1),
         "step_hbm_frac": round(ab["step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": ab["step"],
