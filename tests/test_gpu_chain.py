@@ -131,3 +131,50 @@ def test_indexshare_shared_layer_reuses_indices():
                                      wl.mla_dtype, full["kv_len"])
     assert_rowwise(host(out), o_out, RTOL[wl.mla_dtype], "shared layer out")
     assert_rowwise(host(lse), o_lse, RTOL[wl.mla_dtype], "shared layer lse")
+
+
+def test_graph_replays_match_eager():
+    """The chain captured in a HIP graph (how the bench times it) gives, on every replay, the
+    bits of the eager run: the library records no memset nodes and keeps no state between
+    calls. Eager work and synchronisations run between the replays."""
+    L = binding()
+    wl = workloads.BATCHED_DECODE_32K.scaled(B=4, n_kv=8192)
+    inp = workloads.gen_all(wl, 3)
+    d = to_device_inputs(wl, inp)
+    rows = wl.B * wl.n_q
+    ws_t = torch.empty(max(1, L.dsa_topk_workspace_size(rows, wl.n_kv, wl.top_k)), dtype=torch.uint8, device="cuda")
+    ns = L.dsa_sparse_mla_num_splits(wl.B, wl.n_q, wl.top_k)
+    ws_m = torch.empty(max(1, L.dsa_sparse_mla_workspace_size(wl.B, wl.n_q, wl.Hm, wl.top_k, wl.d_latent, ns)),
+                       dtype=torch.uint8, device="cuda")
+    scores = torch.empty((wl.B, wl.n_q, wl.n_kv), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.B, wl.n_q, wl.top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.B, wl.n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((wl.B, wl.n_q, wl.Hm), dtype=torch.float32, device="cuda")
+
+    def step():
+        L.dsa_index_score(d["q"], d["k"], d["w"], scores, kv_len=d["kv_len"], scale=wl.scale)
+        L.dsa_topk(scores, idx, wl.top_k, workspace=ws_t)
+        L.dsa_sparse_mla_attn(d["qa"], d["latent"], idx, out, wl.d_latent, wl.sm_scale, lse=lse,
+                              kv_len=d["kv_len"], n_split=ns, workspace=ws_m)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [host(t).copy() for t in (scores, idx, out, lse)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (scores, idx, out, lse):
+            t.fill_(0)  # eager work between replays; the replay must rewrite everything
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("scores", "idx", "out", "lse"), (scores, idx, out, lse), ref):
+            assert np.array_equal(host(t).view(np.uint32) if t.dtype != torch.int32 else host(t),
+                                  r.view(np.uint32) if r.dtype != np.int32 else r), f"replay {rep}: {name}"
