@@ -276,6 +276,13 @@ struct DmaShare {
   static constexpr int lo = NBLK / 8;
 };
 
+// Partial-output slots (16 bytes each) per 32-head tile of one part: 4 dim quarters x 4
+// dim tiles x 4 column groups x 64 lanes.
+constexpr int kFragSlots = 4 * 4 * 4 * 64;
+__device__ __forceinline__ int frag_slot(int pq, int ht, int n_ht, int dt, int c, int lane) {
+  return (((pq * n_ht + ht) * 4 + dt) * 4 + c) * 64 + lane;
+}
+
 template <int DR>
 __global__ __launch_bounds__(512) void sparse_mla_mfma(
     const bf16_t* __restrict__ qa, const bf16_t* __restrict__ lat, const int* __restrict__ idx,
@@ -599,33 +606,101 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     if (h >= Hm) continue;
     const float m = s_ml[0][h], l = s_ml[1][h];
     const long qh = (long)bi * Hm + h;
-    float* dst;
-    float scale;
     if (n_split == 1) {
-      dst = out + qh * DL;
-      scale = l > 0.f ? 1.f / l : 0.f;
+      float* dst = out + qh * DL;
+      const float scale = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int d = 128 * pq + 32 * dt + 8 * c + 4 * (lane >> 5);
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[dt][ht][4 * c + e] * scale;
+          *reinterpret_cast<f32x4*>(dst + d) = v;
+        }
+      if (lse && pq == 0 && lane < 32) lse[qh] = l > 0.f ? m + __logf(l) : -INFINITY;
     } else {
+      // Partial outputs in fragment order (see mla_merge_frag): every store instruction of
+      // the wave writes 1 KB contiguous, where the [head][dim] order would spread it over 32
+      // rows 2 KB apart.
       const long ph = ((long)bi * n_split + sp) * Hm + h;
-      dst = ws_o + ph * DL;
-      scale = 1.f;
       if (pq == 0 && lane < 32) {
         ws_ml[2 * ph] = m;
         ws_ml[2 * ph + 1] = l;
       }
-    }
+      float* blk = ws_o + ((long)bi * n_split + sp) * (n_ht * kFragSlots) * 4;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int d = 128 * pq + 32 * dt + 8 * c + 4 * (lane >> 5);
-        f32x4 v;
+        for (int c = 0; c < 4; ++c) {
+          f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = o[dt][ht][4 * c + e] * scale;
-        *reinterpret_cast<f32x4*>(dst + d) = v;
-      }
-      if (n_split == 1 && lse && pq == 0 && lane < 32) lse[qh] = l > 0.f ? m + __logf(l) : -INFINITY;
+          for (int e = 0; e < 4; ++e) v[e] = o[dt][ht][4 * c + e];
+          *reinterpret_cast<f32x4*>(blk + frag_slot(pq, ht, n_ht, dt, c, lane) * 4) = v;
+        }
     }
   }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// merge of the MFMA kernel's partials, stored per part in fragment order: 16-byte slot
+// ((((pq * n_ht + ht) * 4 + dt) * 4 + c) * 64 + lane) holds output dims
+// d = 128 pq + 32 dt + 8 c + 4 (lane / 32) .. +3 of head 32 ht + lane % 32. One thread per
+// slot; consecutive threads read consecutive slots of every part.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mla_merge_frag(const float* __restrict__ ws_o,
+                                                      const float* __restrict__ ws_ml,
+                                                      float* __restrict__ out, float* __restrict__ lse,
+                                                      int Hm, int n_ht, int n_split, long total) {
+  const long gid = (long)xcd_remap(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int per = n_ht * kFragSlots;  // slots per part
+  const long bi = gid / per;
+  const int s = (int)(gid - bi * per);
+  const int lane = s & 63, c = (s >> 6) & 3, dt = (s >> 8) & 3, hq = s >> 10;
+  const int ht = hq % n_ht, pq = hq / n_ht;
+  const int h = 32 * ht + (lane & 31);
+  if (h >= Hm) return;
+  const int d = 128 * pq + 32 * dt + 8 * c + 4 * (lane >> 5);
+  constexpr int SB = 8;
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_split; s0 += SB) {
+    float m[SB], l[SB];
+    f32x4 v[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const long part = bi * n_split + s0 + j;
+      const bool in = s0 + j < n_split;
+      m[j] = in ? ws_ml[2 * (part * Hm + h)] : -INFINITY;
+      l[j] = in ? ws_ml[2 * (part * Hm + h) + 1] : 0.f;
+      v[j] = in ? *reinterpret_cast<const f32x4*>(ws_o + (part * per + s) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) mb = fmaxf(mb, m[j]);
+    if (mb == -INFINITY) continue;
+    const float r = M == -INFINITY ? 0.f : __expf(M - mb);
+    L *= r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] *= r;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      if (m[j] == -INFINITY) continue;
+      const float f = __expf(m[j] - mb);
+      L = fmaf(f, l[j], L);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = fmaf(f, v[j][k], acc[k]);
+    }
+    M = mb;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] *= inv;
+  *reinterpret_cast<f32x4*>(out + (bi * Hm + h) * 512 + d) = acc;
+  if (lse && d == 0) lse[bi * Hm + h] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -707,8 +782,9 @@ int mla_auto_splits(int B, int n_q, int top_k) {
 size_t mla_workspace_bytes(int B, int n_q, int Hm, int top_k, int d_latent, int n_split) {
   (void)top_k;
   if (n_split <= 1) return 0;
-  const size_t parts = (size_t)B * n_q * n_split * Hm;
-  return align256(parts * d_latent * sizeof(float)) + align256(parts * 2 * sizeof(float));
+  const size_t parts = (size_t)B * n_q * n_split;
+  const size_t hpad = (size_t)(Hm + 31) / 32 * 32;  // the MFMA kernel's fragment order pads heads to 32
+  return align256(parts * hpad * d_latent * sizeof(float)) + align256(parts * Hm * 2 * sizeof(float));
 }
 
 bool mla_mfma_supported(int Hm, int d_latent, int d_rope, int dtype) {
@@ -724,10 +800,10 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
   float* ws_o = nullptr;
   float* ws_ml = nullptr;
   if (n_split > 1) {
-    const size_t parts = (size_t)rows * n_split * Hm;
+    const size_t hpad = (size_t)(Hm + 31) / 32 * 32;
     ws_o = reinterpret_cast<float*>(workspace);
     ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                     align256(parts * d_latent * sizeof(float)));
+                                     align256((size_t)rows * n_split * hpad * d_latent * sizeof(float)));
   }
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
     const unsigned blocks = (unsigned)(rows * n_split);
@@ -761,7 +837,12 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
-  if (d_latent % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
+  if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
+    const int n_ht = (Hm + 31) / 32;
+    const long total = rows * n_ht * kFragSlots;
+    hipLaunchKernelGGL(mla_merge_frag, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws_o,
+                       ws_ml, out, lse, Hm, n_ht, n_split, total);
+  } else if (d_latent % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
     const long total = rows * Hm * (d_latent / 4);
     hipLaunchKernelGGL(mla_merge<4>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws_o, ws_ml,
                        out, lse, Hm, n_split, d_latent / 4, total);

@@ -50,7 +50,7 @@ DEC = workloads.GLM_DECODE_8K
 
 @pytest.mark.parametrize("Hm,top_k,n_split", [(64, 1, 1), (64, 31, 1), (64, 32, 1), (64, 33, 1), (64, 100, 3),
                                               (16, 300, 2), (48, 256, 1), (64, 2048, 0), (64, 2048, 8),
-                                              (32, 513, 5)])
+                                              (32, 513, 5), (48, 256, 4)])
 def test_mfma_shapes(Hm, top_k, n_split):
     wl = DEC.scaled(B=2, n_kv=3000, Hm=Hm, top_k=top_k)
     _run(wl, _indices(2, 1, wl.n_kv, top_k, top_k), 1, n_split)
