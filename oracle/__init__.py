@@ -387,3 +387,113 @@ def dsa_step(inp: dict, wl) -> dict:
     out, lse = sparse_mla(inp["qa"], inp["latent"], idx, wl.sm_scale, wl.d_latent, wl.mla_dtype,
                           inp["kv_len"])
     return {"scores": S, "idx": idx, "out": out, "lse": lse}
+
+
+# ----------------------------------------------------------------------------
+# 5. pooled (kpool) indexer: pool compression, pool scores, token selection
+# ----------------------------------------------------------------------------
+# vllm-rdna "Glm5Next (GLM-5.3-Flash) on gfx1030" PR, architecture section and the DSA
+# attention and first-cut kernel commit bodies: the indexer cache holds one packed row per
+# token (257 = k | gate | valid for 128-dim keys), groups of kpool = 4 tokens are compressed
+# into one pool key with softmax(gate + ape) weights, queries score pool keys (relu per head,
+# weighted head sum), top-k runs caller-side over pools, and the last incomplete pool (the
+# tail, at most 3 tokens) is always selected, so 2048 selected tokens plus the tail give an
+# attended width of 2051. Readings (also in the design doc): the softmax runs per dimension over
+# the pool's tokens, ape[j][d] is indexed by the token's slot j in its pool; a token whose
+# valid entry is zero takes no part in its pool's softmax and is never attended; a pool with
+# no valid token has the zero key; a pool is visible to a query once its last token is
+# (kpool p + kpool - 1 <= pos and < kv_len); top_k counts tokens, so top_k / kpool pools
+# are kept.
+def packed_fields(packed, D: int, row_dtype: int):
+    """Packed rows [B][n_kv][>= 2 D + 1] -> (k [B][n_kv][D], gate [B][n_kv][D], valid
+    [B][n_kv] bool), decoded exactly. valid is any nonzero value (+0 and -0 are not valid)."""
+    x = decode(packed, row_dtype)
+    return x[..., :D], x[..., D:2 * D], x[..., 2 * D] != 0
+
+
+def kpool_compress_f64(packed, ape, D: int, kpool: int, row_dtype: int) -> np.ndarray:
+    """Pool keys [B][n_kv // kpool][D] in float64: for pool p and dim d, over the valid tokens
+    t = kpool p + j of the pool, a = gate[t][d] + ape[j][d], wts = softmax_j(a),
+    key[p][d] = sum_j wts_j k[t][d]. A pool with no valid token has the zero key."""
+    k, gate, valid = packed_fields(packed, D, row_dtype)
+    ape = np.asarray(ape, np.float64)
+    B, n_kv = valid.shape
+    n_pool = n_kv // kpool
+    out = np.zeros((B, n_pool, D))
+    for b in range(B):
+        for p in range(n_pool):
+            toks = [kpool * p + j for j in range(kpool) if valid[b, kpool * p + j]]
+            if not toks:
+                continue
+            a = np.stack([gate[b, t] + ape[t - kpool * p] for t in toks])  # [n][D]
+            e = np.exp(a - a.max(axis=0, keepdims=True))
+            wts = e / e.sum(axis=0, keepdims=True)
+            out[b, p] = (wts * np.stack([k[b, t] for t in toks])).sum(axis=0)
+    return out
+
+
+def kpool_compress(packed, ape, D: int, kpool: int, row_dtype: int, out_dtype: int) -> np.ndarray:
+    """kpool_compress_f64 rounded to the pool-cache dtype (see encode)."""
+    return encode(kpool_compress_f64(packed, ape, D, kpool, row_dtype), out_dtype)
+
+
+def kpool_positions(kv_len, q_pos, n_q: int, kpool: int):
+    """Token-level (kv_len [B], q_pos [B][n_q] or None) -> pool-level ones: pools wholly
+    inside the cache, and the last pool whose final token is at or before the query."""
+    kv_len = np.asarray(kv_len, np.int64)
+    qp = _default_q_pos(kv_len, n_q) if q_pos is None else np.asarray(q_pos, np.int64)
+    return kv_len // kpool, (qp + 1) // kpool - 1
+
+
+def kpool_scores(q, pooled, w, kv_len, q_pos, scale: float, kpool: int, q_dtype: int, k_dtype: int):
+    """Scores of every pool key [B][n_q][n_pool] fp32: the plain indexer score of section 1
+    over the pool keys, with pool-level visibility (kpool_positions)."""
+    n_q = np.asarray(q).shape[1]
+    pl, pp = kpool_positions(kv_len, q_pos, n_q, kpool)
+    return index_score(q, pooled, w, pl, pp, scale, q_dtype, k_dtype)
+
+
+def kpool_select(pool_scores, packed_valid, kv_len, q_pos, top_k: int, kpool: int) -> np.ndarray:
+    """Token indices [B][n_q][kpool * (top_k // kpool) + kpool - 1] int32: the top_k // kpool
+    best pools (section 2's rule: ties to the lower pool, ascending, -1 padded), each
+    expanded to its kpool tokens in order, then the tail tokens kpool * floor((pos + 1) /
+    kpool) .. pos, always selected; -1 for padding, tokens whose valid entry is zero and
+    tail slots past the query."""
+    S = np.asarray(pool_scores)
+    B, n_q, n_pool = S.shape
+    kp = top_k // kpool
+    width = kpool * kp + kpool - 1
+    kv_len = np.asarray(kv_len, np.int64)
+    qp = _default_q_pos(kv_len, n_q) if q_pos is None else np.asarray(q_pos, np.int64)
+    pidx = topk(S.reshape(-1, n_pool), kp).reshape(B, n_q, kp)
+    out = np.full((B, n_q, width), -1, np.int32)
+    for b in range(B):
+        for i in range(n_q):
+            for s in range(kp):
+                p = int(pidx[b, i, s])
+                if p < 0:
+                    continue
+                for j in range(kpool):
+                    t = kpool * p + j
+                    if packed_valid[b, t]:
+                        out[b, i, kpool * s + j] = t
+            pos = int(qp[b, i])
+            t0 = kpool * ((pos + 1) // kpool)
+            for j in range(kpool - 1):
+                t = t0 + j
+                if t <= pos and t < min(int(kv_len[b]), packed_valid.shape[1]) and packed_valid[b, t]:
+                    out[b, i, kpool * kp + j] = t
+    return out
+
+
+def kpool_step(inp: dict, wl) -> dict:
+    """The pooled chain of one decode step: compress every complete pool of the cache, score
+    the pools, select tokens, attend (NoPE latent rows)."""
+    pooled = kpool_compress(inp["packed"], inp["ape"], wl.D, wl.kpool, wl.idx_dtype, wl.idx_dtype)
+    S = kpool_scores(inp["q"], pooled, inp["w"], inp["kv_len"], inp["q_pos"], wl.scale, wl.kpool,
+                     wl.idx_dtype, wl.idx_dtype)
+    _, _, valid = packed_fields(inp["packed"], wl.D, wl.idx_dtype)
+    idx = kpool_select(S, valid, inp["kv_len"], inp["q_pos"], wl.top_k, wl.kpool)
+    out, lse = sparse_mla(inp["qa"], inp["latent"], idx, wl.sm_scale, wl.d_latent, wl.mla_dtype,
+                          inp["kv_len"])
+    return {"pooled": pooled, "scores": S, "idx": idx, "out": out, "lse": lse}

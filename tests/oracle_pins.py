@@ -432,3 +432,140 @@ def pins_sink(fn, plain, topk):
             lim = min(kv_len[b], q_pos[b, i] + 1)
             must = {t for t in range(start[b], start[b] + 3) if t < lim}
             assert must <= set(sel[b, i].tolist()), (b, i, must, sel[b, i])
+
+
+# ----------------------------------------------------------------------------
+# pooled indexer (vllm-rdna "Glm5Next" PR: packed rows k | gate | valid, pools of kpool
+# tokens compressed with softmax(gate + ape), pool scores, pools expanded to tokens plus the
+# always-selected tail)
+#   compress(packed, ape, D, kpool, row_dtype) -> float64 [B][n_kv // kpool][D]
+#   select(pool_scores, valid, kv_len, q_pos, top_k, kpool) -> int32 [B][n_q][width]
+# ----------------------------------------------------------------------------
+def _pack(k, gate, valid):
+    return np.concatenate([k, gate, np.asarray(valid, np.float64)[..., None]], axis=-1).astype(np.float32)
+
+
+def pins_kpool_compress(fn):
+    rng = _rng(21)
+    B, n_kv, D, kp = 2, 16, 8, 4
+    k = rng.standard_normal((B, n_kv, D))
+    ones = np.ones((B, n_kv))
+    # equal gates and no position embedding: the mean of the pool's tokens
+    got = fn(_pack(k, np.zeros((B, n_kv, D)), ones), np.zeros((kp, D)), D, kp, 0)
+    assert got.shape == (B, n_kv // kp, D), "pool count"
+    _close(got, k.astype(np.float32).astype(np.float64).reshape(B, n_kv // kp, kp, D).mean(axis=2), 1e-12,
+           "uniform pool = mean")
+    # a gate 60 above the others picks that token, in that dim only (softmax per dim, over tokens)
+    gate = np.zeros((B, n_kv, D))
+    gate[0, 5, 3] = 60.0
+    got = fn(_pack(k, gate, ones), np.zeros((kp, D)), D, kp, 0)
+    k32 = k.astype(np.float32).astype(np.float64)
+    assert abs(got[0, 1, 3] - k32[0, 5, 3]) <= 1e-20 + 1e-12 * abs(k32[0, 5, 3]), "one-hot gate"
+    others = [d for d in range(D) if d != 3]
+    _close(got[0, 1, others], k32[0, 4:8, others].mean(axis=1), 1e-12, "other dims stay uniform")
+    # the position embedding is indexed by the token's slot in its pool: moving it into the
+    # gates of every pool changes nothing
+    gate = rng.standard_normal((B, n_kv, D))
+    ape = rng.standard_normal((kp, D)) * 2
+    slot = np.arange(n_kv) % kp
+    a = fn(_pack(k, gate, ones), ape.astype(np.float32), D, kp, 0)
+    b = fn(_pack(k, gate + ape.astype(np.float32).astype(np.float64)[slot][None], ones), np.zeros((kp, D)), D, kp, 0)
+    _close(a, b, 1e-6, "ape = per-slot gate shift")
+    # a common shift of a pool's gates in one dim changes nothing (softmax over the pool)
+    g2 = gate.copy()
+    g2[1, 8:12, :] += 7.0
+    _close(fn(_pack(k, g2, ones), ape.astype(np.float32), D, kp, 0), a, 1e-6, "shift invariance")
+    # against scipy's softmax, pool by pool
+    pk = _pack(k, gate, ones).astype(np.float64)
+    for bb in range(B):
+        for p in range(n_kv // kp):
+            z = pk[bb, kp * p:kp * p + kp, D:2 * D] + ape.astype(np.float32).astype(np.float64)
+            want = (scipy.special.softmax(z, axis=0) * pk[bb, kp * p:kp * p + kp, :D]).sum(axis=0)
+            _close(a[bb, p], want, 1e-12, f"scipy softmax pool {p}")
+    # invalid tokens take no part; a pool without valid tokens is zero
+    valid = ones.copy()
+    valid[0, 1] = 0.0
+    valid[1, 12:16] = 0.0
+    got = fn(_pack(k, np.zeros((B, n_kv, D)), valid), np.zeros((kp, D)), D, kp, 0)
+    _close(got[0, 0], k32[0, [0, 2, 3]].mean(axis=0), 1e-12, "invalid token excluded")
+    assert np.all(got[1, 3] == 0.0), "empty pool is zero"
+    # pools group tokens kpool p .. kpool p + kpool - 1
+    kk = np.zeros((B, n_kv, D))
+    kk[:, 4:8] = 1.0
+    got = fn(_pack(kk, gate, ones), ape.astype(np.float32), D, kp, 0)
+    assert np.all(np.abs(got[:, 1] - 1.0) < 1e-12) and np.all(got[:, [0, 2, 3]] == 0.0), "pool grouping"
+    # a partial pool at the end of the cache is not compressed
+    assert fn(_pack(k[:, :15], gate[:, :15], ones[:, :15]), ape, D, kp, 0).shape == (B, 3, D), "partial pool"
+
+
+def _brute_select(S, valid, kv_len, q_pos, top_k, kp):
+    """Independent restatement on tiny inputs: rank pools by (score desc, index asc) among
+    finite scores, keep top_k // kp, list their tokens, then the tail."""
+    B, n_q, n_pool = S.shape
+    kk = top_k // kp
+    out = []
+    for b in range(B):
+        for i in range(n_q):
+            cand = [(float(S[b, i, p]), p) for p in range(n_pool) if np.isfinite(S[b, i, p])]
+            cand.sort(key=lambda x: (-x[0], x[1]))
+            pools = sorted(p for _, p in cand[:kk])
+            toks = []
+            for p in pools:
+                toks += [t if valid[b, t] else -1 for t in range(kp * p, kp * p + kp)]
+            toks += [-1] * (kp * kk - len(toks))
+            pos = int(q_pos[b, i])
+            full = (pos + 1) // kp * kp
+            tail = [t if (t <= pos and t < kv_len[b] and valid[b, t]) else -1 for t in range(full, full + kp - 1)]
+            out.append(toks + tail)
+    return np.array(out, np.int32).reshape(B, n_q, -1)
+
+
+def pins_kpool_select(fn, scores_fn, dense_fn, sparse_fn):
+    rng = _rng(22)
+    B, n_q, H, D, kp, n_kv = 3, 2, 4, 8, 4, 40
+    kv_len = np.array([40, 38, 23])
+    q_pos = np.array([[30, 39], [26, 37], [2, 22]])
+    n_pool = n_kv // kp
+    # pool-level visibility: pool p is scored iff kp p + kp - 1 <= pos and kp (p + 1) <= kv_len
+    qi = rng.standard_normal((B, n_q, H, D)).astype(np.float32)
+    pk = rng.standard_normal((B, n_pool, D)).astype(np.float32)
+    w = rng.random((B, n_q, H)).astype(np.float32)
+    # (one query sits past its cache's end, where kv_len alone decides)
+    q_far = q_pos.copy()
+    q_far[2, 1] = 30
+    for qp_ in (q_pos, q_far):
+        S = scores_fn(qi, pk, w, kv_len, qp_, 1.0, kp, 0, 0)
+        for b in range(B):
+            for i in range(n_q):
+                vis = [kp * p + kp - 1 <= qp_[b, i] and kp * (p + 1) <= kv_len[b] for p in range(n_pool)]
+                assert np.array_equal(np.isfinite(S[b, i]), np.array(vis)), f"pool visibility {b} {i}"
+    S = scores_fn(qi, pk, w, kv_len, q_pos, 1.0, kp, 0, 0)
+    valid = np.ones((B, n_kv), bool)
+    valid[1, 5] = False
+    valid[0, 29] = False
+    # ties on purpose
+    Sq = np.round(S * 2) / 2
+    for top_k in (4, 8, 12, 40, 400):
+        got = fn(Sq, valid, kv_len, q_pos, top_k, kp)
+        assert got.shape == (B, n_q, kp * (top_k // kp) + kp - 1), f"width at top_k {top_k}"
+        assert np.array_equal(got, _brute_select(Sq, valid, kv_len, q_pos, top_k, kp)), f"brute force top_k {top_k}"
+    # top_k covering every pool: the selection is every token 0 .. pos, and attention over it
+    # is dense causal attention (no rope part)
+    allv = np.ones((B, n_kv), bool)
+    idx = fn(S, allv, kv_len, q_pos, 4 * n_kv, kp)
+    for b in range(B):
+        for i in range(n_q):
+            sel = sorted(t for t in idx[b, i].tolist() if t >= 0)
+            assert sel == list(range(q_pos[b, i] + 1)), f"full selection {b} {i}"
+    qa = rng.standard_normal((B, n_q, 3, 16)).astype(np.float32)
+    lat = rng.standard_normal((B, n_kv, 16)).astype(np.float32)
+    o_s, l_s = sparse_fn(qa, lat, idx, 0.25, 16, 0, kv_len)
+    o_d, l_d = dense_fn(qa, lat, 0.25, 16, 0, kv_len, q_pos)
+    _close(o_s, o_d, 1e-12, "full kpool selection = dense")
+    _close(l_s, l_d, 1e-12, "full kpool selection = dense (lse)")
+    # tails: pos = kp m + r keeps tokens kp m .. pos when r < kp - 1, none when r = kp - 1
+    for pos in range(12):
+        got = fn(np.full((1, 1, 3), -np.inf), np.ones((1, 12), bool), np.array([12]), np.array([[pos]]), 4, kp)
+        tail = [t for t in got[0, 0].tolist() if t >= 0]
+        m, r = divmod(pos, kp)
+        assert tail == (list(range(kp * m, pos + 1)) if r < kp - 1 else []), f"tail at pos {pos}"

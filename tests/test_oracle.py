@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import workloads
-from oracle_pins import F64, pins_hadamard, pins_mla, pins_prep, pins_rope, pins_scores, pins_sink, pins_topk
+from oracle_pins import (F64, pins_hadamard, pins_kpool_compress, pins_kpool_select, pins_mla, pins_prep,
+                         pins_rope, pins_scores, pins_sink, pins_topk)
 
 
 def test_score_pins():
@@ -325,3 +326,109 @@ def test_sink_pins_catch(kind):
 
 def test_sink_mutant_harness_is_faithful():
     pins_sink(_sink_mutant("none"), oracle.index_score, oracle.topk)
+
+
+# ---------------------------------------------------------------------------
+# pooled indexer
+# ---------------------------------------------------------------------------
+def test_kpool_compress_pins():
+    pins_kpool_compress(oracle.kpool_compress_f64)
+
+
+def _compress_mutant(kind):
+    def fn(packed, ape, D, kpool, row_dtype):
+        k, gate, valid = oracle.packed_fields(packed, D, row_dtype)
+        ape = np.asarray(ape, np.float64)
+        B, n_kv = valid.shape
+        n_pool = n_kv // kpool
+        off = 1 if kind == "pool_offset" else 0
+        out = np.zeros((B, n_pool, D))
+        for b in range(B):
+            for p in range(n_pool):
+                toks = [min(kpool * p + j + off, n_kv - 1) for j in range(kpool)]
+                if kind != "include_invalid":
+                    toks = [t for t in toks if valid[b, t]]
+                if not toks:
+                    continue
+                if kind == "no_ape":
+                    a = np.stack([gate[b, t] for t in toks])
+                elif kind == "ape_by_pool":
+                    a = np.stack([gate[b, t] + ape[p % kpool] for t in toks])
+                else:
+                    a = np.stack([gate[b, t] + ape[t - kpool * p - off] for t in toks])
+                ax = 1 if kind == "softmax_over_dims" else 0
+                e = np.exp(a - a.max(axis=ax, keepdims=True))
+                wts = e if kind == "unnormalised" else e / e.sum(axis=ax, keepdims=True)
+                out[b, p] = (wts * np.stack([k[b, t] for t in toks])).sum(axis=0)
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["pool_offset", "include_invalid", "no_ape", "ape_by_pool",
+                                  "softmax_over_dims", "unnormalised"])
+def test_kpool_compress_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_kpool_compress(_compress_mutant(kind))
+
+
+def test_kpool_compress_mutant_harness_is_faithful():
+    pins_kpool_compress(_compress_mutant("none"))
+
+
+def test_kpool_select_pins():
+    pins_kpool_select(oracle.kpool_select, oracle.kpool_scores, oracle.dense_mla_f64, oracle.sparse_mla_f64)
+
+
+def _kscores_mutant(kind):
+    def fn(q, pooled, w, kv_len, q_pos, scale, kpool, qd, kd):
+        n_q = np.asarray(q).shape[1]
+        pl, pp = oracle.kpool_positions(kv_len, q_pos, n_q, kpool)
+        if kind == "visible_floor":
+            pp = np.asarray(q_pos) // kpool
+        if kind == "len_ceil":
+            pl = (np.asarray(kv_len) + kpool - 1) // kpool
+        return oracle.index_score(q, pooled, w, pl, pp, scale, qd, kd)
+    return fn
+
+
+def _select_mutant(kind):
+    def fn(S, valid, kv_len, q_pos, top_k, kpool):
+        if kind == "pools_as_tokens":
+            return oracle.kpool_select(S, valid, kv_len, q_pos, top_k * kpool, kpool)
+        out = oracle.kpool_select(S, valid, kv_len, q_pos, top_k, kpool)
+        kp = top_k // kpool
+        B, n_q, _ = out.shape
+        for b in range(B):
+            for i in range(n_q):
+                pos = int(np.asarray(q_pos)[b, i])
+                if kind == "no_tail":
+                    out[b, i, kpool * kp:] = -1
+                if kind == "tail_floor":
+                    t0 = kpool * (pos // kpool)
+                    for j in range(kpool - 1):
+                        t = t0 + j
+                        out[b, i, kpool * kp + j] = t if (t <= pos and valid[b, t]) else -1
+                if kind == "keep_invalid":
+                    row = out[b, i]
+                    sel = row[:kpool * kp]
+                    pools = sorted({int(t) // kpool for t in sel if t >= 0})
+                    full = [t for p in pools for t in range(kpool * p, kpool * p + kpool)]
+                    row[:len(full)] = full
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["visible_floor", "len_ceil"])
+def test_kpool_score_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_kpool_select(oracle.kpool_select, _kscores_mutant(kind), oracle.dense_mla_f64, oracle.sparse_mla_f64)
+
+
+@pytest.mark.parametrize("kind", ["pools_as_tokens", "no_tail", "tail_floor", "keep_invalid"])
+def test_kpool_select_pins_catch(kind):
+    with pytest.raises(AssertionError):
+        pins_kpool_select(_select_mutant(kind), oracle.kpool_scores, oracle.dense_mla_f64, oracle.sparse_mla_f64)
+
+
+def test_kpool_mutant_harness_is_faithful():
+    pins_kpool_select(_select_mutant("none"), _kscores_mutant("none"), oracle.dense_mla_f64, oracle.sparse_mla_f64)

@@ -44,6 +44,7 @@ DTYPE_NAMES = {F32: "f32", BF16: "bf16", F16: "f16"}
 # tensor tags for the per-tensor streams
 _TAG_Q, _TAG_K, _TAG_W, _TAG_QA, _TAG_LAT = 1, 2, 3, 4, 5
 _TAG_PQ, _TAG_PK, _TAG_PLAT = 6, 7, 8
+_TAG_KPK, _TAG_GATE, _TAG_APE, _TAG_HOLE = 9, 10, 11, 12
 
 
 @dataclasses.dataclass(frozen=True)
@@ -67,6 +68,7 @@ class Workload:
     scale: float = 1.0       # indexer score scale (applied after the head sum)
     sm_scale: float = 1.0 / 16.0   # 1/sqrt(192 + 64)
     q_pos_start: Optional[int] = None  # causal prefill: query i sits at q_pos_start + i
+    kpool: int = 0           # pooled indexer: tokens per pool (0: the per-token indexer)
 
     @property
     def Dc(self) -> int:
@@ -202,6 +204,47 @@ def gen_prep(wl: Workload, seed: int) -> Dict[str, np.ndarray]:
                     for b in range(wl.B)])
     return {"q_in": q.astype(np.float32), "k_in": k.astype(np.float32),
             "latent_in": round_to(lat, wl.mla_dtype), "pos": wl.q_pos()}
+
+
+# Pooled-indexer decode at the GLM-5.3-Flash DSA shape (vllm-rdna "Glm5Next" PR, architecture
+# section: 32 indexer heads x 128, top-k 2048, pools of 4 tokens; MLA without RoPE, 64 heads
+# over the 512-wide latent), batched like the 32K decode workload.
+KPOOL_DECODE_32K = Workload("kpool_decode_b32_32k", 5, B=32, n_q=1, H=32, D=128, n_kv=32768,
+                            top_k=2048, Hm=64, d_latent=512, d_rope=0, idx_dtype=F16,
+                            mla_dtype=BF16, rotate=False, w_scale=1.0 / math.sqrt(32.0),
+                            latent_std=0.5, kpool=4)
+
+
+def gen_kpool(wl: Workload, seed: int, hole_frac: float = 0.0, kv_len=None) -> Dict[str, np.ndarray]:
+    """Inputs of the pooled-indexer chain. Packed indexer rows [B][n_kv][2 D + 1] in the
+    indexer dtype: k ~ N(0, 1) / sqrt(D), gate ~ N(0, 1), valid = 1 for written tokens
+    (t < kv_len[b]) and 0 beyond, and 0 for a hole_frac fraction of written tokens when asked;
+    ape [kpool][D] fp32 ~ N(0, 1); indexer q [B][n_q][H][D] ~ N(0, 1) / sqrt(D); w ~ U(0, 1)
+    * w_scale; absorbed query [B][n_q][Hm][d_latent] ~ N(0, 1); latent [B][n_kv][d_latent] ~
+    N(0, latent_std). kv_len defaults to n_kv - (b % kpool), so the sequences end with tails of
+    0 .. kpool - 1 tokens; q_pos = kv_len - n_q + i."""
+    D, kp = wl.D, wl.kpool
+    if kv_len is None:
+        kv_len = np.array([wl.n_kv - (b % kp) for b in range(wl.B)], np.int32)
+    kv_len = np.asarray(kv_len, np.int32)
+    s = 1.0 / math.sqrt(D)
+    packed, q, w, qa, lat = [], [], [], [], []
+    for b in range(wl.B):
+        k = _draw_normal(_rng(seed, wl.wid, b, _TAG_KPK), (wl.n_kv, D), s)
+        gate = _draw_normal(_rng(seed, wl.wid, b, _TAG_GATE), (wl.n_kv, D), 1.0)
+        valid = (np.arange(wl.n_kv) < kv_len[b]).astype(np.float64)
+        if hole_frac > 0:
+            valid[_rng(seed, wl.wid, b, _TAG_HOLE).random(wl.n_kv) < hole_frac] = 0.0
+        packed.append(round_to(np.concatenate([k, gate, valid[:, None]], axis=1), wl.idx_dtype))
+        q.append(round_to(_draw_normal(_rng(seed, wl.wid, b, _TAG_Q), (wl.n_q, wl.H, D), s), wl.idx_dtype))
+        w.append((_rng(seed, wl.wid, b, _TAG_W).random((wl.n_q, wl.H)) * wl.w_scale).astype(np.float32))
+        qa.append(round_to(_draw_normal(_rng(seed, wl.wid, b, _TAG_QA), (wl.n_q, wl.Hm, wl.Dc), 1.0), wl.mla_dtype))
+        lat.append(round_to(_draw_normal(_rng(seed, wl.wid, b, _TAG_LAT), (wl.n_kv, wl.Dc), wl.latent_std),
+                            wl.mla_dtype))
+    ape = _draw_normal(_rng(seed, wl.wid, 0, _TAG_APE), (kp, D), 1.0).astype(np.float32)
+    q_pos = (kv_len[:, None].astype(np.int64) - wl.n_q + np.arange(wl.n_q)[None]).astype(np.int32)
+    return {"packed": np.stack(packed), "ape": ape, "q": np.stack(q), "w": np.stack(w),
+            "qa": np.stack(qa), "latent": np.stack(lat), "kv_len": kv_len, "q_pos": q_pos}
 
 
 def random_scores(rows: int, n: int, seed: int, tie_frac: float = 0.0, neg_inf_frac: float = 0.0,
