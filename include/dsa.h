@@ -206,6 +206,72 @@ int dsa_topk_source_layer(int layer);
  */
 int dsa_set_tuning(const char* key, int value);
 
+/*
+ * Pooled (kpool) indexer, a second DSA variant (vllm-rdna pull request "Glm5Next
+ * (GLM-5.3-Flash) on gfx1030": architecture section, DSA attention commit and first-cut
+ * kernel commit). The indexer cache keeps one packed row per token, k[D] | gate[D] | valid
+ * (257 values for D = 128); groups of kpool consecutive tokens (pools) are compressed into
+ * one key with softmax(gate + ape) weights, queries score pool keys, top-k picks pools, and
+ * the attended set is the selected pools' tokens plus the last incomplete pool (the tail),
+ * which is always attended. A decode step is dsa_kpool_index_score -> dsa_topk over pools
+ * (top_pools = top_k / kpool) -> dsa_kpool_expand -> dsa_sparse_mla_attn over the tokens.
+ */
+
+/*
+ * Pool keys of pools [pool_begin, pool_end) of every sequence:
+ *
+ *   pooled[b][p][d] = sum_j softmax_j(gate[t_j][d] + ape[j][d]) * k[t_j][d]
+ *
+ * over the pool's tokens t_j = kpool p + j (j < kpool) whose valid entry is nonzero (+0 and
+ * -0 are not valid); a pool without valid tokens gets the zero key. Computed in fp32 and
+ * rounded to out_dtype (nearest even).
+ *
+ * packed     device, [B][n_kv][row_stride] of row_dtype: k in columns 0..D-1, gate in
+ *            D..2D-1, valid in column 2D (row_stride >= 2 D + 1; 257 packs D = 128 rows)
+ * ape        device, [kpool][D] fp32 position embedding of a token's slot in its pool
+ * pooled     device, [B][n_kv / kpool][D] of out_dtype (the pool cache); only the given
+ *            pools are written
+ * 1 <= kpool <= 8, D <= 4096, 0 <= pool_begin <= pool_end <= n_kv / kpool (a decode step
+ * compresses the one pool that its new token completes; a prefill compresses them all).
+ */
+int dsa_kpool_compress(const void* packed, int row_stride, int row_dtype, const float* ape, void* pooled,
+                       int out_dtype, int B, int n_kv, int D, int kpool, int pool_begin, int pool_end,
+                       hipStream_t stream);
+
+/*
+ * Scores of pool keys: dsa_index_score over the pool cache (n_pool = pools per sequence),
+ * with kv_len and q_pos in tokens. Pool p is scored when all its tokens are in the cache and
+ * the last one is at or before the query: kpool (p + 1) <= kv_len[b] and
+ * kpool p + kpool - 1 <= q_pos[b][i]; otherwise its score is -inf. Shapes, dtypes, defaults
+ * (kv_len NULL: n_pool * kpool tokens; q_pos NULL: kv_len - n_q + i) and errors as in
+ * dsa_index_score; scores is [B][n_q][n_pool]. 1 <= kpool <= 8.
+ */
+int dsa_kpool_index_score(const void* q, const void* pooled, const float* w, const int32_t* kv_len,
+                          const int32_t* q_pos, float* scores, int B, int n_q, int H, int D, int n_pool,
+                          int kpool, int q_dtype, int k_dtype, float scale, hipStream_t stream);
+
+/*
+ * Selected pools -> attended tokens.
+ *
+ *   tok_idx[b][i][kpool s + j]           = kpool * pool_idx[b][i][s] + j      (s < top_pools, j < kpool)
+ *   tok_idx[b][i][kpool top_pools + j]   = kpool * floor((pos + 1) / kpool) + j   (j < kpool - 1, the tail)
+ *
+ * with -1 for a -1 pool, a token whose valid entry is zero, a token at or past kv_len[b], and
+ * a tail token after the query position pos = q_pos[b][i]. The width is
+ * kpool * top_pools + kpool - 1 (2051 for 512 pools of 4); pool order is kept, so ascending
+ * pool indices (dsa_topk's output) give ascending tokens.
+ *
+ * pool_idx   device, [B][n_q][top_pools] int32 (dsa_topk over the pool scores)
+ * packed     device, the packed rows of dsa_kpool_compress (only the valid column is read)
+ * kv_len     device, [B] int32 tokens, or NULL (n_kv)
+ * q_pos      device, [B][n_q] int32 token positions, or NULL (kv_len - n_q + i)
+ * tok_idx    device, [B][n_q][kpool * top_pools + kpool - 1] int32 out
+ * B * n_q <= 65535, 1 <= kpool <= 8.
+ */
+int dsa_kpool_expand(const int32_t* pool_idx, const void* packed, int row_stride, int row_dtype, int D,
+                     const int32_t* kv_len, const int32_t* q_pos, int32_t* tok_idx, int B, int n_q, int n_kv,
+                     int top_pools, int kpool, hipStream_t stream);
+
 /* Static text of a status code. */
 const char* dsa_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -481,7 +481,7 @@ def kpool_select(pool_scores, packed_valid, kv_len, q_pos, top_k: int, kpool: in
             t0 = kpool * ((pos + 1) // kpool)
             for j in range(kpool - 1):
                 t = t0 + j
-                if t <= pos and t < min(int(kv_len[b]), packed_valid.shape[1]) and packed_valid[b, t]:
+                if 0 <= t <= pos and t < min(int(kv_len[b]), packed_valid.shape[1]) and packed_valid[b, t]:
                     out[b, i, kpool * kp + j] = t
     return out
 

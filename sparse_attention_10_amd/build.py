@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["index_score.hip", "topk.hip", "sparse_mla.hip", "indexer_prep.hip", "dsa_api.cpp"]
+SOURCES = ["index_score.hip", "topk.hip", "sparse_mla.hip", "indexer_prep.hip", "kpool.hip", "dsa_api.cpp"]
 ARCH = "gfx950"
 
 

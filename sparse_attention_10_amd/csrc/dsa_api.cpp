@@ -95,7 +95,7 @@ int dsa_set_tuning(const char* key, int value) {
 static int index_score_checked(const char* fn, const void* q, const void* k_cache, const float* w,
                                const int32_t* kv_len, const int32_t* q_pos, float* scores, int B, int n_q,
                                int H, int D, int n_kv, int q_dtype, int k_dtype, float scale,
-                               dsa::SinkArgs sink, hipStream_t stream) {
+                               dsa::ScoreArgs sink, hipStream_t stream) {
   if (!q || !k_cache || !w || !scores)
     return fail(DSA_ERR_NULL, "%s: q, k_cache, w and scores must be non-NULL", fn);
   if (B < 1 || n_q < 1 || H < 1 || D < 1 || n_kv < 1)
@@ -121,7 +121,7 @@ int dsa_index_score(const void* q, const void* k_cache, const float* w, const in
                     const int32_t* q_pos, float* scores, int B, int n_q, int H, int D, int n_kv,
                     int q_dtype, int k_dtype, float scale, hipStream_t stream) {
   return index_score_checked("dsa_index_score", q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv,
-                             q_dtype, k_dtype, scale, dsa::SinkArgs{nullptr, 0, 0.f}, stream);
+                             q_dtype, k_dtype, scale, dsa::ScoreArgs{nullptr, 0, 0.f, 1}, stream);
 }
 
 int dsa_index_score_sink(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
@@ -131,7 +131,7 @@ int dsa_index_score_sink(const void* q, const void* k_cache, const float* w, con
   if (n_sink < 0) return fail(DSA_ERR_SHAPE, "dsa_index_score_sink: n_sink=%d must be >= 0", n_sink);
   if (!std::isfinite(sink_boost)) return fail(DSA_ERR_SHAPE, "dsa_index_score_sink: sink_boost must be finite");
   return index_score_checked("dsa_index_score_sink", q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv,
-                             q_dtype, k_dtype, scale, dsa::SinkArgs{sink_start, n_sink, sink_boost}, stream);
+                             q_dtype, k_dtype, scale, dsa::ScoreArgs{sink_start, n_sink, sink_boost, 1}, stream);
 }
 
 size_t dsa_topk_workspace_size(int rows, int n_kv, int top_k) {
@@ -233,4 +233,51 @@ int dsa_indexer_prep(const float* q_in, const float* k_in, const void* latent_in
                     "dsa_indexer_prep launch");
 }
 
+int dsa_kpool_compress(const void* packed, int row_stride, int row_dtype, const float* ape, void* pooled,
+                       int out_dtype, int B, int n_kv, int D, int kpool, int pool_begin, int pool_end,
+                       hipStream_t stream) {
+  if (!packed || !ape || !pooled)
+    return fail(DSA_ERR_NULL, "dsa_kpool_compress: packed, ape and pooled must be non-NULL");
+  if (B < 1 || n_kv < 1 || D < 1 || D > 4096 || kpool < 1 || kpool > 8 || row_stride < 2 * D + 1)
+    return fail(DSA_ERR_SHAPE, "dsa_kpool_compress: B=%d n_kv=%d D=%d kpool=%d row_stride=%d out of range "
+                               "(D <= 4096, 1 <= kpool <= 8, row_stride >= 2 D + 1)", B, n_kv, D, kpool, row_stride);
+  if (B > 65535 || (long long)B * n_kv * row_stride > (1LL << 40))
+    return fail(DSA_ERR_SHAPE, "dsa_kpool_compress: cache too large");
+  if (pool_begin < 0 || pool_end < pool_begin || pool_end > n_kv / kpool)
+    return fail(DSA_ERR_SHAPE, "dsa_kpool_compress: pools [%d, %d) outside [0, %d)", pool_begin, pool_end,
+                n_kv / kpool);
+  if (!valid_dtype(row_dtype) || !valid_dtype(out_dtype))
+    return fail(DSA_ERR_DTYPE, "dsa_kpool_compress: unknown dtype (rows %d, pooled %d)", row_dtype, out_dtype);
+  return hip_status(dsa::launch_kpool_compress(packed, row_stride, row_dtype, ape, pooled, out_dtype, B, n_kv, D,
+                                               kpool, pool_begin, pool_end, stream),
+                    "dsa_kpool_compress launch");
+}
+
+int dsa_kpool_index_score(const void* q, const void* pooled, const float* w, const int32_t* kv_len,
+                          const int32_t* q_pos, float* scores, int B, int n_q, int H, int D, int n_pool,
+                          int kpool, int q_dtype, int k_dtype, float scale, hipStream_t stream) {
+  if (kpool < 1 || kpool > 8)
+    return fail(DSA_ERR_SHAPE, "dsa_kpool_index_score: kpool=%d must be in [1, 8]", kpool);
+  return index_score_checked("dsa_kpool_index_score", q, pooled, w, kv_len, q_pos, scores, B, n_q, H, D, n_pool,
+                             q_dtype, k_dtype, scale, dsa::ScoreArgs{nullptr, 0, 0.f, kpool}, stream);
+}
+
+int dsa_kpool_expand(const int32_t* pool_idx, const void* packed, int row_stride, int row_dtype, int D,
+                     const int32_t* kv_len, const int32_t* q_pos, int32_t* tok_idx, int B, int n_q, int n_kv,
+                     int top_pools, int kpool, hipStream_t stream) {
+  if (!pool_idx || !packed || !tok_idx)
+    return fail(DSA_ERR_NULL, "dsa_kpool_expand: pool_idx, packed and tok_idx must be non-NULL");
+  if (B < 1 || n_q < 1 || n_kv < 1 || D < 1 || top_pools < 1 || kpool < 1 || kpool > 8 || row_stride < 2 * D + 1)
+    return fail(DSA_ERR_SHAPE, "dsa_kpool_expand: B=%d n_q=%d n_kv=%d D=%d top_pools=%d kpool=%d row_stride=%d "
+                               "out of range", B, n_q, n_kv, D, top_pools, kpool, row_stride);
+  if ((long long)B * n_q > 65535 || (long long)kpool * top_pools + kpool - 1 > (1 << 24) ||
+      (long long)B * n_kv * row_stride > (1LL << 40))
+    return fail(DSA_ERR_SHAPE, "dsa_kpool_expand: B * n_q (<= 65535), width or cache too large");
+  if (!valid_dtype(row_dtype)) return fail(DSA_ERR_DTYPE, "dsa_kpool_expand: unknown row dtype %d", row_dtype);
+  return hip_status(dsa::launch_kpool_expand(pool_idx, packed, row_stride, row_dtype, D, kv_len, q_pos, tok_idx,
+                                             B, n_q, n_kv, top_pools, kpool, stream),
+                    "dsa_kpool_expand launch");
+}
+
 }  // extern "C"
+

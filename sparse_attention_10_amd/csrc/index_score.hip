@@ -31,13 +31,29 @@ struct SinkRange {
   float boost;
   __device__ __forceinline__ float add(int t, float v) const { return t >= lo && t < hi ? v + boost : v; }
 };
-__device__ __forceinline__ SinkRange sink_range(const SinkArgs& s, int b) {
+__device__ __forceinline__ SinkRange sink_range(const ScoreArgs& s, int b) {
   SinkRange r{0, 0, s.boost};
   if (s.n > 0) {
     r.lo = s.start ? s.start[b] : 0;
     r.hi = (int)min((long)r.lo + s.n, (long)INT_MAX);
   }
   return r;
+}
+
+// Keys [0, limit) of query i of sequence b (row bi) are scored, the rest are -inf: keys after
+// the query's position or past the cache's length (ik_llama_opt log, lightning-indexer
+// sub-commit: causal mask). With pools of kpool tokens (vllm-rdna "Glm5Next" PR, kpool
+// indexer) key p holds tokens kpool p .. kpool p + kpool - 1; it is in the cache when all of
+// them are and visible once its last one is: limit = min(floor(len / kpool),
+// floor((pos + 1) / kpool)), with len and pos in tokens.
+__device__ __forceinline__ long floor_div(long a, long m) { return a >= 0 ? a / m : -((-a + m - 1) / m); }
+__device__ __forceinline__ int key_limit(const int* kv_len, const int* q_pos, long bi, int b, int i, int n_q,
+                                         int n_kv, int kpool) {
+  const long cap = (long)n_kv * kpool;
+  const long len = kv_len ? min((long)kv_len[b], cap) : cap;
+  const long pos = q_pos ? (long)q_pos[bi] : len - n_q + i;
+  const long lim = min(floor_div(len, kpool), floor_div(pos + 1, kpool));
+  return (int)max(0L, min(lim, (long)n_kv));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -47,19 +63,18 @@ template <typename T>
 __global__ __launch_bounds__(256) void index_score_plain(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
-    int n_q, int H, int D, int n_kv, float scale, SinkArgs sink) {
+    int n_q, int H, int D, int n_kv, float scale, ScoreArgs sink) {
   extern __shared__ float qs[];  // [H][D] of this query
   const int bi = blockIdx.y;
   const int b = bi / n_q, i = bi - b * n_q;
   const T* qp = q + (long)bi * H * D;
   for (int e = threadIdx.x; e < H * D; e += blockDim.x) qs[e] = load_as_f32(qp, e);
   __syncthreads();
-  const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
-  const int pos = q_pos ? q_pos[bi] : len - n_q + i;
+  const int limit = key_limit(kv_len, q_pos, bi, b, i, n_q, n_kv, sink.kpool);
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n_kv) return;
   float* out = scores + (long)bi * n_kv;
-  if (t > pos || t >= len) {
+  if (t >= limit) {
     out[t] = -INFINITY;
     return;
   }
@@ -190,16 +205,14 @@ template <typename T16, int ITERS, bool FULLH>
 __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
-    int n_q, int H, int n_kv, float scale, SinkArgs sink) {
+    int n_q, int H, int n_kv, float scale, ScoreArgs sink) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDecWaves][64 * 256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int bi = blockIdx.y;
   const int b = bi / n_q, i = bi - b * n_q;
-  const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
-  const int pos = q_pos ? q_pos[bi] : len - n_q + i;
-  const int limit = min(len, pos + 1);  // keys [0, limit) are scored, the rest are -inf
+  const int limit = key_limit(kv_len, q_pos, bi, b, i, n_q, n_kv, sink.kpool);  // keys [0, limit) are scored
   const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k) + (long)b * n_kv * 256;
   float* out = scores + (long)bi * n_kv;
   uint8_t* my = lds[wave];
@@ -277,7 +290,7 @@ template <typename T16, int NWV, bool FULLH>
 __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
-    int n_q, int H, int n_kv, int key_span, float scale, SinkArgs sink) {
+    int n_q, int H, int n_kv, int key_span, float scale, ScoreArgs sink) {
   constexpr int kPreQB = NWV * kPreQPW;     // queries per block
   constexpr int kCPT = 1024 / (NWV * 64);  // 16-byte tile chunks each thread stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][64 * 256];
@@ -288,15 +301,9 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
   const int g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.z;
   const int q0 = blockIdx.x * kPreQB;
-  const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
   if (tid < kPreQB) {
     const int qi = q0 + tid;
-    int lim = 0;
-    if (qi < n_q) {
-      const int pos = q_pos ? q_pos[(long)b * n_q + qi] : len - n_q + qi;
-      lim = max(0, min(len, pos + 1));
-    }
-    s_limit[tid] = lim;
+    s_limit[tid] = qi < n_q ? key_limit(kv_len, q_pos, (long)b * n_q + qi, b, qi, n_q, n_kv, sink.kpool) : 0;
   }
   __syncthreads();
   int kmax = 0;
@@ -434,7 +441,7 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
 template <typename T16>
 static hipError_t launch_mfma(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int n_kv,
-                              float scale, SinkArgs sink, hipStream_t stream) {
+                              float scale, ScoreArgs sink, hipStream_t stream) {
   if (n_q >= 8) {
     const int nwv = g_score_prefill_waves > 0 ? g_score_prefill_waves : kPrefillWaves;
     const int qb = nwv * kPreQPW;
@@ -486,7 +493,7 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
 
 hipError_t launch_index_score(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int D,
-                              int n_kv, int dtype, float scale, SinkArgs sink, hipStream_t stream) {
+                              int n_kv, int dtype, float scale, ScoreArgs sink, hipStream_t stream) {
   const bool mfma_ok = D == 128 && H <= 32 && (dtype == kBF16 || dtype == kF16);
   if (mfma_ok) {
     if (dtype == kBF16)

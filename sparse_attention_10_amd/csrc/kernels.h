@@ -10,19 +10,21 @@ namespace dsa {
 
 constexpr int kF32 = 0, kBF16 = 1, kF16 = 2;
 
-// Attention-sink boost: scores of keys [start[b], start[b] + n) of sequence b get + boost
-// (start NULL: 0; n = 0: off). Masked keys stay -inf.
-struct SinkArgs {
+// Score options. Attention-sink boost: scores of keys [start[b], start[b] + n) of sequence b
+// get + boost (start NULL: 0; n = 0: off); masked keys stay -inf. kpool: each key stands for a
+// pool of kpool consecutive tokens, while kv_len and q_pos stay in tokens (1: keys are tokens).
+struct ScoreArgs {
   const int* start;
   int n;
   float boost;
+  int kpool;
 };
 
 extern int g_score_cpw;  // 64-key chunks per wave of the decode scoring kernel, 0 automatic
 extern int g_score_prefill_waves;  // waves per block of the prefill scoring kernel (4 or 8), 0 automatic
 hipError_t launch_index_score(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int D,
-                              int n_kv, int dtype, float scale, SinkArgs sink, hipStream_t stream);
+                              int n_kv, int dtype, float scale, ScoreArgs sink, hipStream_t stream);
 
 // top-k: path 0 = automatic, 1 = one workgroup per row, 2 = two-stage, 3 = filtered
 struct TopkPlan {
@@ -50,5 +52,13 @@ hipError_t launch_indexer_prep(const float* q_in, const float* k_in, const void*
                                void* q_out, void* k_cache, void* latent_cache, int B, int n_new, int H,
                                int n_kv, int row_bytes, int out_dtype, double log2_base, int hadamard,
                                hipStream_t stream);
+
+// pooled indexer: pool compression of packed k | gate | valid rows, pool -> token expansion
+hipError_t launch_kpool_compress(const void* packed, int row_stride, int row_dtype, const float* ape,
+                                 void* pooled, int out_dtype, int B, int n_kv, int D, int kpool,
+                                 int pool_begin, int pool_end, hipStream_t stream);
+hipError_t launch_kpool_expand(const int* pool_idx, const void* packed, int row_stride, int row_dtype, int D,
+                               const int* kv_len, const int* q_pos, int* tok_idx, int B, int n_q, int n_kv,
+                               int top_pools, int kpool, hipStream_t stream);
 
 }  // namespace dsa

@@ -22,6 +22,7 @@ _DTYPE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.float16: DSA_F
 
 EXPORTED = ("dsa_index_score", "dsa_index_score_sink", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
             "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_indexer_prep", "dsa_layer_computes_topk", "dsa_topk_source_layer", "dsa_set_tuning",
+            "dsa_kpool_compress", "dsa_kpool_index_score", "dsa_kpool_expand",
             "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -53,6 +54,12 @@ def _load() -> ctypes.CDLL:
     lib.dsa_sparse_mla_attn.restype = I
     lib.dsa_indexer_prep.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.dsa_indexer_prep.restype = I
+    lib.dsa_kpool_compress.argtypes = [P, I, I, P, P, I, I, I, I, I, I, I, P]
+    lib.dsa_kpool_compress.restype = I
+    lib.dsa_kpool_index_score.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    lib.dsa_kpool_index_score.restype = I
+    lib.dsa_kpool_expand.argtypes = [P, P, I, I, I, P, P, P, I, I, I, I, I, P]
+    lib.dsa_kpool_expand.restype = I
     lib.dsa_layer_computes_topk.argtypes = [I]
     lib.dsa_layer_computes_topk.restype = I
     lib.dsa_topk_source_layer.argtypes = [I]
@@ -256,3 +263,66 @@ def dsa_topk_source_layer(layer: int) -> int:
 
 def dsa_set_tuning(key: str, value: int) -> None:
     _check(lib.dsa_set_tuning(key.encode(), int(value)), "dsa_set_tuning")
+
+
+def _int32_opt(t: Optional[torch.Tensor], name: str) -> None:
+    if t is not None:
+        _dev(t, name)
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+
+
+def dsa_kpool_compress(packed: torch.Tensor, ape: torch.Tensor, pooled: torch.Tensor, D: int, kpool: int,
+                       pool_begin: int = 0, pool_end: Optional[int] = None, stream=None) -> torch.Tensor:
+    """packed [B][n_kv][row_stride] (k | gate | valid, row_stride >= 2 D + 1), ape [kpool][D] fp32,
+    pooled [B][n_kv // kpool][D] (output; pools [pool_begin, pool_end) are written)."""
+    B, n_kv, stride = packed.shape
+    for t, n in ((packed, "packed"), (ape, "ape"), (pooled, "pooled")):
+        _dev(t, n)
+    if tuple(ape.shape) != (kpool, D) or ape.dtype != torch.float32 or tuple(pooled.shape) != (B, n_kv // kpool, D):
+        raise ValueError("dsa_kpool_compress: inconsistent shapes or dtypes")
+    end = n_kv // kpool if pool_end is None else pool_end
+    _check(lib.dsa_kpool_compress(packed.data_ptr(), stride, _DTYPE[packed.dtype], ape.data_ptr(), pooled.data_ptr(),
+                                  _DTYPE[pooled.dtype], B, n_kv, D, kpool, int(pool_begin), int(end),
+                                  _stream(stream)), "dsa_kpool_compress")
+    return pooled
+
+
+def dsa_kpool_index_score(q: torch.Tensor, pooled: torch.Tensor, w: torch.Tensor, scores: torch.Tensor, kpool: int,
+                          kv_len: Optional[torch.Tensor] = None, q_pos: Optional[torch.Tensor] = None,
+                          scale: float = 1.0, stream=None) -> torch.Tensor:
+    """q [B][n_q][H][D], pooled [B][n_pool][D] (same dtype), w [B][n_q][H] fp32, scores [B][n_q][n_pool]
+    fp32 (output); kv_len [B] and q_pos [B][n_q] int32 in tokens, or None."""
+    B, n_q, H, D = q.shape
+    n_pool = pooled.shape[1]
+    for t, n in ((q, "q"), (pooled, "pooled"), (w, "w"), (scores, "scores")):
+        _dev(t, n)
+    if tuple(pooled.shape) != (B, n_pool, D) or tuple(w.shape) != (B, n_q, H) \
+            or tuple(scores.shape) != (B, n_q, n_pool) or w.dtype != torch.float32 or scores.dtype != torch.float32:
+        raise ValueError("dsa_kpool_index_score: inconsistent shapes or dtypes")
+    _int32_opt(kv_len, "kv_len")
+    _int32_opt(q_pos, "q_pos")
+    _check(lib.dsa_kpool_index_score(q.data_ptr(), pooled.data_ptr(), w.data_ptr(), _ptr(kv_len), _ptr(q_pos),
+                                     scores.data_ptr(), B, n_q, H, D, n_pool, int(kpool), _DTYPE[q.dtype],
+                                     _DTYPE[pooled.dtype], float(scale), _stream(stream)), "dsa_kpool_index_score")
+    return scores
+
+
+def dsa_kpool_expand(pool_idx: torch.Tensor, packed: torch.Tensor, D: int, tok_idx: torch.Tensor, kpool: int,
+                     kv_len: Optional[torch.Tensor] = None, q_pos: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """pool_idx [B][n_q][top_pools] int32, packed [B][n_kv][row_stride], tok_idx
+    [B][n_q][kpool * top_pools + kpool - 1] int32 (output)."""
+    B, n_q, top_pools = pool_idx.shape
+    n_kv, stride = packed.shape[1], packed.shape[2]
+    for t, n in ((pool_idx, "pool_idx"), (packed, "packed"), (tok_idx, "tok_idx")):
+        _dev(t, n)
+    if pool_idx.dtype != torch.int32 or tok_idx.dtype != torch.int32 or packed.shape[0] != B \
+            or tuple(tok_idx.shape) != (B, n_q, kpool * top_pools + kpool - 1):
+        raise ValueError("dsa_kpool_expand: inconsistent shapes or dtypes")
+    _int32_opt(kv_len, "kv_len")
+    _int32_opt(q_pos, "q_pos")
+    _check(lib.dsa_kpool_expand(pool_idx.data_ptr(), packed.data_ptr(), stride, _DTYPE[packed.dtype], D,
+                                _ptr(kv_len), _ptr(q_pos), tok_idx.data_ptr(), B, n_q, n_kv, top_pools, int(kpool),
+                                _stream(stream)), "dsa_kpool_expand")
+    return tok_idx

@@ -209,3 +209,39 @@ def test_indexshare_layer_map(lib):
         assert all(lib.dsa_layer_computes_topk(m) == 0 for m in range(src + 1, l + 1))
     assert lib.dsa_layer_computes_topk(-1) == E_SHAPE
     assert lib.dsa_topk_source_layer(-3) == E_SHAPE
+
+
+def _compress(lib, packed=FAKE, stride=257, rdt=2, ape=FAKE, pooled=FAKE, odt=2, B=2, n_kv=64, D=128, kpool=4,
+              p0=0, p1=16):
+    return lib.dsa_kpool_compress(packed, stride, rdt, ape, pooled, odt, B, n_kv, D, kpool, p0, p1, None)
+
+
+def test_kpool_compress_validation(lib):
+    assert _compress(lib, packed=None) == E_NULL
+    assert _compress(lib, ape=None) == E_NULL
+    assert _compress(lib, pooled=None) == E_NULL
+    assert _compress(lib, stride=256) == E_SHAPE            # no room for the valid column
+    assert _compress(lib, kpool=0) == E_SHAPE
+    assert _compress(lib, kpool=9) == E_SHAPE
+    assert _compress(lib, p1=17) == E_SHAPE                 # past the 16 complete pools
+    assert _compress(lib, p0=5, p1=4) == E_SHAPE
+    assert _compress(lib, p0=-1) == E_SHAPE
+    assert _compress(lib, rdt=7) == E_DTYPE
+    assert _compress(lib, odt=-1) == E_DTYPE
+    assert _compress(lib, p0=3, p1=3) == OK                 # empty range: nothing launched
+
+
+def test_kpool_score_and_expand_validation(lib):
+    f = lib.dsa_kpool_index_score
+    assert f(FAKE, FAKE, FAKE, None, None, FAKE, 1, 1, 32, 128, 100, 0, 1, 1, 1.0, None) == E_SHAPE
+    assert f(FAKE, FAKE, FAKE, None, None, FAKE, 1, 1, 32, 128, 100, 9, 1, 1, 1.0, None) == E_SHAPE
+    assert f(None, FAKE, FAKE, None, None, FAKE, 1, 1, 32, 128, 100, 4, 1, 1, 1.0, None) == E_NULL
+    assert f(FAKE, FAKE, FAKE, None, None, FAKE, 1, 1, 32, 128, 100, 4, 1, 2, 1.0, None) == E_DTYPE
+    g = lib.dsa_kpool_expand
+    assert g(None, FAKE, 257, 2, 128, None, None, FAKE, 1, 1, 64, 4, 4, None) == E_NULL
+    assert g(FAKE, FAKE, 257, 2, 128, None, None, None, 1, 1, 64, 4, 4, None) == E_NULL
+    assert g(FAKE, FAKE, 256, 2, 128, None, None, FAKE, 1, 1, 64, 4, 4, None) == E_SHAPE
+    assert g(FAKE, FAKE, 257, 2, 128, None, None, FAKE, 1, 1, 64, 0, 4, None) == E_SHAPE
+    assert g(FAKE, FAKE, 257, 2, 128, None, None, FAKE, 1, 1, 64, 4, 0, None) == E_SHAPE
+    assert g(FAKE, FAKE, 257, 2, 128, None, None, FAKE, 300, 300, 64, 4, 4, None) == E_SHAPE
+    assert g(FAKE, FAKE, 257, 5, 128, None, None, FAKE, 1, 1, 64, 4, 4, None) == E_DTYPE

@@ -1,0 +1,216 @@
+"""The pooled (kpool) indexer chain on the GPU against the oracle: pool compression of packed
+k | gate | valid rows, pool scores, pool -> token expansion with the always-selected tail, and
+attention over the expanded tokens (vllm-rdna "Glm5Next (GLM-5.3-Flash) on gfx1030" PR).
+
+Rules: 16-bit pool keys equal the oracle's rounding except where the float64 value sits
+within 1e-6 of a rounding midpoint, measured against the pool's largest |k| (the kernel sums
+in fp32, whose error scales with the terms, and may round either way there; fewer than 1e-3
+of the values may differ), fp32 pool keys within 1e-5; pool scores within the dtype tolerance with
+the -inf pattern identical; the expansion fed the oracle's pool selection is bit-exact; end
+to end, pool indices follow the tie-band rule and attention is within tolerance of the
+oracle evaluated on the GPU's own tokens.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import RTOL, assert_rowwise, binding, check_index_rule, dev, host
+
+pytestmark = pytest.mark.gpu
+import torch  # noqa: E402
+
+KP = workloads.KPOOL_DECODE_32K
+TORCH = {workloads.F32: torch.float32, workloads.BF16: torch.bfloat16, workloads.F16: torch.float16}
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return host(t.view(torch.int16)).view(np.uint16)
+
+
+def _term_scale(packed, D, kpool, row_dtype, pools=slice(None)):
+    """Per pool, the largest |k| among its tokens: the scale of the fp32 rounding error of a
+    weighted sum whose terms may cancel."""
+    k, _, _ = oracle.packed_fields(packed, D, row_dtype)
+    B, n_kv, _ = k.shape
+    n_pool = n_kv // kpool
+    m = np.abs(k[:, :n_pool * kpool]).reshape(B, n_pool, kpool * D).max(axis=2)
+    return np.broadcast_to(m[:, pools, None], (B, m[:, pools].shape[1], D))
+
+
+def _check_pool_keys(got: torch.Tensor, x64: np.ndarray, dtype: int, what: str, term: np.ndarray) -> None:
+    if dtype == workloads.F32:
+        assert_rowwise(host(got), x64, 1e-5, what)
+        return
+    want = oracle.encode(x64, dtype)
+    g = _bits(got)
+    bad = g != want
+    if bad.any():
+        gv = oracle.decode(g[bad], dtype)
+        wv = oracle.decode(want[bad], dtype)
+        x = x64[bad]
+        near_mid = np.abs(gv - x) <= np.abs(wv - x) + 1e-6 * term[bad]
+        assert near_mid.all(), f"{what}: {int((~near_mid).sum())} pool-key values off by more than a midpoint flip"
+        assert bad.mean() < 1e-3, f"{what}: {bad.mean():.2e} of the values round differently"
+
+
+def _compress(inp, wl, out_dtype=None, p0=0, p1=None, fill=None):
+    L = binding()
+    packed = dev(inp["packed"], wl.idx_dtype)
+    odt = wl.idx_dtype if out_dtype is None else out_dtype
+    shape = (wl.B, wl.n_kv // wl.kpool, wl.D)
+    pooled = torch.full(shape, fill, dtype=TORCH[odt], device="cuda") if fill is not None else \
+        torch.empty(shape, dtype=TORCH[odt], device="cuda")
+    L.dsa_kpool_compress(packed, dev(inp["ape"]), pooled, wl.D, wl.kpool, p0, p1)
+    return packed, pooled
+
+
+@pytest.mark.parametrize("row_dtype,out_dtype", [(workloads.F16, workloads.F16), (workloads.BF16, workloads.BF16),
+                                                 (workloads.F32, workloads.F32), (workloads.F16, workloads.F32),
+                                                 (workloads.F32, workloads.BF16)])
+def test_compress(row_dtype, out_dtype):
+    wl = KP.scaled(B=3, n_kv=1030, idx_dtype=row_dtype)   # 257 pools and a partial one
+    inp = workloads.gen_kpool(wl, 1, hole_frac=0.2)
+    _, pooled = _compress(inp, wl, out_dtype)
+    torch.cuda.synchronize()
+    x64 = oracle.kpool_compress_f64(inp["packed"], inp["ape"], wl.D, wl.kpool, row_dtype)
+    _check_pool_keys(pooled, x64, out_dtype, f"pool keys {row_dtype}->{out_dtype}",
+                     _term_scale(inp["packed"], wl.D, wl.kpool, row_dtype))
+
+
+def test_compress_range_and_pool_sizes():
+    L = binding()
+    for kpool in (1, 2, 3, 8):
+        wl = KP.scaled(B=2, n_kv=203, D=64, kpool=kpool)
+        inp = workloads.gen_kpool(wl, 2, hole_frac=0.3)
+        n_pool = wl.n_kv // kpool
+        p0, p1 = n_pool // 3, n_pool - 1
+        _, pooled = _compress(inp, wl, p0=p0, p1=p1, fill=7.0)
+        torch.cuda.synchronize()
+        x64 = oracle.kpool_compress_f64(inp["packed"], inp["ape"], wl.D, kpool, wl.idx_dtype)
+        _check_pool_keys(pooled[:, p0:p1].contiguous(), x64[:, p0:p1], wl.idx_dtype, f"kpool {kpool} range",
+                         _term_scale(inp["packed"], wl.D, kpool, wl.idx_dtype, slice(p0, p1)))
+        rest = torch.cat([pooled[:, :p0], pooled[:, p1:]], dim=1)
+        assert bool((rest == 7.0).all()), f"kpool {kpool}: pools outside the range were written"
+    # a packed row wider than 2 D + 1 (padded stride)
+    wl = KP.scaled(B=2, n_kv=64, D=16)
+    inp = workloads.gen_kpool(wl, 3, hole_frac=0.2)
+    wide = np.zeros((2, 64, 40), np.uint16)
+    wide[:, :, :33] = inp["packed"]
+    packed = dev(wide, wl.idx_dtype)
+    pooled = torch.empty((2, 16, 16), dtype=torch.float16, device="cuda")
+    L.dsa_kpool_compress(packed, dev(inp["ape"]), pooled, 16, 4)
+    torch.cuda.synchronize()
+    _check_pool_keys(pooled, oracle.kpool_compress_f64(inp["packed"], inp["ape"], 16, 4, wl.idx_dtype),
+                     wl.idx_dtype, "padded stride", _term_scale(inp["packed"], 16, 4, wl.idx_dtype))
+
+
+@pytest.mark.parametrize("n_q,H,dtype,explicit", [(1, 32, workloads.F16, False), (2, 32, workloads.F16, True),
+                                                  (16, 32, workloads.F16, True), (12, 20, workloads.BF16, True),
+                                                  (3, 4, workloads.F32, True)])
+def test_pool_scores(n_q, H, dtype, explicit):
+    L = binding()
+    wl = KP.scaled(B=3, n_q=n_q, H=H, n_kv=1200, idx_dtype=dtype)
+    inp = workloads.gen_kpool(wl, 4, hole_frac=0.1, kv_len=[1200, 1195, 7])
+    q_pos = None
+    if explicit:
+        rng = np.random.default_rng(5)
+        q_pos = np.stack([rng.integers(-2, int(n), size=n_q) for n in inp["kv_len"]]).astype(np.int32)
+        q_pos[0, 0] = 2   # no complete pool yet
+    pooled_o = oracle.kpool_compress(inp["packed"], inp["ape"], wl.D, wl.kpool, dtype, dtype)
+    n_pool = wl.n_kv // wl.kpool
+    scores = torch.empty((wl.B, n_q, n_pool), dtype=torch.float32, device="cuda")
+    L.dsa_kpool_index_score(dev(inp["q"], dtype), dev(pooled_o, dtype), dev(inp["w"]), scores, wl.kpool,
+                            kv_len=dev(inp["kv_len"]), q_pos=None if q_pos is None else dev(q_pos), scale=0.75)
+    torch.cuda.synchronize()
+    want = oracle.kpool_scores(inp["q"], pooled_o, inp["w"], inp["kv_len"], q_pos, 0.75, wl.kpool, dtype, dtype)
+    assert_rowwise(host(scores), want, RTOL[dtype], f"pool scores n_q={n_q} H={H}")
+
+
+def test_expand_bit_exact():
+    L = binding()
+    for n_q, explicit, top_k in ((1, False, 2048), (3, True, 64), (2, True, 4)):
+        wl = KP.scaled(B=4, n_q=n_q, n_kv=1100, top_k=top_k)
+        inp = workloads.gen_kpool(wl, 6, hole_frac=0.15)
+        q_pos = None
+        if explicit:
+            rng = np.random.default_rng(7)
+            q_pos = np.stack([rng.integers(0, int(n), size=n_q) for n in inp["kv_len"]]).astype(np.int32)
+            q_pos[1, 0] = 1
+        pooled_o = oracle.kpool_compress(inp["packed"], inp["ape"], wl.D, wl.kpool, wl.idx_dtype, wl.idx_dtype)
+        S = oracle.kpool_scores(inp["q"], pooled_o, inp["w"], inp["kv_len"], q_pos, 1.0, wl.kpool,
+                                wl.idx_dtype, wl.idx_dtype)
+        kp = top_k // wl.kpool
+        pidx = oracle.topk(S.reshape(-1, S.shape[-1]), kp).reshape(wl.B, n_q, kp)
+        _, _, valid = oracle.packed_fields(inp["packed"], wl.D, wl.idx_dtype)
+        want = oracle.kpool_select(S, valid, inp["kv_len"], q_pos, top_k, wl.kpool)
+        tok = torch.full(want.shape, 12345, dtype=torch.int32, device="cuda")
+        L.dsa_kpool_expand(dev(pidx), dev(inp["packed"], wl.idx_dtype), wl.D, tok, wl.kpool,
+                           kv_len=dev(inp["kv_len"]), q_pos=None if q_pos is None else dev(q_pos))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(tok), want), f"expansion n_q={n_q} top_k={top_k}"
+
+
+def run_kpool_chain(wl, inp):
+    """compress every complete pool -> pool scores -> top-k over pools -> tokens -> attention."""
+    L = binding()
+    packed, pooled = _compress(inp, wl)
+    rows, n_pool, kp = wl.B * wl.n_q, wl.n_kv // wl.kpool, wl.top_k // wl.kpool
+    kv_len = dev(inp["kv_len"])
+    scores = torch.empty((wl.B, wl.n_q, n_pool), dtype=torch.float32, device="cuda")
+    L.dsa_kpool_index_score(dev(inp["q"], wl.idx_dtype), pooled, dev(inp["w"]), scores, wl.kpool, kv_len=kv_len,
+                            scale=wl.scale)
+    pidx = torch.empty((wl.B, wl.n_q, kp), dtype=torch.int32, device="cuda")
+    L.dsa_topk(scores, pidx, kp)
+    width = wl.kpool * kp + wl.kpool - 1
+    tok = torch.empty((wl.B, wl.n_q, width), dtype=torch.int32, device="cuda")
+    L.dsa_kpool_expand(pidx, packed, wl.D, tok, wl.kpool, kv_len=kv_len)
+    out = torch.empty((wl.B, wl.n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((wl.B, wl.n_q, wl.Hm), dtype=torch.float32, device="cuda")
+    L.dsa_sparse_mla_attn(dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype), tok, out, wl.d_latent,
+                          wl.sm_scale, lse=lse, kv_len=kv_len)
+    torch.cuda.synchronize()
+    return host(scores), host(pidx), host(tok), host(out), host(lse)
+
+
+def _check_chain(wl, inp, res, seqs):
+    scores, pidx, tok, out, lse = res
+    kp = wl.top_k // wl.kpool
+    for b in seqs:
+        sl = slice(b, b + 1)
+        packed_b = inp["packed"][sl]
+        pooled_o = oracle.kpool_compress(packed_b, inp["ape"], wl.D, wl.kpool, wl.idx_dtype, wl.idx_dtype)
+        S = oracle.kpool_scores(inp["q"][sl], pooled_o, inp["w"][sl], inp["kv_len"][sl], None, wl.scale,
+                                wl.kpool, wl.idx_dtype, wl.idx_dtype)
+        assert_rowwise(scores[sl], S, RTOL[wl.idx_dtype], f"{wl.name} pool scores b={b}")
+        o_p = oracle.topk(S.reshape(-1, S.shape[-1]), kp).reshape(1, wl.n_q, kp)
+        check_index_rule(pidx[sl], o_p, S, f"{wl.name} pools b={b}")
+        _, _, valid = oracle.packed_fields(packed_b, wl.D, wl.idx_dtype)
+        # the GPU's tokens are the expansion of the GPU's own pools
+        S_gpu_sel = np.full_like(S, -np.inf)
+        for i in range(wl.n_q):
+            for p in pidx[b, i]:
+                if p >= 0:
+                    S_gpu_sel[0, i, p] = 1.0
+        assert np.array_equal(tok[sl], oracle.kpool_select(S_gpu_sel, valid, inp["kv_len"][sl], None, wl.top_k,
+                                                           wl.kpool)), f"{wl.name} tokens b={b}"
+        o_out, o_lse = oracle.sparse_mla(inp["qa"][sl], inp["latent"][sl], tok[sl], wl.sm_scale, wl.d_latent,
+                                         wl.mla_dtype, inp["kv_len"][sl])
+        assert_rowwise(out[sl], o_out, RTOL[wl.mla_dtype], f"{wl.name} out b={b}")
+        assert_rowwise(lse[sl], o_lse, RTOL[wl.mla_dtype], f"{wl.name} lse b={b}")
+
+
+def test_chain_small():
+    wl = KP.scaled(B=4, n_kv=3000, top_k=256)
+    inp = workloads.gen_kpool(wl, 8, hole_frac=0.05)
+    _check_chain(wl, inp, run_kpool_chain(wl, inp), range(wl.B))
+
+
+def test_chain_full_sequences():
+    """32768-token caches, top_k 2048 (512 pools, 2051 attended tokens), the decode batch of the
+    bench's pooled leg cut to 4 sequences (tails of 0..3 tokens); every sequence compared."""
+    wl = KP.scaled(B=4)
+    inp = workloads.gen_kpool(wl, 9)
+    res = run_kpool_chain(wl, inp)
+    assert res[2].shape[-1] == 2051
+    _check_chain(wl, inp, res, range(wl.B))
