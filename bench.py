@@ -129,6 +129,124 @@ def write_traffic(wl_name, fetch_csv, write_csv, copy_mib):
     print(json.dumps(out))
 
 
+def kpool_bytes(wl, width):
+    """Algorithmic bytes of one pooled-indexer decode step: pool keys, q, w, the pool scores
+    written and read, pool indices written and read, the valid entries of the selected tokens,
+    token indices written and read, the absorbed query, the selected latent rows, out, lse."""
+    rows = wl.B * wl.n_q
+    n_pool, kp = wl.n_kv // wl.kpool, wl.top_k // wl.kpool
+    isz, msz = 2, 2
+    score = wl.B * n_pool * wl.D * isz + rows * wl.H * (wl.D * isz + 4) + rows * n_pool * 4
+    topk = rows * n_pool * 4 + rows * kp * 4
+    expand = rows * kp * 4 + rows * width * (isz + 4)
+    mla = rows * width * 4 + rows * wl.Hm * wl.Dc * msz + rows * width * wl.Dc * msz + rows * wl.Hm * (wl.d_latent + 1) * 4
+    return {"index_score": score, "topk": topk, "expand": expand, "sparse_mla": mla,
+            "step": score + topk + expand + mla}
+
+
+def kpool_leg(dsa, dev, steps, warmup, seed):
+    """The pooled-indexer (kpool) decode step at the batched 32K decode shape, timed like the main
+    step: compress the cache's complete pools once (the prefill-time cost), then K steps of
+    pool scores -> top-k over pools -> expansion to tokens -> sparse MLA (no rope), replayed from
+    a graph; per-call times from HIP events in an eager pass. Inputs are drawn on the device
+    from torch's seeded generator with the distributions of workloads.gen_kpool."""
+    import torch
+    import workloads
+    wl = workloads.KPOOL_DECODE_32K
+    g = torch.Generator(device=dev).manual_seed(seed + 5)
+    B, n_kv, D, kpool = wl.B, wl.n_kv, wl.D, wl.kpool
+    n_pool, kp = n_kv // kpool, wl.top_k // kpool
+    width = kpool * kp + kpool - 1
+    kv_len = torch.tensor([n_kv - (b % kpool) for b in range(B)], dtype=torch.int32, device=dev)
+    packed = torch.empty((B, n_kv, 2 * D + 1), dtype=torch.float16, device=dev)
+    packed[:, :, :D] = torch.randn((B, n_kv, D), generator=g, device=dev) / D ** 0.5
+    packed[:, :, D:2 * D] = torch.randn((B, n_kv, D), generator=g, device=dev)
+    packed[:, :, 2 * D] = (torch.arange(n_kv, device=dev)[None] < kv_len[:, None].long()).half()
+    ape = torch.randn((kpool, D), generator=g, device=dev)
+    q = (torch.randn((B, 1, wl.H, D), generator=g, device=dev) / D ** 0.5).half()
+    w = torch.rand((B, 1, wl.H), generator=g, device=dev) * wl.w_scale
+    qa = torch.randn((B, 1, wl.Hm, wl.Dc), generator=g, device=dev).bfloat16()
+    lat = (torch.randn((B, n_kv, wl.Dc), generator=g, device=dev) * wl.latent_std).bfloat16()
+    pooled = torch.empty((B, n_pool, D), dtype=torch.float16, device=dev)
+    scores = torch.empty((B, 1, n_pool), dtype=torch.float32, device=dev)
+    pidx = torch.empty((B, 1, kp), dtype=torch.int32, device=dev)
+    tok = torch.empty((B, 1, width), dtype=torch.int32, device=dev)
+    out = torch.empty((B, 1, wl.Hm, wl.d_latent), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, 1, wl.Hm), dtype=torch.float32, device=dev)
+    ns = dsa.dsa_sparse_mla_num_splits(B, 1, width)
+    ws_t = torch.empty(max(1, dsa.dsa_topk_workspace_size(B, n_pool, kp)), dtype=torch.uint8, device=dev)
+    ws_m = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(B, 1, wl.Hm, width, wl.d_latent, ns)),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def compress_all():
+        dsa.dsa_kpool_compress(packed, ape, pooled, D, kpool)
+
+    calls = {
+        "index_score": lambda: dsa.dsa_kpool_index_score(q, pooled, w, scores, kpool, kv_len=kv_len, scale=wl.scale),
+        "topk": lambda: dsa.dsa_topk(scores, pidx, kp, workspace=ws_t),
+        "expand": lambda: dsa.dsa_kpool_expand(pidx, packed, D, tok, kpool, kv_len=kv_len),
+        "sparse_mla": lambda: dsa.dsa_sparse_mla_attn(qa, lat, tok, out, wl.d_latent, wl.sm_scale, lse=lse,
+                                                      kv_len=kv_len, n_split=ns, workspace=ws_m),
+    }
+
+    def kstep():
+        for f in calls.values():
+            f()
+
+    for _ in range(3):
+        compress_all()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        compress_all()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    compress_ms = e0.elapsed_time(e1) / 10
+    compress_b = B * n_kv * (2 * D + 1) * 2 + B * n_pool * D * 2 + kpool * D * 4
+    for _ in range(max(1, warmup)):
+        kstep()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for s_ in range(steps):
+        ev[s_][0].record(stream)
+        for j, f in enumerate(calls.values()):
+            f()
+            ev[s_][j + 1].record(stream)
+    torch.cuda.synchronize()
+    per = {name: sum(ev[s_][j].elapsed_time(ev[s_][j + 1]) for s_ in range(steps)) / steps
+           for j, name in enumerate(calls)}
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        kstep()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kstep()
+    for _ in range(max(1, warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    ab = kpool_bytes(wl, width)
+    return {"workload": wl.name, "B": B, "n_kv": n_kv, "kpool": kpool, "top_k_tokens": wl.top_k,
+            "pools_selected": kp, "attended_width": width, "d_rope": wl.d_rope, "indexer_dtype": "f16",
+            "ms_per_step": round(step_s * 1e3, 4), "tokens_per_s": round(B / step_s, 1),
+            "step_algorithmic_bytes": ab["step"], "step_hbm_gbs": round(ab["step"] / step_s / 1e9, 1),
+            "step_hbm_frac": round(ab["step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
+            "kernels_gbs": {k_: round(ab[k_] / (per[k_] * 1e-3) / 1e9, 1) for k_ in per},
+            "compress_all_pools": {"ms": round(compress_ms, 4), "bytes": compress_b,
+                                   "gbs": round(compress_b / (compress_ms * 1e-3) / 1e9, 1),
+                                   "frac": round(compress_b / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(wl, inp, seconds_target=15.0):
     """The oracle chain on whole sequences of the workload until ~seconds_target of work."""
     import numpy as np
@@ -174,6 +292,8 @@ def main():
                     help="run the step as this many chains over equal slices of the batch, each on its "
                          "own stream, so one slice's latency-bound stages overlap another's streaming")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kpool", action="store_true",
+                    help="skip the pooled-indexer (kpool) decode leg of the bench line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--scrub-mib", type=int, default=0,
                     help="also time eager steps with a buffer of this many MiB written between them "
@@ -395,6 +515,10 @@ def main():
     torch.cuda.synchronize()
     prep_ms = pe0.elapsed_time(pe1) / (reps * 20)
 
+    kpool = None
+    if not args.no_kpool and wl.n_q == 1:
+        kpool = kpool_leg(dsa, dev, args.steps, args.warmup, args.seed)
+
     # a plain device-to-device copy of 1 GiB: the bandwidth a streaming kernel reaches here
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     cdst = torch.empty_like(csrc)
@@ -483,6 +607,8 @@ def main():
                    "~0.3-0.4 tokens/s and 200-token prefill ~3.2 tokens/s on an RTX 4060 Ti 16GB with SSD "
                    "expert streaming",
     }
+    if kpool is not None:
+        result["kpool"] = kpool
     if scrub is not None:
         result["cold_cache_eager"] = scrub
     if not args.no_cpu_baseline:
