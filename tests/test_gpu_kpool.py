@@ -80,18 +80,27 @@ def test_compress(row_dtype, out_dtype):
 
 def test_compress_range_and_pool_sizes():
     L = binding()
-    for kpool in (1, 2, 3, 8):
-        wl = KP.scaled(B=2, n_kv=203, D=64, kpool=kpool)
+    # odd and even pool counts and row strides, every pool size
+    for n_kv, kpool in ((203, 1), (203, 2), (203, 3), (203, 8), (204, 2), (204, 4), (204, 8), (204, 3)):
+        wl = KP.scaled(B=2, n_kv=n_kv, D=64, kpool=kpool)
         inp = workloads.gen_kpool(wl, 2, hole_frac=0.3)
         n_pool = wl.n_kv // kpool
         p0, p1 = n_pool // 3, n_pool - 1
         _, pooled = _compress(inp, wl, p0=p0, p1=p1, fill=7.0)
         torch.cuda.synchronize()
         x64 = oracle.kpool_compress_f64(inp["packed"], inp["ape"], wl.D, kpool, wl.idx_dtype)
-        _check_pool_keys(pooled[:, p0:p1].contiguous(), x64[:, p0:p1], wl.idx_dtype, f"kpool {kpool} range",
+        _check_pool_keys(pooled[:, p0:p1].contiguous(), x64[:, p0:p1], wl.idx_dtype, f"n_kv {n_kv} kpool {kpool} range",
                          _term_scale(inp["packed"], wl.D, kpool, wl.idx_dtype, slice(p0, p1)))
         rest = torch.cat([pooled[:, :p0], pooled[:, p1:]], dim=1)
-        assert bool((rest == 7.0).all()), f"kpool {kpool}: pools outside the range were written"
+        assert bool((rest == 7.0).all()), f"n_kv {n_kv} kpool {kpool}: pools outside the range were written"
+    # wide rows (D 1024 and 4096)
+    for D in (1024, 4096):
+        wl = KP.scaled(B=1, n_kv=24, D=D)
+        inp = workloads.gen_kpool(wl, 10, hole_frac=0.2)
+        _, pooled = _compress(inp, wl)
+        torch.cuda.synchronize()
+        _check_pool_keys(pooled, oracle.kpool_compress_f64(inp["packed"], inp["ape"], D, 4, wl.idx_dtype),
+                         wl.idx_dtype, f"D {D}", _term_scale(inp["packed"], D, 4, wl.idx_dtype))
     # a packed row wider than 2 D + 1 (padded stride)
     wl = KP.scaled(B=2, n_kv=64, D=16)
     inp = workloads.gen_kpool(wl, 3, hole_frac=0.2)
