@@ -283,7 +283,7 @@ __device__ __forceinline__ int frag_slot(int pq, int ht, int n_ht, int dt, int c
   return (((pq * n_ht + ht) * 4 + dt) * 4 + c) * 64 + lane;
 }
 
-template <int DR>
+template <int DR, int NHT>
 __global__ __launch_bounds__(512) void sparse_mla_mfma(
     const bf16_t* __restrict__ qa, const bf16_t* __restrict__ lat, const int* __restrict__ idx,
     const int* __restrict__ kv_len, float* __restrict__ out, float* __restrict__ lse,
@@ -339,13 +339,16 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
 #pragma unroll
     for (int s = 0; s < KSW; ++s) qreg[s] = *reinterpret_cast<const i32x4*>(qp + (4 * s + g) * 16);
   }
-  const int n_ht = (Hm + 31) / 32;
+  constexpr int n_ht = NHT;  // 32-head tiles: (Hm + 31) / 32
   wait_vmcnt<0>();  // query registers ready before the first DMA, so later waits count DMAs only
   __syncthreads();
 
   const uint8_t* latb = reinterpret_cast<const uint8_t*>(lat) + (long)b * n_kv * ROWB;
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_zero_row);
-  const int my_blocks = wave < (NBLK % 8 == 0 ? 8 : NBLK % 8) ? DmaShare<NBLK>::hi : DmaShare<NBLK>::lo;
+  asm volatile("" : "+s"(zero));  // kept in scalar registers, not rebuilt from the symbol per DMA
+  // the DMA share and wait counts of this wave, known uniform (scalar branches, no exec masks)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int my_blocks = wave_u < (NBLK % 8 == 0 ? 8 : NBLK % 8) ? DmaShare<NBLK>::hi : DmaShare<NBLK>::lo;
   // per-lane DMA constants: block j of this wave fills LDS slots (j*8 + wave)*64 + lane, which
   // hold chunk dma_c[j] of tile row dma_r[j]
   int dma_r[NJ], dma_c[NJ];
@@ -363,16 +366,20 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int ts = tile * kTileRows + dma_r[j];
-      rows[j] = (j * 8 + wave < NBLK && ts < nslots) ? s_idx[ts] : -1;
+      rows[j] = ((j < NBLK / 8 || j * 8 + wave_u < NBLK) && ts < nslots) ? s_idx[ts] : -1;
     }
   };
-  auto issue = [&](int tile, const int (&rows)[NJ]) {
-    uint8_t* stage = s_ring + (tile % kNst) * TILE_BYTES;
+  // ring stage st = tile % kNst, kept by the callers as a counter (no division per step)
+  auto issue = [&](int st, const int (&rows)[NJ]) {
+    uint8_t* stage = s_ring + st * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int blk = j * 8 + wave;
-      if (blk < NBLK) {
-        const uint8_t* src = (rows[j] >= 0 ? latb + (long)rows[j] * ROWB : zero) + dma_c[j];
+      const int blk = j * 8 + wave_u;
+      if (j < NBLK / 8 || blk < NBLK) {  // the first NBLK / 8 blocks belong to every wave
+        // a select, not a branch: padding slots read the zero row
+        const uintptr_t real = reinterpret_cast<uintptr_t>(latb) + (uintptr_t)((long)max(rows[j], 0) * ROWB);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(
+            (rows[j] >= 0 ? real : reinterpret_cast<uintptr_t>(zero)) + dma_c[j]);
         __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + blk * 1024), 16, 0, 0);
       }
     }
@@ -401,7 +408,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   for (int p = 0; p < kNst - 2; ++p)
     if (p < ntiles) {
       tile_rows(p, next_rows);
-      issue(p, next_rows);
+      issue(p, next_rows);  // stage p
     }
   tile_rows(kNst - 2, next_rows);
 
@@ -430,23 +437,43 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   // One step: wait for this wave's DMA of the score tile, barrier, refill the freed stage.
   // Both kinds of wave run the same steps (and barriers) in loops of their own, so each
   // keeps only its own state in registers.
-  auto step = [&](int it) {
+  // su = stage of tile it + 1; tile it + kNst - 1 goes to stage (su + kNst - 2) % kNst.
+  // Steady steps (0 <= it <= ntiles - kNst: the score tile has kNst - 3 later tiles in flight and
+  // a tile is issued) are compiled apart from the others, without the bounds tests and the
+  // case analysis of the wait count, which cost the waves scalar instructions on every step.
+  auto step = [&](int it, int su, auto steady) {
+    constexpr bool S = decltype(steady)::value;
     const int u = it + 1;  // score tile of this step
-    if (u < ntiles) wait_tiles(min(kNst - 3, ntiles - 1 - u));
+    if constexpr (S) {
+      if (my_blocks == DmaShare<NBLK>::hi) wait_vmcnt<(kNst - 3) * DmaShare<NBLK>::hi>();
+      else wait_vmcnt<(kNst - 3) * DmaShare<NBLK>::lo>();
+    } else {
+      if (u < ntiles) wait_tiles(min(kNst - 3, ntiles - 1 - u));
+    }
     lds_barrier();
-    if (it + kNst - 1 < ntiles) issue(it + kNst - 1, next_rows);
+    if (S || it + kNst - 1 < ntiles) issue(su >= 2 ? su - 2 : su + kNst - 2, next_rows);
     tile_rows(it + kNst, next_rows);
+  };
+  // it = -1, then the steady steps, then the rest, with su = (it + 1) % kNst
+  auto run_steps = [&](auto&& body) {
+    int it = -1, su = 0;
+    body(it, su, std::false_type());
+    for (++it, su = 1; it <= ntiles - kNst; ++it, su = su + 1 == kNst ? 0 : su + 1) body(it, su, std::true_type());
+    for (; it < ntiles; ++it, su = su + 1 == kNst ? 0 : su + 1) body(it, su, std::false_type());
   };
 
   if (score_wave) {
     float m_run = -INFINITY, l_run = 0.f;
     constexpr int KH = KSW / 2;
-    auto score_step = [&](int it) {
-      step(it);
+    // the same test as `scores`, in a form the compiler sees as uniform (scalar branch)
+    const bool scores_u = wave_u * 16 < Hm;
+    auto score_step = [&](int it, int su, auto steady) {
+      constexpr bool S = decltype(steady)::value;
+      step(it, su, steady);
       const int u = it + 1;
-      if (scores && u < ntiles) {
+      if (scores_u && (S || u < ntiles)) {
         const int buf = u & 1;
-        const uint32_t bufa = lds_addr(s_ring + (u % kNst) * TILE_BYTES);
+        const uint32_t bufa = lds_addr(s_ring + su * TILE_BYTES);
         int sv = -1;
         if (lane < kTileRows) {
           const int ts = u * kTileRows + lane;
@@ -521,7 +548,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
         s_flag[u & 1][hg] = 0u;
       }
     };
-    for (int it = -1; it < ntiles; ++it) score_step(it);
+    run_steps(score_step);
     // final statistics of each head
     if (scores) {
       l_run += shfl_xor(l_run, 16);
@@ -546,8 +573,8 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     // for the score waves) into the registers the step's products have just consumed, so a
     // step only waits for its probabilities.
     i16x4 va[4][2];
-    auto read_v = [&](int tile) {
-      const uint32_t bufa = lds_addr(s_ring + (tile % kNst) * TILE_BYTES);
+    auto read_v = [&](int st) {
+      const uint32_t bufa = lds_addr(s_ring + st * TILE_BYTES);
       static_for<0, 4>([&](auto DT) {
         constexpr int dt = decltype(DT)::value;
         va[dt][0] = ds_read_tr16_off<0>(bufa + tr_off[dt][0]);
@@ -555,9 +582,10 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
       });
     };
     const uint32_t p_off = ((lane & 31) * kTileRows + 8 * (lane >> 5)) * 2;
-    for (int it = -1; it < ntiles; ++it) {
-      step(it);  // its lgkmcnt(0) wait completes the reads into va
-      if (it >= 0) {
+    auto value_step = [&](int it, int su, auto steady) {
+      constexpr bool S = decltype(steady)::value;
+      step(it, su, steady);  // its lgkmcnt(0) wait completes the reads into va
+      if (S || it >= 0) {
         const int buf = it & 1;
         const uint4 fl = *reinterpret_cast<const uint4*>(s_flag[buf]);
         if ((fl.x | fl.y | fl.z | fl.w) != 0u) {  // uniform: some head group moved its reference
@@ -596,8 +624,9 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
             for (int ht = 0; ht < 2; ++ht)
               if (ht < n_ht) o[dt][ht] = mma32_bf16(av[dt], pb[2 * ht + hl], o[dt][ht]);
       }
-      if (it + 1 < ntiles) read_v(it + 1);
-    }
+      if (S || it + 1 < ntiles) read_v(su);  // tile it + 1
+    };
+    run_steps(value_step);
     __syncthreads();  // the score waves' statistics are in s_ml
     // lane holds O^T[32 dt + 8 (i / 4) + 4 (l / 32) + i % 4][32 ht + l % 32], i < 16
 #pragma unroll
@@ -807,14 +836,10 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
   }
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
     const unsigned blocks = (unsigned)(rows * n_split);
-    if (d_rope == 64)
-      hipLaunchKernelGGL(sparse_mla_mfma<64>, dim3(blocks), dim3(512), 0, stream, (const bf16_t*)q_abs,
-                         (const bf16_t*)latent, idx, kv_len, out, lse, ws_o, ws_ml, n_q, Hm, n_kv,
-                         top_k, sm_scale, n_split, chunk);
-    else
-      hipLaunchKernelGGL(sparse_mla_mfma<0>, dim3(blocks), dim3(512), 0, stream, (const bf16_t*)q_abs,
-                         (const bf16_t*)latent, idx, kv_len, out, lse, ws_o, ws_ml, n_q, Hm, n_kv,
-                         top_k, sm_scale, n_split, chunk);
+    auto kernel = d_rope == 64 ? (Hm > 32 ? sparse_mla_mfma<64, 2> : sparse_mla_mfma<64, 1>)
+                               : (Hm > 32 ? sparse_mla_mfma<0, 2> : sparse_mla_mfma<0, 1>);
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(512), 0, stream, (const bf16_t*)q_abs, (const bf16_t*)latent,
+                       idx, kv_len, out, lse, ws_o, ws_ml, n_q, Hm, n_kv, top_k, sm_scale, n_split, chunk);
   } else {
     const int Dc = d_latent + d_rope;
     dim3 grid(n_split, (unsigned)rows, (Hm + kPlainHeads - 1) / kPlainHeads);
