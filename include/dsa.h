@@ -201,7 +201,9 @@ int dsa_topk_source_layer(int layer);
  * each wave of the 16-bit decode scoring kernel walks (0 = automatic, else 1..64, taken
  * down to 1, 2, 4 or 8). key "score_prefill_waves": waves per workgroup of the 16-bit
  * scoring kernel for 8 or more queries per sequence, each wave taking 2 queries (0 =
- * automatic, else 4 or 8). Returns DSA_OK,
+ * automatic, else 4 or 8). key "mla_tiles_per_step": 16-row tiles of selected latent rows
+ * that the 16-bit sparse MLA kernel takes between two workgroup barriers (2 = default, or 1;
+ * both give results within the same tolerance, with a different summation order). Returns DSA_OK,
  * or DSA_ERR_SHAPE for an unknown key or value. Process-wide; set it before launching work.
  */
 int dsa_set_tuning(const char* key, int value);

@@ -89,6 +89,12 @@ int dsa_set_tuning(const char* key, int value) {
     dsa::g_score_prefill_waves = value;
     return ok();
   }
+  if (std::strcmp(key, "mla_tiles_per_step") == 0) {
+    if (value != 1 && value != 2)
+      return fail(DSA_ERR_SHAPE, "mla_tiles_per_step must be 1 or 2 (got %d)", value);
+    dsa::g_mla_tiles_per_step = value;
+    return ok();
+  }
   return fail(DSA_ERR_SHAPE, "dsa_set_tuning: unknown key '%s'", key);
 }
 

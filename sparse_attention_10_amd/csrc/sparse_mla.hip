@@ -283,7 +283,7 @@ __device__ __forceinline__ int frag_slot(int pq, int ht, int n_ht, int dt, int c
   return (((pq * n_ht + ht) * 4 + dt) * 4 + c) * 64 + lane;
 }
 
-template <int DR, int NHT>
+template <int DR, int NHT, int TPS>
 __global__ __launch_bounds__(512) void sparse_mla_mfma(
     const bf16_t* __restrict__ qa, const bf16_t* __restrict__ lat, const int* __restrict__ idx,
     const int* __restrict__ kv_len, float* __restrict__ out, float* __restrict__ lse,
@@ -299,11 +299,14 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   constexpr int SB = KSW % 3 == 0 ? 3 : 2;      // score k-steps per LDS batch
   constexpr int NJ = DmaShare<NBLK>::hi;
   static_assert(kTileRows * CPR % 64 == 0 && KSW % SB == 0, "tile shape");
+  constexpr int SR = kTileRows * TPS;           // rows per step
+  constexpr int MAXA = kNst - 3 * TPS;          // later tiles in flight when a step's tiles are due
+  static_assert(MAXA >= 1 && MAXA <= 4, "ring depth");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kNst * TILE_BYTES];
   __shared__ int s_idx[kMlaMaxChunk];
-  // probabilities of one tile: [buffer][hi, lo][head][row], bf16 bits
-  __shared__ __attribute__((aligned(16))) uint16_t s_p[2][2][64 * kTileRows];
+  // probabilities of one step's rows: [buffer][hi, lo][head][row], bf16 bits
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[2][2][64 * SR];
   __shared__ __attribute__((aligned(16))) float s_alpha[2][64];   // rescale factor per head
   __shared__ __attribute__((aligned(16))) uint32_t s_flag[2][4];  // score wave rescaled
   __shared__ float s_ml[2][64];                                   // final m, l per head
@@ -359,7 +362,9 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     dma_r[j] = r;
     dma_c[j] = ((slot - r * CPR) ^ (r & 7)) * 16;
   }
-  const int ntiles = (nslots + kTileRows - 1) / kTileRows;
+  // steps take TPS tiles; the last step's tiles past the slots are padding (zero rows, p = 0)
+  const int nsteps = (nslots + SR - 1) / SR;
+  const int ntiles = nsteps * TPS;
   // The cache rows of a tile's DMA slots are read from s_idx one step before the tile is
   // issued, so the DMA issue itself never waits for LDS.
   auto tile_rows = [&](int tile, int (&rows)[NJ]) {
@@ -384,33 +389,36 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
       }
     }
   };
-  // waits: at most `ahead` later tiles of this wave's DMA may still be in flight
+  // waits: at most `ahead` (<= MAXA) later tiles of this wave's DMA may still be in flight
   auto wait_tiles = [&](int ahead) {
-    static_assert(kNst - 3 == 4, "wait cases");
     if (my_blocks == DmaShare<NBLK>::hi) {
       constexpr int h = DmaShare<NBLK>::hi;
-      if (ahead >= 4) wait_vmcnt<4 * h>();
-      else if (ahead == 3) wait_vmcnt<3 * h>();
-      else if (ahead == 2) wait_vmcnt<2 * h>();
-      else if (ahead == 1) wait_vmcnt<h>();
+      if (ahead >= 4 && MAXA >= 4) wait_vmcnt<4 * h>();
+      else if (ahead >= 3 && MAXA >= 3) wait_vmcnt<3 * h>();
+      else if (ahead >= 2 && MAXA >= 2) wait_vmcnt<2 * h>();
+      else if (ahead >= 1) wait_vmcnt<h>();
       else wait_vmcnt<0>();
     } else {
       constexpr int l = DmaShare<NBLK>::lo;
-      if (ahead >= 4) wait_vmcnt<4 * l>();
-      else if (ahead == 3) wait_vmcnt<3 * l>();
-      else if (ahead == 2) wait_vmcnt<2 * l>();
-      else if (ahead == 1) wait_vmcnt<l>();
+      if (ahead >= 4 && MAXA >= 4) wait_vmcnt<4 * l>();
+      else if (ahead >= 3 && MAXA >= 3) wait_vmcnt<3 * l>();
+      else if (ahead >= 2 && MAXA >= 2) wait_vmcnt<2 * l>();
+      else if (ahead >= 1) wait_vmcnt<l>();
       else wait_vmcnt<0>();
     }
   };
   __syncthreads();  // s_idx and the zeroed probabilities are visible
-  int next_rows[NJ];
-  for (int p = 0; p < kNst - 2; ++p)
+  // Tile t goes to stage t % kNst. Before the first step tiles [0, kNst - 2 TPS) are issued;
+  // step it then issues tiles TPS (it - 1) + kNst + h (h < TPS) into the stages of step it - 1's
+  // tiles, which both kinds of wave are done with once step it's barrier has passed.
+  int next_rows[TPS][NJ];
+  for (int p = 0; p < kNst - 2 * TPS; ++p)
     if (p < ntiles) {
-      tile_rows(p, next_rows);
-      issue(p, next_rows);  // stage p
+      tile_rows(p, next_rows[0]);
+      issue(p, next_rows[0]);  // stage p
     }
-  tile_rows(kNst - 2, next_rows);
+#pragma unroll
+  for (int h = 0; h < TPS; ++h) tile_rows(kNst - 2 * TPS + h, next_rows[h]);
 
   // Score reads: row r16, chunk 4 s + g stored at (4 s + g) ^ (r16 & 7); for k-steps of one
   // parity the offset grows by 128 bytes per two steps, so two bases cover all steps.
@@ -434,32 +442,40 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
       }
   }
 
-  // One step: wait for this wave's DMA of the score tile, barrier, refill the freed stage.
-  // Both kinds of wave run the same steps (and barriers) in loops of their own, so each
-  // keeps only its own state in registers.
-  // su = stage of tile it + 1; tile it + kNst - 1 goes to stage (su + kNst - 2) % kNst.
-  // Steady steps (0 <= it <= ntiles - kNst: the score tile has kNst - 3 later tiles in flight and
-  // a tile is issued) are compiled apart from the others, without the bounds tests and the
+  // One step: wait for this wave's DMA of the score tiles, barrier, refill the freed stages.
+  // In step it the score waves take the tiles of step u = it + 1, the value waves those of
+  // step it. Both kinds of wave run the same steps (and barriers) in loops of their own, so
+  // each keeps only its own state in registers. su = stage of tile TPS (it + 1).
+  // Steady steps (0 <= it, TPS it <= ntiles - kNst: MAXA later tiles are in flight and all TPS
+  // tiles are issued) are compiled apart from the others, without the bounds tests and the
   // case analysis of the wait count, which cost the waves scalar instructions on every step.
+  auto stage_add = [](int st, int d) {  // (st + d) mod kNst for -kNst <= d < kNst
+    st += d;
+    return st < 0 ? st + kNst : (st >= kNst ? st - kNst : st);
+  };
   auto step = [&](int it, int su, auto steady) {
     constexpr bool S = decltype(steady)::value;
-    const int u = it + 1;  // score tile of this step
+    const int u = it + 1;  // score step
     if constexpr (S) {
-      if (my_blocks == DmaShare<NBLK>::hi) wait_vmcnt<(kNst - 3) * DmaShare<NBLK>::hi>();
-      else wait_vmcnt<(kNst - 3) * DmaShare<NBLK>::lo>();
+      if (my_blocks == DmaShare<NBLK>::hi) wait_vmcnt<MAXA * DmaShare<NBLK>::hi>();
+      else wait_vmcnt<MAXA * DmaShare<NBLK>::lo>();
     } else {
-      if (u < ntiles) wait_tiles(min(kNst - 3, ntiles - 1 - u));
+      // issued so far: tiles < min(TPS (it - 1) + kNst, ntiles); due: tiles < TPS (u + 1)
+      if (u < nsteps) wait_tiles(max(0, min(TPS * (it - 1) + kNst, ntiles) - TPS * (u + 1)));
     }
     lds_barrier();
-    if (S || it + kNst - 1 < ntiles) issue(su >= 2 ? su - 2 : su + kNst - 2, next_rows);
-    tile_rows(it + kNst, next_rows);
+#pragma unroll
+    for (int h = 0; h < TPS; ++h)
+      if (S || TPS * (it - 1) + kNst + h < ntiles) issue(stage_add(su, h - 2 * TPS), next_rows[h]);
+#pragma unroll
+    for (int h = 0; h < TPS; ++h) tile_rows(TPS * it + kNst + h, next_rows[h]);
   };
-  // it = -1, then the steady steps, then the rest, with su = (it + 1) % kNst
+  // it = -1, then the steady steps, then the rest, with su = TPS (it + 1) % kNst
   auto run_steps = [&](auto&& body) {
     int it = -1, su = 0;
     body(it, su, std::false_type());
-    for (++it, su = 1; it <= ntiles - kNst; ++it, su = su + 1 == kNst ? 0 : su + 1) body(it, su, std::true_type());
-    for (; it < ntiles; ++it, su = su + 1 == kNst ? 0 : su + 1) body(it, su, std::false_type());
+    for (++it, su = TPS; TPS * it <= ntiles - kNst; ++it, su = stage_add(su, TPS)) body(it, su, std::true_type());
+    for (; it < nsteps; ++it, su = stage_add(su, TPS)) body(it, su, std::false_type());
   };
 
   if (score_wave) {
@@ -471,44 +487,47 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
       constexpr bool S = decltype(steady)::value;
       step(it, su, steady);
       const int u = it + 1;
-      if (scores_u && (S || u < ntiles)) {
+      if (scores_u && (S || u < nsteps)) {
         const int buf = u & 1;
-        const uint32_t bufa = lds_addr(s_ring + su * TILE_BYTES);
         int sv = -1;
-        if (lane < kTileRows) {
-          const int ts = u * kTileRows + lane;
+        if (lane < SR) {
+          const int ts = u * SR + lane;
           sv = ts < nslots ? s_idx[ts] : -1;
         }
-        const uint32_t vbits = (uint32_t)__ballot(sv >= 0);
-        // S^T tile: rows 4 g + e, head r16. The k-step reads go out in two halves; the first
-        // half's products run while the second half is in flight, and the k-steps feed three
-        // accumulators in turn so consecutive MFMAs do not wait on each other.
-        const uint32_t sb0 = bufa + sc_off0, sb1 = bufa + sc_off1;
-        i32x4 ka[KH], kb[KH];
-        static_for<0, KH>([&](auto S) {
-          constexpr int st = decltype(S)::value;
-          ka[st] = ds_read_b128_off<128 * (st >> 1)>((st & 1) ? sb1 : sb0);
-        });
-        static_for<0, KH>([&](auto S) {
-          constexpr int st = KH + decltype(S)::value;
-          kb[st - KH] = ds_read_b128_off<128 * (st >> 1)>((st & 1) ? sb1 : sb0);
-        });
-        lds_wait_first<KH>(ka);
-        f32x4 sacc[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        static_for<0, KH>([&](auto S) {
-          constexpr int st = decltype(S)::value;
-          sacc[st % 3] = mma_bf16(ka[st], qreg[st], sacc[st % 3]);
-        });
-        lds_wait_all<KH>(kb);
-        static_for<0, KH>([&](auto S) {
-          constexpr int st = KH + decltype(S)::value;
-          sacc[st % 3] = mma_bf16(kb[st - KH], qreg[st], sacc[st % 3]);
-        });
-        const uint32_t vr = vbits >> (4 * g);
-        float z[4];
+        const uint64_t vbits = __ballot(sv >= 0);
+        float z[TPS][4];
+        static_for<0, TPS>([&](auto H) {
+          constexpr int h = decltype(H)::value;
+          const uint32_t bufa = lds_addr(s_ring + stage_add(su, h) * TILE_BYTES);
+          // S^T tile h: rows 4 g + e, head r16. The k-step reads go out in two halves; the first
+          // half's products run while the second half is in flight, and the k-steps feed three
+          // accumulators in turn so consecutive MFMAs do not wait on each other.
+          const uint32_t sb0 = bufa + sc_off0, sb1 = bufa + sc_off1;
+          i32x4 ka[KH], kb[KH];
+          static_for<0, KH>([&](auto K) {
+            constexpr int st = decltype(K)::value;
+            ka[st] = ds_read_b128_off<128 * (st >> 1)>((st & 1) ? sb1 : sb0);
+          });
+          static_for<0, KH>([&](auto K) {
+            constexpr int st = KH + decltype(K)::value;
+            kb[st - KH] = ds_read_b128_off<128 * (st >> 1)>((st & 1) ? sb1 : sb0);
+          });
+          lds_wait_first<KH>(ka);
+          f32x4 sacc[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+          static_for<0, KH>([&](auto K) {
+            constexpr int st = decltype(K)::value;
+            sacc[st % 3] = mma_bf16(ka[st], qreg[st], sacc[st % 3]);
+          });
+          lds_wait_all<KH>(kb);
+          static_for<0, KH>([&](auto K) {
+            constexpr int st = KH + decltype(K)::value;
+            sacc[st % 3] = mma_bf16(kb[st - KH], qreg[st], sacc[st % 3]);
+          });
+          const uint32_t vr = (uint32_t)(vbits >> (kTileRows * h + 4 * g));
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          z[e] = (vr >> e) & 1u ? ((sacc[0][e] + sacc[1][e]) + sacc[2][e]) * sm_scale : -INFINITY;
+          for (int e = 0; e < 4; ++e)
+            z[h][e] = (vr >> e) & 1u ? ((sacc[0][e] + sacc[1][e]) + sacc[2][e]) * sm_scale : -INFINITY;
+        });
         // m_run is a reference max, not the exact running max: weights are exp(z - m_run) and
         // O, l are kept relative to it. It moves (and O, l are rescaled by alpha) only when a
         // score exceeds it by more than kLazyRescale, so weights stay below e^kLazyRescale
@@ -516,7 +535,9 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
         // path needs no cross-lane reduction. m_run is equal in the four lanes of a head; each
         // lane sums the weights of its own rows (l_run) and the lanes are added at the end.
         // O / l and m_run + log(l) do not depend on the reference.
-        const float zl = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        float zl = fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3]));
+#pragma unroll
+        for (int h = 1; h < TPS; ++h) zl = fmaxf(zl, fmaxf(fmaxf(z[h][0], z[h][1]), fmaxf(z[h][2], z[h][3])));
         float alpha = 1.f;
         const bool rescale = __ballot(zl > m_run + kLazyRescale) != 0;
         if (rescale) {
@@ -527,24 +548,27 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
           l_run *= alpha;
           m_run = m_new;
         }
-        float pr[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pr[e] = z[e] == -INFINITY ? 0.f : __expf(z[e] - m_run);
-        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         // p = hi + lo with both parts bf16 (round to nearest even): the value product runs
         // once per part, so the weights keep about 16 significant bits.
         typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-        bf16x4 hi4, lo4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hi4[e] = (__bf16)pr[e];
+        for (int h = 0; h < TPS; ++h) {
+          float pr[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lo4[e] = (__bf16)(pr[e] - (float)hi4[e]);
-        const int po = head * kTileRows + 4 * g;
-        *reinterpret_cast<bf16x4*>(&s_p[buf][0][po]) = hi4;
-        *reinterpret_cast<bf16x4*>(&s_p[buf][1][po]) = lo4;
+          for (int e = 0; e < 4; ++e) pr[e] = z[h][e] == -INFINITY ? 0.f : __expf(z[h][e] - m_run);
+          l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+          bf16x4 hi4, lo4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hi4[e] = (__bf16)pr[e];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lo4[e] = (__bf16)(pr[e] - (float)hi4[e]);
+          const int po = head * SR + kTileRows * h + 4 * g;
+          *reinterpret_cast<bf16x4*>(&s_p[buf][0][po]) = hi4;
+          *reinterpret_cast<bf16x4*>(&s_p[buf][1][po]) = lo4;
+        }
         if (lane < 16) s_alpha[buf][head] = alpha;
         if (lane == 0) s_flag[buf][hg] = rescale ? 1u : 0u;
-      } else if (u < ntiles && lane == 0) {
+      } else if (u < nsteps && lane == 0) {
         s_flag[u & 1][hg] = 0u;
       }
     };
@@ -569,19 +593,22 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
       for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][ht][e] = 0.f;
-    // The value operands of tile it + 1 are read at the end of step it (that tile is in LDS
+    // The value operands of step it + 1 are read at the end of step it (its tiles are in LDS
     // for the score waves) into the registers the step's products have just consumed, so a
-    // step only waits for its probabilities.
-    i16x4 va[4][2];
-    auto read_v = [&](int st) {
-      const uint32_t bufa = lds_addr(s_ring + st * TILE_BYTES);
-      static_for<0, 4>([&](auto DT) {
-        constexpr int dt = decltype(DT)::value;
-        va[dt][0] = ds_read_tr16_off<0>(bufa + tr_off[dt][0]);
-        va[dt][1] = ds_read_tr16_off<0>(bufa + tr_off[dt][1]);
+    // step only waits for its probabilities. su = stage of the step's first tile.
+    i16x4 va[TPS][4][2];
+    auto read_v = [&](int su) {
+      static_for<0, TPS>([&](auto H) {
+        constexpr int h = decltype(H)::value;
+        const uint32_t bufa = lds_addr(s_ring + stage_add(su, h) * TILE_BYTES);
+        static_for<0, 4>([&](auto DT) {
+          constexpr int dt = decltype(DT)::value;
+          va[h][dt][0] = ds_read_tr16_off<0>(bufa + tr_off[dt][0]);
+          va[h][dt][1] = ds_read_tr16_off<0>(bufa + tr_off[dt][1]);
+        });
       });
     };
-    const uint32_t p_off = ((lane & 31) * kTileRows + 8 * (lane >> 5)) * 2;
+    const uint32_t p_off = ((lane & 31) * SR + 8 * (lane >> 5)) * 2;
     auto value_step = [&](int it, int su, auto steady) {
       constexpr bool S = decltype(steady)::value;
       step(it, su, steady);  // its lgkmcnt(0) wait completes the reads into va
@@ -598,33 +625,39 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
               for (int e = 0; e < 16; ++e) o[dt][ht][e] *= a;
           }
         }
-        // B operands: P^T [16 rows][32 heads], lane holds head 32 ht + l % 32, rows 8 (l / 32) ..
+        // B operands: P^T [16 rows of tile h][32 heads], lane holds head 32 ht + l % 32, rows
+        // 16 h + 8 (l / 32) ..
         const uint32_t pbase = lds_addr(&s_p[buf][0][0]) + p_off;
-        constexpr int PHL = 64 * kTileRows * 2;  // bytes between the hi and lo parts
-        constexpr int PHT = 32 * kTileRows * 2;  // bytes between the two head tiles
-        i32x4 pb[4];
-        pb[0] = ds_read_b128_off<0>(pbase);
-        pb[1] = ds_read_b128_off<PHL>(pbase);
-        pb[2] = ds_read_b128_off<PHT>(pbase);
-        pb[3] = ds_read_b128_off<PHT + PHL>(pbase);
-        lds_wait_all<4>(pb);
-        asm volatile("" : "+v"(va[0][0]), "+v"(va[0][1]), "+v"(va[1][0]), "+v"(va[1][1]),
-                     "+v"(va[2][0]), "+v"(va[2][1]), "+v"(va[3][0]), "+v"(va[3][1]));
-        // all hi-part products first, then the lo parts: the two products into one
-        // accumulator are eight MFMAs apart, so none waits for the previous one's result
-        i32x4 av[4];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          av[dt] = __builtin_bit_cast(i32x4, __builtin_shufflevector(va[dt][0], va[dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
+        constexpr int PHL = 64 * SR * 2;  // bytes between the hi and lo parts
+        constexpr int PHT = 32 * SR * 2;  // bytes between the two head tiles
+        static_for<0, TPS>([&](auto H) {
+          constexpr int h = decltype(H)::value;
+          constexpr int PH = kTileRows * 2 * h;  // bytes to tile h's rows
+          i32x4 pb[4];
+          pb[0] = ds_read_b128_off<PH>(pbase);
+          pb[1] = ds_read_b128_off<PH + PHL>(pbase);
+          pb[2] = ds_read_b128_off<PH + PHT>(pbase);
+          pb[3] = ds_read_b128_off<PH + PHT + PHL>(pbase);
+          lds_wait_all<4>(pb);
+          asm volatile("" : "+v"(va[h][0][0]), "+v"(va[h][0][1]), "+v"(va[h][1][0]), "+v"(va[h][1][1]),
+                       "+v"(va[h][2][0]), "+v"(va[h][2][1]), "+v"(va[h][3][0]), "+v"(va[h][3][1]));
+          // all hi-part products first, then the lo parts: the two products into one
+          // accumulator are eight MFMAs apart, so none waits for the previous one's result
+          i32x4 av[4];
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt)
+            av[dt] = __builtin_bit_cast(i32x4, __builtin_shufflevector(va[h][dt][0], va[h][dt][1], 0, 1, 2, 3, 4,
+                                                                       5, 6, 7));
 #pragma unroll
-            for (int ht = 0; ht < 2; ++ht)
-              if (ht < n_ht) o[dt][ht] = mma32_bf16(av[dt], pb[2 * ht + hl], o[dt][ht]);
+          for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+              for (int ht = 0; ht < 2; ++ht)
+                if (ht < n_ht) o[dt][ht] = mma32_bf16(av[dt], pb[2 * ht + hl], o[dt][ht]);
+        });
       }
-      if (S || it + 1 < ntiles) read_v(su);  // tile it + 1
+      if (S || it + 1 < nsteps) read_v(su);  // step it + 1
     };
     run_steps(value_step);
     __syncthreads();  // the score waves' statistics are in s_ml
@@ -796,6 +829,8 @@ __global__ __launch_bounds__(256) void mla_merge(const float* __restrict__ ws_o,
 // ---------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+int g_mla_tiles_per_step = 2;  // measured faster on every workload (fewer barrier steps)
+
 int mla_auto_splits(int B, int n_q, int top_k) {
   const long rows = (long)B * n_q;
   long s = (256 + rows - 1) / rows;             // about one workgroup per CU
@@ -836,8 +871,11 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
   }
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
     const unsigned blocks = (unsigned)(rows * n_split);
-    auto kernel = d_rope == 64 ? (Hm > 32 ? sparse_mla_mfma<64, 2> : sparse_mla_mfma<64, 1>)
-                               : (Hm > 32 ? sparse_mla_mfma<0, 2> : sparse_mla_mfma<0, 1>);
+    auto kernel = g_mla_tiles_per_step == 2
+        ? (d_rope == 64 ? (Hm > 32 ? sparse_mla_mfma<64, 2, 2> : sparse_mla_mfma<64, 1, 2>)
+                        : (Hm > 32 ? sparse_mla_mfma<0, 2, 2> : sparse_mla_mfma<0, 1, 2>))
+        : (d_rope == 64 ? (Hm > 32 ? sparse_mla_mfma<64, 2, 1> : sparse_mla_mfma<64, 1, 1>)
+                        : (Hm > 32 ? sparse_mla_mfma<0, 2, 1> : sparse_mla_mfma<0, 1, 1>));
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(512), 0, stream, (const bf16_t*)q_abs, (const bf16_t*)latent,
                        idx, kv_len, out, lse, ws_o, ws_ml, n_q, Hm, n_kv, top_k, sm_scale, n_split, chunk);
   } else {

@@ -120,3 +120,36 @@ def test_deterministic():
     a, _ = _run(wl, idx, 8)
     b, _ = _run(wl, idx, 8)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.fixture
+def one_tile_per_step():
+    """The kernel variant taking one 16-row tile between barriers (the default takes two)."""
+    L = binding()
+    L.dsa_set_tuning("mla_tiles_per_step", 1)
+    yield
+    L.dsa_set_tuning("mla_tiles_per_step", 2)
+
+
+@pytest.mark.parametrize("Hm,top_k,n_split,d_rope", [(64, 1, 1, 64), (64, 17, 1, 64), (64, 32, 1, 64),
+                                                     (64, 33, 1, 64), (64, 100, 3, 64), (16, 300, 2, 64),
+                                                     (48, 256, 4, 64), (64, 2048, 0, 64), (64, 2048, 8, 64),
+                                                     (32, 513, 5, 64), (64, 2051, 0, 0), (64, 2048, 1, 64)])
+def test_one_tile_per_step(one_tile_per_step, Hm, top_k, n_split, d_rope):
+    """The shapes of the MFMA tests with one 16-row tile between barriers (the default takes two:
+    one softmax update and one probability buffer per 32 rows, odd tile counts ending with a
+    padding tile, which the default-path tests above cover)."""
+    wl = DEC.scaled(B=2, n_kv=3000, Hm=Hm, top_k=top_k, d_rope=d_rope)
+    _run(wl, _indices(2, 1, wl.n_kv, top_k, top_k + 11), 1, n_split)
+
+
+def test_one_tile_per_step_padding_kv_len_and_peaks(one_tile_per_step):
+    wl = DEC.scaled(B=3, n_q=2, n_kv=500, top_k=200)
+    _run(wl, _indices(3, 2, wl.n_kv, 200, 2, pad=37, bad=9), 2, n_split=3, kv_len=[500, 250, 499])
+    test_peaked_softmax()
+    test_empty_selection()
+    wl = DEC.scaled(B=2, n_kv=5000, top_k=2048)
+    idx = _indices(2, 1, 5000, 2048, 7)
+    a, _ = _run(wl, idx, 7, n_split=1)
+    b, _ = _run(wl, idx, 7, n_split=16)
+    assert_rowwise(b, a, 1e-5, "one tile per step: split 16 vs 1")
