@@ -95,6 +95,11 @@ int dsa_set_tuning(const char* key, int value) {
     dsa::g_mla_tiles_per_step = value;
     return ok();
   }
+  if (std::strcmp(key, "mla_head_split") == 0) {
+    if (value < 0 || value > 2) return fail(DSA_ERR_SHAPE, "mla_head_split must be 0, 1 or 2 (got %d)", value);
+    dsa::g_mla_head_split = value;
+    return ok();
+  }
   return fail(DSA_ERR_SHAPE, "dsa_set_tuning: unknown key '%s'", key);
 }
 

@@ -40,6 +40,7 @@ hipError_t launch_topk(const float* scores, int* idx, int rows, int n_kv, int to
 
 // sparse MLA
 extern int g_mla_tiles_per_step;  // 16-row tiles per step of the 16-bit MLA kernel (1 or 2, default 2)
+extern int g_mla_head_split;      // 64 heads as two 32-head workgroup rows: 0 automatic, 1 never, 2 always
 int mla_auto_splits(int B, int n_q, int top_k);
 size_t mla_workspace_bytes(int B, int n_q, int Hm, int top_k, int d_latent, int n_split);
 bool mla_mfma_supported(int Hm, int d_latent, int d_rope, int dtype);

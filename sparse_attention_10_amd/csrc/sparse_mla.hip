@@ -288,7 +288,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     const bf16_t* __restrict__ qa, const bf16_t* __restrict__ lat, const int* __restrict__ idx,
     const int* __restrict__ kv_len, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, int n_q, int Hm, int n_kv, int top_k,
-    float sm_scale, int n_split, int chunk) {
+    float sm_scale, int n_split, int chunk, int hsplit) {
   constexpr int DL = 512;
   constexpr int DC = DL + DR;
   constexpr int ROWB = DC * 2;                  // bytes per row
@@ -319,7 +319,10 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bi = logical / n_split;
   const int sp = logical - bi * n_split;
-  const int b = bi / n_q;
+  // with hsplit = 2 a query's 64 heads run as two workgroup rows of 32 heads (bi = 2 query +
+  // half), which share the query's index row and cache
+  const int bq = bi / hsplit;
+  const int b = bq / n_q;
   const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
   const int s0 = sp * chunk, s1 = min(top_k, s0 + chunk);
   const int nslots = max(0, s1 - s0);
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   const int head = hg * 16 + r16;
 
   for (int j = tid; j < nslots; j += 512) {
-    const int r = idx[(long)bi * top_k + s0 + j];
+    const int r = idx[(long)bq * top_k + s0 + j];
     s_idx[j] = (r >= 0 && r < len) ? r : -1;
   }
   {  // heads without a score wave keep zero probabilities
@@ -829,7 +832,16 @@ __global__ __launch_bounds__(256) void mla_merge(const float* __restrict__ ws_o,
 // ---------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-int g_mla_tiles_per_step = 2;  // measured faster on every workload (fewer barrier steps)
+int g_mla_tiles_per_step = 2;
+int g_mla_head_split = 0;
+
+// Workgroup rows per query of the MFMA kernel: 2 (32 heads each) when 64 heads would leave
+// at least half of the 256 CUs without a workgroup, else 1. Partials keep the same bytes.
+static int mla_head_split(int Hm, long rows, int n_split) {
+  if (Hm != 64 || g_mla_head_split == 1) return 1;
+  if (g_mla_head_split == 2) return 2;
+  return rows * n_split <= 128 ? 2 : 1;
+}  // measured faster on every workload (fewer barrier steps)
 
 int mla_auto_splits(int B, int n_q, int top_k) {
   const long rows = (long)B * n_q;
@@ -870,14 +882,16 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
                                      align256((size_t)rows * n_split * hpad * d_latent * sizeof(float)));
   }
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
-    const unsigned blocks = (unsigned)(rows * n_split);
+    const int hs = mla_head_split(Hm, rows, n_split);
+    const int Hk = Hm / hs;  // heads per workgroup row; the [query][head] arrays are read as [query * hs][Hk]
+    const unsigned blocks = (unsigned)(rows * hs * n_split);
     auto kernel = g_mla_tiles_per_step == 2
-        ? (d_rope == 64 ? (Hm > 32 ? sparse_mla_mfma<64, 2, 2> : sparse_mla_mfma<64, 1, 2>)
-                        : (Hm > 32 ? sparse_mla_mfma<0, 2, 2> : sparse_mla_mfma<0, 1, 2>))
-        : (d_rope == 64 ? (Hm > 32 ? sparse_mla_mfma<64, 2, 1> : sparse_mla_mfma<64, 1, 1>)
-                        : (Hm > 32 ? sparse_mla_mfma<0, 2, 1> : sparse_mla_mfma<0, 1, 1>));
+        ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2> : sparse_mla_mfma<64, 1, 2>)
+                        : (Hk > 32 ? sparse_mla_mfma<0, 2, 2> : sparse_mla_mfma<0, 1, 2>))
+        : (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 1> : sparse_mla_mfma<64, 1, 1>)
+                        : (Hk > 32 ? sparse_mla_mfma<0, 2, 1> : sparse_mla_mfma<0, 1, 1>));
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(512), 0, stream, (const bf16_t*)q_abs, (const bf16_t*)latent,
-                       idx, kv_len, out, lse, ws_o, ws_ml, n_q, Hm, n_kv, top_k, sm_scale, n_split, chunk);
+                       idx, kv_len, out, lse, ws_o, ws_ml, n_q, Hk, n_kv, top_k, sm_scale, n_split, chunk, hs);
   } else {
     const int Dc = d_latent + d_rope;
     dim3 grid(n_split, (unsigned)rows, (Hm + kPlainHeads - 1) / kPlainHeads);
@@ -901,10 +915,11 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
-    const int n_ht = (Hm + 31) / 32;
-    const long total = rows * n_ht * kFragSlots;
+    const int hs = mla_head_split(Hm, rows, n_split);
+    const int n_ht = (Hm / hs + 31) / 32;
+    const long total = rows * hs * n_ht * kFragSlots;
     hipLaunchKernelGGL(mla_merge_frag, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws_o,
-                       ws_ml, out, lse, Hm, n_ht, n_split, total);
+                       ws_ml, out, lse, Hm / hs, n_ht, n_split, total);
   } else if (d_latent % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
     const long total = rows * Hm * (d_latent / 4);
     hipLaunchKernelGGL(mla_merge<4>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws_o, ws_ml,

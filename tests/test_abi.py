@@ -146,6 +146,9 @@ def test_tuning_switch(lib):
     assert lib.dsa_set_tuning(b"mla_tiles_per_step", 0) == E_SHAPE
     assert lib.dsa_set_tuning(b"mla_tiles_per_step", 3) == E_SHAPE
     assert lib.dsa_set_tuning(b"mla_tiles_per_step", 2) == OK
+    for v in (1, 2, 0):
+        assert lib.dsa_set_tuning(b"mla_head_split", v) == OK
+    assert lib.dsa_set_tuning(b"mla_head_split", 3) == E_SHAPE
     for v in (4, 8, 0):
         assert lib.dsa_set_tuning(b"score_prefill_waves", v) == OK
     for v in (1, 2, 12, 16, -4):

@@ -153,3 +153,21 @@ def test_one_tile_per_step_padding_kv_len_and_peaks(one_tile_per_step):
     a, _ = _run(wl, idx, 7, n_split=1)
     b, _ = _run(wl, idx, 7, n_split=16)
     assert_rowwise(b, a, 1e-5, "one tile per step: split 16 vs 1")
+
+
+@pytest.fixture(params=[1, 2], ids=["heads_together", "heads_split"])
+def head_split(request):
+    """64 heads in one workgroup row, or as two 32-head rows sharing the query's selection (the
+    automatic choice splits when 64-head rows would fill at most half of the chip, as in most
+    small cases above)."""
+    L = binding()
+    L.dsa_set_tuning("mla_head_split", request.param)
+    yield request.param
+    L.dsa_set_tuning("mla_head_split", 0)
+
+
+@pytest.mark.parametrize("B,top_k,n_split,d_rope", [(2, 2048, 8, 64), (3, 100, 3, 64), (2, 2051, 0, 0),
+                                                    (2, 33, 1, 64), (20, 700, 8, 64)])
+def test_head_split_forced(head_split, B, top_k, n_split, d_rope):
+    wl = DEC.scaled(B=B, n_kv=3000, top_k=top_k, d_rope=d_rope)
+    _run(wl, _indices(B, 1, wl.n_kv, top_k, top_k + 5, pad=3), 9, n_split, kv_len=[3000 - 7 * b for b in range(B)])
