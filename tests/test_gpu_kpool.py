@@ -223,3 +223,14 @@ def test_chain_full_sequences():
     res = run_kpool_chain(wl, inp)
     assert res[2].shape[-1] == 2051
     _check_chain(wl, inp, res, range(wl.B))
+
+
+def test_chain_bench_launch_configuration():
+    """The bench's pooled leg launch configuration: 32 sequences of 32768 tokens (8 MLA parts
+    per query, 64-head workgroups); sequences 0, 13 and 31 (tails of 0, 1 and 3 tokens) drawn
+    from their own streams and compared with the oracle, the others valid zero rows."""
+    wl = KP
+    sel = (0, 13, 31)
+    inp = workloads.gen_kpool(wl, 11, seqs=sel)
+    res = run_kpool_chain(wl, inp)
+    _check_chain(wl, inp, res, sel)

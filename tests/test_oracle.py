@@ -432,3 +432,23 @@ def test_kpool_select_pins_catch(kind):
 
 def test_kpool_mutant_harness_is_faithful():
     pins_kpool_select(_select_mutant("none"), _kscores_mutant("none"), oracle.dense_mla_f64, oracle.sparse_mla_f64)
+
+
+def test_kpool_generator_sequence_subset():
+    """Sequences drawn alone equal the same sequences of the full draw; the others are zero rows
+    that keep their valid entries (the GPU tests use this to run the full batch shape)."""
+    wl = workloads.KPOOL_DECODE_32K.scaled(B=5, n_kv=64, top_k=16)
+    a = workloads.gen_kpool(wl, 3, hole_frac=0.1, seqs=(1, 4))
+    b = workloads.gen_kpool(wl, 3, hole_frac=0.1)
+    for name in ("packed", "q", "w", "qa", "latent"):
+        assert a[name].dtype == b[name].dtype
+        assert np.array_equal(a[name][[1, 4]], b[name][[1, 4]]), name
+        others = a[name][[0, 2, 3]]
+        if name == "packed":
+            assert not others[..., :-1].any()
+            valid = oracle.decode(others[..., -1], wl.idx_dtype)
+            assert np.array_equal(valid, (np.arange(64)[None] < a["kv_len"][[0, 2, 3], None]).astype(float))
+        else:
+            assert not others.any(), name
+    for name in ("ape", "kv_len", "q_pos"):
+        assert np.array_equal(a[name], b[name])

@@ -215,21 +215,35 @@ KPOOL_DECODE_32K = Workload("kpool_decode_b32_32k", 5, B=32, n_q=1, H=32, D=128,
                             latent_std=0.5, kpool=4)
 
 
-def gen_kpool(wl: Workload, seed: int, hole_frac: float = 0.0, kv_len=None) -> Dict[str, np.ndarray]:
+def gen_kpool(wl: Workload, seed: int, hole_frac: float = 0.0, kv_len=None, seqs=None) -> Dict[str, np.ndarray]:
     """Inputs of the pooled-indexer chain. Packed indexer rows [B][n_kv][2 D + 1] in the
     indexer dtype: k ~ N(0, 1) / sqrt(D), gate ~ N(0, 1), valid = 1 for written tokens
     (t < kv_len[b]) and 0 beyond, and 0 for a hole_frac fraction of written tokens when asked;
     ape [kpool][D] fp32 ~ N(0, 1); indexer q [B][n_q][H][D] ~ N(0, 1) / sqrt(D); w ~ U(0, 1)
     * w_scale; absorbed query [B][n_q][Hm][d_latent] ~ N(0, 1); latent [B][n_kv][d_latent] ~
     N(0, latent_std). kv_len defaults to n_kv - (b % kpool), so the sequences end with tails of
-    0 .. kpool - 1 tokens; q_pos = kv_len - n_q + i."""
+    0 .. kpool - 1 tokens; q_pos = kv_len - n_q + i. With seqs given, only those sequences are
+    drawn (each from its own streams, so they equal the full draw); the others hold zero keys,
+    gates, queries, weights and latent rows with the same valid entries."""
     D, kp = wl.D, wl.kpool
     if kv_len is None:
         kv_len = np.array([wl.n_kv - (b % kp) for b in range(wl.B)], np.int32)
     kv_len = np.asarray(kv_len, np.int32)
     s = 1.0 / math.sqrt(D)
     packed, q, w, qa, lat = [], [], [], [], []
+    def zeros(shape, dtype):  # the storage form of 0.0: 0.0f, or all-zero 16-bit patterns
+        return np.zeros(shape, np.float32 if dtype == F32 else np.uint16)
+
     for b in range(wl.B):
+        if seqs is not None and b not in seqs:
+            pk = zeros((wl.n_kv, 2 * D + 1), wl.idx_dtype)
+            pk[:, 2 * D] = round_to((np.arange(wl.n_kv) < kv_len[b]).astype(np.float64), wl.idx_dtype)
+            packed.append(pk)
+            q.append(zeros((wl.n_q, wl.H, D), wl.idx_dtype))
+            w.append(np.zeros((wl.n_q, wl.H), np.float32))
+            qa.append(zeros((wl.n_q, wl.Hm, wl.Dc), wl.mla_dtype))
+            lat.append(zeros((wl.n_kv, wl.Dc), wl.mla_dtype))
+            continue
         k = _draw_normal(_rng(seed, wl.wid, b, _TAG_KPK), (wl.n_kv, D), s)
         gate = _draw_normal(_rng(seed, wl.wid, b, _TAG_GATE), (wl.n_kv, D), 1.0)
         valid = (np.arange(wl.n_kv) < kv_len[b]).astype(np.float64)
