@@ -305,8 +305,12 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kNst * TILE_BYTES];
   __shared__ int s_idx[kMlaMaxChunk];
-  // probabilities of one step's rows: [buffer][hi, lo][head][row], bf16 bits
-  __shared__ __attribute__((aligned(16))) uint16_t s_p[2][2][64 * SR];
+  // probabilities of one step's rows: [buffer][hi, lo][head][row], bf16 bits. A head's rows are
+  // PS = SR + 8 values apart (SR·2 + 16 bytes): with that stride the 8-byte writes of 16 heads
+  // and the 16-byte reads of 8 heads each touch distinct LDS banks (a stride of SR·2 = 32 or 64
+  // bytes put 4 heads on the same banks).
+  constexpr int PS = SR + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[2][2][64 * PS];
   __shared__ __attribute__((aligned(16))) float s_alpha[2][64];   // rescale factor per head
   __shared__ __attribute__((aligned(16))) uint32_t s_flag[2][4];  // score wave rescaled
   __shared__ float s_ml[2][64];                                   // final m, l per head
@@ -565,7 +569,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
           for (int e = 0; e < 4; ++e) hi4[e] = (__bf16)pr[e];
 #pragma unroll
           for (int e = 0; e < 4; ++e) lo4[e] = (__bf16)(pr[e] - (float)hi4[e]);
-          const int po = head * SR + kTileRows * h + 4 * g;
+          const int po = head * PS + kTileRows * h + 4 * g;
           *reinterpret_cast<bf16x4*>(&s_p[buf][0][po]) = hi4;
           *reinterpret_cast<bf16x4*>(&s_p[buf][1][po]) = lo4;
         }
@@ -611,7 +615,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
         });
       });
     };
-    const uint32_t p_off = ((lane & 31) * SR + 8 * (lane >> 5)) * 2;
+    const uint32_t p_off = ((lane & 31) * PS + 8 * (lane >> 5)) * 2;
     auto value_step = [&](int it, int su, auto steady) {
       constexpr bool S = decltype(steady)::value;
       step(it, su, steady);  // its lgkmcnt(0) wait completes the reads into va
@@ -631,8 +635,8 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
         // B operands: P^T [16 rows of tile h][32 heads], lane holds head 32 ht + l % 32, rows
         // 16 h + 8 (l / 32) ..
         const uint32_t pbase = lds_addr(&s_p[buf][0][0]) + p_off;
-        constexpr int PHL = 64 * SR * 2;  // bytes between the hi and lo parts
-        constexpr int PHT = 32 * SR * 2;  // bytes between the two head tiles
+        constexpr int PHL = 64 * PS * 2;  // bytes between the hi and lo parts
+        constexpr int PHT = 32 * PS * 2;  // bytes between the two head tiles
         static_for<0, TPS>([&](auto H) {
           constexpr int h = decltype(H)::value;
           constexpr int PH = kTileRows * 2 * h;  // bytes to tile h's rows
