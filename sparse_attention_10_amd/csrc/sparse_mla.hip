@@ -83,15 +83,19 @@ __global__ __launch_bounds__(256) void sparse_mla_plain(
       s_rows[e] = r >= 0 ? load_as_f32(lat, ((long)b * n_kv + r) * Dc + d) : 0.f;
     }
     __syncthreads();
-    if (tid < kPlainHeads * kPlainRows) {
-      const int h = tid / kPlainRows, j = tid - h * kPlainRows;
-      float z = -INFINITY;
-      if (s_row[j] >= 0 && h < nh) {
-        float acc = 0.f;
-        for (int d = 0; d < Dc; ++d) acc = fmaf(s_q[h * Dc + d], s_rows[j * Dc + d], acc);
-        z = sm_scale * acc;
-      }
-      s_z[tid] = z;
+    // z for the 8 x 16 (head, row) pairs: 16 lanes per pair on consecutive dims (rows Dc
+    // floats apart would put the lanes of a one-pair-per-lane loop on the same LDS banks),
+    // 16 pairs per pass, the lanes' partial sums added with xor shuffles inside their group
+    for (int p0 = 0; p0 < kPlainHeads * kPlainRows; p0 += 16) {
+      const int pr = p0 + (tid >> 4), l = tid & 15;
+      const int h = pr / kPlainRows, j = pr - h * kPlainRows;
+      float acc = 0.f;
+      for (int d = l; d < Dc; d += 16) acc = fmaf(s_q[h * Dc + d], s_rows[j * Dc + d], acc);
+      acc += shfl_xor(acc, 8);
+      acc += shfl_xor(acc, 4);
+      acc += shfl_xor(acc, 2);
+      acc += shfl_xor(acc, 1);
+      if (l == 0) s_z[pr] = (s_row[j] >= 0 && h < nh) ? sm_scale * acc : -INFINITY;
     }
     __syncthreads();
     if (tid < kPlainHeads) {
