@@ -234,3 +234,58 @@ def test_chain_bench_launch_configuration():
     inp = workloads.gen_kpool(wl, 11, seqs=sel)
     res = run_kpool_chain(wl, inp)
     _check_chain(wl, inp, res, sel)
+
+
+def test_graph_replays_match_eager():
+    """The pooled chain (compression, pool scores, top-k over pools, expansion, NoPE MLA with a
+    head split and a merge) captured in a HIP graph gives the eager bits on every replay, with
+    eager work and synchronisations between the replays."""
+    L = binding()
+    wl = KP.scaled(B=3, n_kv=4100, top_k=512)
+    inp = workloads.gen_kpool(wl, 12, hole_frac=0.05)
+    n_pool, kp = wl.n_kv // wl.kpool, wl.top_k // wl.kpool
+    packed, ape = dev(inp["packed"], wl.idx_dtype), dev(inp["ape"])
+    q, w, kv_len = dev(inp["q"], wl.idx_dtype), dev(inp["w"]), dev(inp["kv_len"])
+    qa, lat = dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype)
+    width = wl.kpool * kp + wl.kpool - 1
+    pooled = torch.empty((wl.B, n_pool, wl.D), dtype=torch.float16, device="cuda")
+    scores = torch.empty((wl.B, 1, n_pool), dtype=torch.float32, device="cuda")
+    pidx = torch.empty((wl.B, 1, kp), dtype=torch.int32, device="cuda")
+    tok = torch.empty((wl.B, 1, width), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.B, 1, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
+    ws_t = torch.empty(max(1, L.dsa_topk_workspace_size(wl.B, n_pool, kp)), dtype=torch.uint8, device="cuda")
+    ns = L.dsa_sparse_mla_num_splits(wl.B, 1, width)
+    ws_m = torch.empty(max(1, L.dsa_sparse_mla_workspace_size(wl.B, 1, wl.Hm, width, wl.d_latent, ns)),
+                       dtype=torch.uint8, device="cuda")
+
+    def step():
+        L.dsa_kpool_compress(packed, ape, pooled, wl.D, wl.kpool)
+        L.dsa_kpool_index_score(q, pooled, w, scores, wl.kpool, kv_len=kv_len, scale=wl.scale)
+        L.dsa_topk(scores, pidx, kp, workspace=ws_t)
+        L.dsa_kpool_expand(pidx, packed, wl.D, tok, wl.kpool, kv_len=kv_len)
+        L.dsa_sparse_mla_attn(qa, lat, tok, out, wl.d_latent, wl.sm_scale, kv_len=kv_len, n_split=ns,
+                              workspace=ws_m)
+
+    step()
+    torch.cuda.synchronize()
+    outs = (pooled, scores, pidx, tok, out)
+    ref = [host(t.view(torch.int16) if t.dtype == torch.float16 else t).copy() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(0)  # eager work between replays; the replay must rewrite everything
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("pooled", "scores", "pidx", "tok", "out"), outs, ref):
+            got = host(t.view(torch.int16) if t.dtype == torch.float16 else t)
+            assert np.array_equal(got.view(np.uint32) if got.dtype == np.float32 else got,
+                                  r.view(np.uint32) if r.dtype == np.float32 else r), f"replay {rep}: {name}"
