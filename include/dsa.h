@@ -236,8 +236,9 @@ int dsa_set_tuning(const char* key, int value);
  * ape        device, [kpool][D] fp32 position embedding of a token's slot in its pool
  * pooled     device, [B][n_kv / kpool][D] of out_dtype (the pool cache); only the given
  *            pools are written
- * 1 <= kpool <= 8, D <= 4096, 0 <= pool_begin <= pool_end <= n_kv / kpool (a decode step
- * compresses the one pool that its new token completes; a prefill compresses them all).
+ * 1 <= kpool <= 8, D <= 4096, 0 <= pool_begin <= pool_end <= n_kv / kpool and
+ * (pool_end - pool_begin) * D < 2^31 (a decode step compresses the one pool that its new
+ * token completes; a prefill compresses them all).
  */
 int dsa_kpool_compress(const void* packed, int row_stride, int row_dtype, const float* ape, void* pooled,
                        int out_dtype, int B, int n_kv, int D, int kpool, int pool_begin, int pool_end,

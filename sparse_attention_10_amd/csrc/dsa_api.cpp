@@ -257,6 +257,8 @@ int dsa_kpool_compress(const void* packed, int row_stride, int row_dtype, const 
   if (pool_begin < 0 || pool_end < pool_begin || pool_end > n_kv / kpool)
     return fail(DSA_ERR_SHAPE, "dsa_kpool_compress: pools [%d, %d) outside [0, %d)", pool_begin, pool_end,
                 n_kv / kpool);
+  if ((long long)(pool_end - pool_begin) * D > INT_MAX)
+    return fail(DSA_ERR_SHAPE, "dsa_kpool_compress: (pool_end - pool_begin) * D above 2^31 - 1 per call");
   if (!valid_dtype(row_dtype) || !valid_dtype(out_dtype))
     return fail(DSA_ERR_DTYPE, "dsa_kpool_compress: unknown dtype (rows %d, pooled %d)", row_dtype, out_dtype);
   return hip_status(dsa::launch_kpool_compress(packed, row_stride, row_dtype, ape, pooled, out_dtype, B, n_kv, D,

@@ -236,6 +236,8 @@ def test_kpool_compress_validation(lib):
     assert _compress(lib, rdt=7) == E_DTYPE
     assert _compress(lib, odt=-1) == E_DTYPE
     assert _compress(lib, p0=3, p1=3) == OK                 # empty range: nothing launched
+    # one thread per (pool, dim): at most 2^31 - 1 of them per call
+    assert _compress(lib, n_kv=1 << 26, D=4096, stride=8193, B=1, p1=(1 << 24)) == E_SHAPE
 
 
 def test_kpool_score_and_expand_validation(lib):
