@@ -615,6 +615,15 @@ def main():
         result["cold_cache_eager"] = scrub
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        # the same oracle on one thread (BLAS limited to 1), a shorter sample
+        try:
+            import threadpoolctl
+            with threadpoolctl.threadpool_limits(limits=1):
+                one = cpu_baseline(wl, inp, max(1.0, args.cpu_seconds / 3))
+            result["cpu_baseline"]["single_thread"] = {"value": one["value"], "unit": one["unit"],
+                                                       "cores": one["cores"], "sample": one["sample"]}
+        except ImportError:
+            pass
     print(json.dumps(result), flush=True)
     if args.copy_calibration_mib > 0:
         del q, k, w, qa, lat, scores, idx, out, lse, ws_t, ws_m, p_q, p_k, p_lat, p_qout
