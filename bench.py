@@ -313,8 +313,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: every GPU box here has one GPU and this hot path is run "
-              "and reported per GPU only (--gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU: the path is run and reported per GPU only (--gpus 1); "
+              "a run over several GPUs is not part of this library.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

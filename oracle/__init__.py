@@ -27,7 +27,7 @@ Sources (web pages; cited by title and section):
 * ds4 "Hy3 (295B): CUDA backend support" PR, online-softmax commit: the
   single-pass online softmax equals the two-pass one (split-K + merge here).
 
-Readings where the pages are silent or garbled (each also listed in the design doc):
+Readings where the pages are silent or garbled:
 the indexer ``scale`` is an explicit factor applied after the head sum; relu
 is applied per head before the weight; masked keys score exactly -inf; a
 decode query sits at cache position kv_len - 1; NaN and -inf scores are never
@@ -398,7 +398,7 @@ def dsa_step(inp: dict, wl) -> dict:
 # into one pool key with softmax(gate + ape) weights, queries score pool keys (relu per head,
 # weighted head sum), top-k runs caller-side over pools, and the last incomplete pool (the
 # tail, at most 3 tokens) is always selected, so 2048 selected tokens plus the tail give an
-# attended width of 2051. Readings (also in the design doc): the softmax runs per dimension over
+# attended width of 2051. Readings: the softmax runs per dimension over
 # the pool's tokens, ape[j][d] is indexed by the token's slot j in its pool; a token whose
 # valid entry is zero takes no part in its pool's softmax and is never attended; a pool with
 # no valid token has the zero key; a pool is visible to a query once its last token is
