@@ -3,7 +3,7 @@
 //   S[b,i,t] = scale * sum_h w[b,i,h] * relu(sum_d q[b,i,h,d] * k[b,t,d]),  -inf if masked.
 //
 // Three kernels:
-//   index_score_plain        any dtype / shape, one thread per key (fp32 inputs, odd shapes)
+//   index_score_plain        any dtype / shape, 16 lanes per key (fp32 inputs, odd shapes)
 //   index_score_decode_mfma  16-bit inputs, D = 128, H <= 32, few queries per sequence:
 //                            each wave owns 64 keys per step, the 32 heads sit on the MFMA M
 //                            dimension, relu + head weights + head sum run in the epilogue.
@@ -57,8 +57,13 @@ __device__ __forceinline__ int key_limit(const int* kv_len, const int* q_pos, lo
 }
 
 // ---------------------------------------------------------------------------------------
-// plain kernel
+// plain kernel: grid (ceil(n_kv / 64), B * n_q), 256 threads. A 16-lane group scores one key at
+// a time, four keys per group: lane l takes dims l, l + 16, ... of the key's row, so each load
+// of a group reads consecutive values, and every head's dot product is summed with xor shuffles
+// inside the group.
 // ---------------------------------------------------------------------------------------
+constexpr int kPlainKeys = 64;
+
 template <typename T>
 __global__ __launch_bounds__(256) void index_score_plain(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ w,
@@ -71,22 +76,30 @@ __global__ __launch_bounds__(256) void index_score_plain(
   for (int e = threadIdx.x; e < H * D; e += blockDim.x) qs[e] = load_as_f32(qp, e);
   __syncthreads();
   const int limit = key_limit(kv_len, q_pos, bi, b, i, n_q, n_kv, sink.kpool);
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_kv) return;
   float* out = scores + (long)bi * n_kv;
-  if (t >= limit) {
-    out[t] = -INFINITY;
-    return;
-  }
-  const T* kp = k + ((long)b * n_kv + t) * D;
   const float* wp = w + (long)bi * H;
-  float s = 0.f;
-  for (int h = 0; h < H; ++h) {
-    float dot = 0.f;
-    for (int d = 0; d < D; ++d) dot = fmaf(qs[h * D + d], load_as_f32(kp, d), dot);
-    s = fmaf(wp[h], fmaxf(dot, 0.f), s);
+  const SinkRange sk = sink_range(sink, b);
+  const int grp = threadIdx.x >> 4, l = threadIdx.x & 15;
+  for (int kk = 0; kk < kPlainKeys / 16; ++kk) {
+    const int t = blockIdx.x * kPlainKeys + 16 * kk + grp;  // the same in the group's 16 lanes
+    if (t >= n_kv) break;
+    if (t >= limit) {
+      if (l == 0) out[t] = -INFINITY;
+      continue;
+    }
+    const T* kp = k + ((long)b * n_kv + t) * D;
+    float s = 0.f;
+    for (int h = 0; h < H; ++h) {
+      float dot = 0.f;
+      for (int d = l; d < D; d += 16) dot = fmaf(qs[h * D + d], load_as_f32(kp, d), dot);
+      dot += shfl_xor(dot, 8);
+      dot += shfl_xor(dot, 4);
+      dot += shfl_xor(dot, 2);
+      dot += shfl_xor(dot, 1);
+      s = fmaf(wp[h], fmaxf(dot, 0.f), s);
+    }
+    if (l == 0) out[t] = sk.add(t, scale * s);
   }
-  out[t] = sink_range(sink, b).add(t, scale * s);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -500,7 +513,7 @@ hipError_t launch_index_score(const void* q, const void* k, const float* w, cons
       return launch_mfma<bf16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, sink, stream);
     return launch_mfma<f16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, sink, stream);
   }
-  dim3 grid((n_kv + 255) / 256, (unsigned)((long)B * n_q));
+  dim3 grid((unsigned)((n_kv + kPlainKeys - 1) / kPlainKeys), (unsigned)((long)B * n_q));
   const size_t shm = (size_t)H * D * sizeof(float);
   if (dtype == kF32)
     hipLaunchKernelGGL(index_score_plain<float>, grid, dim3(256), shm, stream, (const float*)q,

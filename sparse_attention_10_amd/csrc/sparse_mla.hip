@@ -29,6 +29,7 @@ namespace dsa {
 // ---------------------------------------------------------------------------------------
 constexpr int kPlainHeads = 8;
 constexpr int kPlainRows = 16;
+constexpr int kPlainBatch = 8;  // global loads in flight per thread while staging q and rows
 
 template <typename T>
 __global__ __launch_bounds__(256) void sparse_mla_plain(
@@ -53,9 +54,18 @@ __global__ __launch_bounds__(256) void sparse_mla_plain(
   const int len = kv_len ? min(kv_len[b], n_kv) : n_kv;
   const int tid = threadIdx.x;
 
-  for (int e = tid; e < kPlainHeads * Dc; e += 256) {
-    const int h = e / Dc, d = e - h * Dc;
-    s_q[e] = h < nh ? load_as_f32(qa, ((long)bi * Hm + h0 + h) * Dc + d) : 0.f;
+  // global loads go out kPlainBatch at a time before any is stored, so their latencies overlap
+  for (int e0 = tid; e0 < kPlainHeads * Dc; e0 += 256 * kPlainBatch) {
+    float v[kPlainBatch];
+#pragma unroll
+    for (int u = 0; u < kPlainBatch; ++u) {
+      const int e = e0 + 256 * u;
+      const int h = e / Dc, d = e - h * Dc;
+      v[u] = (e < kPlainHeads * Dc && h < nh) ? load_as_f32(qa, ((long)bi * Hm + h0 + h) * Dc + d) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPlainBatch; ++u)
+      if (e0 + 256 * u < kPlainHeads * Dc) s_q[e0 + 256 * u] = v[u];
   }
   if (tid < kPlainHeads) {
     s_m[tid] = -INFINITY;
@@ -77,10 +87,18 @@ __global__ __launch_bounds__(256) void sparse_mla_plain(
       s_row[tid] = (r >= 0 && r < len) ? r : -1;
     }
     __syncthreads();
-    for (int e = tid; e < kPlainRows * Dc; e += 256) {
-      const int j = e / Dc, d = e - j * Dc;
-      const int r = s_row[j];
-      s_rows[e] = r >= 0 ? load_as_f32(lat, ((long)b * n_kv + r) * Dc + d) : 0.f;
+    for (int e0 = tid; e0 < kPlainRows * Dc; e0 += 256 * kPlainBatch) {
+      float v[kPlainBatch];
+#pragma unroll
+      for (int u = 0; u < kPlainBatch; ++u) {
+        const int e = e0 + 256 * u;
+        const int j = e / Dc, d = e - j * Dc;
+        const int r = e < kPlainRows * Dc ? s_row[j] : -1;
+        v[u] = r >= 0 ? load_as_f32(lat, ((long)b * n_kv + r) * Dc + d) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kPlainBatch; ++u)
+        if (e0 + 256 * u < kPlainRows * Dc) s_rows[e0 + 256 * u] = v[u];
     }
     __syncthreads();
     // z for the 8 x 16 (head, row) pairs: 16 lanes per pair on consecutive dims (rows Dc
@@ -854,7 +872,10 @@ static int mla_head_split(int Hm, long rows, int n_split) {
 int mla_auto_splits(int B, int n_q, int top_k) {
   const long rows = (long)B * n_q;
   long s = (256 + rows - 1) / rows;             // about one workgroup per CU
-  long max_s = top_k / 128;                     // at least 128 slots per part
+  // at least 128 slots per part; short selections may still take up to 4 parts of 16 slots
+  // (one tile each), which cuts the serial row fetches of a single workgroup
+  long max_s = top_k / 128;
+  if (max_s < 4) max_s = top_k / 16 < 4 ? top_k / 16 : 4;
   if (max_s < 1) max_s = 1;
   if (s > max_s) s = max_s;
   const long min_s = (top_k + kMlaMaxChunk - 1) / kMlaMaxChunk;
