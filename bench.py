@@ -140,15 +140,18 @@ def kpool_bytes(wl, width):
     topk = rows * n_pool * 4 + rows * kp * 4
     expand = rows * kp * 4 + rows * width * (isz + 4)
     mla = rows * width * 4 + rows * wl.Hm * wl.Dc * msz + rows * width * wl.Dc * msz + rows * wl.Hm * (wl.d_latent + 1) * 4
+    # the fused call reads the pool indices and the valid entries and never writes token indices
+    fused = rows * kp * 4 + rows * width * isz + mla - rows * width * 4
     return {"index_score": score, "topk": topk, "expand": expand, "sparse_mla": mla,
-            "step": score + topk + expand + mla}
+            "step": score + topk + expand + mla, "fused_sparse_mla": fused, "fused_step": score + topk + fused}
 
 
 def kpool_leg(dsa, dev, steps, warmup, seed):
     """The pooled-indexer (kpool) decode step at the batched 32K decode shape, timed like the main
     step: compress the cache's complete pools once (the prefill-time cost), then K steps of
-    pool scores -> top-k over pools -> expansion to tokens -> sparse MLA (no rope), replayed from
-    a graph; per-call times from HIP events in an eager pass. Inputs are drawn on the device
+    pool scores -> top-k over pools -> sparse MLA (no rope) that expands the pools to tokens
+    itself, replayed from a graph (and the same step with the expansion as a call of its own);
+    per-call times from HIP events in an eager pass. Inputs are drawn on the device
     from torch's seeded generator with the distributions of workloads.gen_kpool."""
     import torch
     import workloads
@@ -182,9 +185,20 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
     def compress_all():
         dsa.dsa_kpool_compress(packed, ape, pooled, D, kpool)
 
+    score_call = lambda: dsa.dsa_kpool_index_score(q, pooled, w, scores, kpool, kv_len=kv_len, scale=wl.scale)  # noqa: E731
+    topk_call = lambda: dsa.dsa_topk(scores, pidx, kp, workspace=ws_t)  # noqa: E731
+    # the step: pool scores, top-k over pools, and the attention call that expands the pools itself
     calls = {
-        "index_score": lambda: dsa.dsa_kpool_index_score(q, pooled, w, scores, kpool, kv_len=kv_len, scale=wl.scale),
-        "topk": lambda: dsa.dsa_topk(scores, pidx, kp, workspace=ws_t),
+        "index_score": score_call,
+        "topk": topk_call,
+        "sparse_mla": lambda: dsa.dsa_kpool_sparse_mla_attn(qa, lat, pidx, packed, D, kpool, out, wl.d_latent,
+                                                            wl.sm_scale, lse=lse, kv_len=kv_len, n_split=ns,
+                                                            workspace=ws_m),
+    }
+    # the same step with the expansion as a call of its own
+    two_calls = {
+        "index_score": score_call,
+        "topk": topk_call,
         "expand": lambda: dsa.dsa_kpool_expand(pidx, packed, D, tok, kpool, kv_len=kv_len),
         "sparse_mla": lambda: dsa.dsa_sparse_mla_attn(qa, lat, tok, out, wl.d_latent, wl.sm_scale, lse=lse,
                                                       kv_len=kv_len, n_split=ns, workspace=ws_m),
@@ -192,6 +206,10 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
 
     def kstep():
         for f in calls.values():
+            f()
+
+    def kstep_two():
+        for f in two_calls.values():
             f()
 
     for _ in range(3):
@@ -217,29 +235,35 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
     torch.cuda.synchronize()
     per = {name: sum(ev[s_][j].elapsed_time(ev[s_][j + 1]) for s_ in range(steps)) / steps
            for j, name in enumerate(calls)}
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        kstep()
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        kstep()
-    for _ in range(max(1, warmup)):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t0) / steps
+    def graph_time(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(max(1, warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    step_s = graph_time(kstep)
+    two_s = graph_time(kstep_two)
     ab = kpool_bytes(wl, width)
+    ab["sparse_mla"] = ab["fused_sparse_mla"]
     return {"workload": wl.name, "B": B, "n_kv": n_kv, "kpool": kpool, "top_k_tokens": wl.top_k,
             "pools_selected": kp, "attended_width": width, "d_rope": wl.d_rope, "indexer_dtype": "f16",
             "ms_per_step": round(step_s * 1e3, 4), "tokens_per_s": round(B / step_s, 1),
-            "step_algorithmic_bytes": ab["step"], "step_hbm_gbs": round(ab["step"] / step_s / 1e9, 1),
-            "step_hbm_frac": round(ab["step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+            "step_algorithmic_bytes": ab["fused_step"], "step_hbm_gbs": round(ab["fused_step"] / step_s / 1e9, 1),
+            "step_hbm_frac": round(ab["fused_step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+            "expansion_as_own_call_ms_per_step": round(two_s * 1e3, 4),
             "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
             "kernels_gbs": {k_: round(ab[k_] / (per[k_] * 1e-3) / 1e9, 1) for k_ in per},
             "compress_all_pools": {"ms": round(compress_ms, 4), "bytes": compress_b,

@@ -219,7 +219,8 @@ int dsa_set_tuning(const char* key, int value);
  * one key with softmax(gate + ape) weights, queries score pool keys, top-k picks pools, and
  * the attended set is the selected pools' tokens plus the last incomplete pool (the tail),
  * which is always attended. A decode step is dsa_kpool_index_score -> dsa_topk over pools
- * (top_pools = top_k / kpool) -> dsa_kpool_expand -> dsa_sparse_mla_attn over the tokens.
+ * (top_pools = top_k / kpool) -> dsa_kpool_expand -> dsa_sparse_mla_attn over the tokens
+ * (or dsa_kpool_sparse_mla_attn for the last two).
  */
 
 /*
@@ -277,6 +278,20 @@ int dsa_kpool_index_score(const void* q, const void* pooled, const float* w, con
 int dsa_kpool_expand(const int32_t* pool_idx, const void* packed, int row_stride, int row_dtype, int D,
                      const int32_t* kv_len, const int32_t* q_pos, int32_t* tok_idx, int B, int n_q, int n_kv,
                      int top_pools, int kpool, hipStream_t stream);
+
+/* dsa_kpool_expand followed by dsa_sparse_mla_attn in one call: the attention kernel makes
+ * each part's token indices from pool_idx itself (the same tokens, in the same slot order, as
+ * tok_idx above), so the expanded index array is never written. Arguments as in the two calls
+ * it replaces; top_k of the attention is kpool * top_pools + kpool - 1 (n_split and the
+ * workspace size are taken for that top_k), and the latent cache and the packed rows share
+ * n_kv and kv_len. Only the MFMA attention shapes (bf16, Hm a multiple of 16 up to 64,
+ * d_latent 512, d_rope 0 or 64); others return DSA_ERR_UNSUPPORTED (use the two calls).
+ * Results are bit-identical to dsa_kpool_expand + dsa_sparse_mla_attn with the same n_split. */
+int dsa_kpool_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* pool_idx, const void* packed,
+                              int row_stride, int row_dtype, int D, const int32_t* kv_len, const int32_t* q_pos,
+                              float* out, float* lse, int B, int n_q, int Hm, int n_kv, int top_pools, int kpool,
+                              int d_latent, int d_rope, float sm_scale, int dtype, int n_split, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Static text of a status code. */
 const char* dsa_status_string(int status);

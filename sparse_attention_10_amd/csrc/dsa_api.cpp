@@ -292,5 +292,51 @@ int dsa_kpool_expand(const int32_t* pool_idx, const void* packed, int row_stride
                     "dsa_kpool_expand launch");
 }
 
+int dsa_kpool_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* pool_idx, const void* packed,
+                              int row_stride, int row_dtype, int D, const int32_t* kv_len, const int32_t* q_pos,
+                              float* out, float* lse, int B, int n_q, int Hm, int n_kv, int top_pools, int kpool,
+                              int d_latent, int d_rope, float sm_scale, int dtype, int n_split, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_kpool_sparse_mla_attn";
+  if (!q_abs || !latent || !pool_idx || !packed || !out)
+    return fail(DSA_ERR_NULL, "%s: q_abs, latent, pool_idx, packed and out must be non-NULL", fn);
+  if (B < 1 || n_q < 1 || Hm < 1 || n_kv < 1 || D < 1 || top_pools < 1 || kpool < 1 || kpool > 8 ||
+      row_stride < 2 * D + 1 || d_latent < 1 || d_rope < 0)
+    return fail(DSA_ERR_SHAPE, "%s: B=%d n_q=%d Hm=%d n_kv=%d D=%d top_pools=%d kpool=%d row_stride=%d "
+                               "d_latent=%d d_rope=%d out of range", fn, B, n_q, Hm, n_kv, D, top_pools, kpool,
+                row_stride, d_latent, d_rope);
+  const long long width = (long long)kpool * top_pools + kpool - 1;
+  if (width > (1 << 24) || (long long)B * n_kv * row_stride > (1LL << 40))
+    return fail(DSA_ERR_SHAPE, "%s: kpool * top_pools or the packed cache too large", fn);
+  if (!valid_dtype(row_dtype)) return fail(DSA_ERR_DTYPE, "%s: unknown row dtype %d", fn, row_dtype);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_DTYPE, "%s: dtype must be F32 or BF16 (got %d)", fn, dtype);
+  if (!dsa::mla_mfma_supported(Hm, d_latent, d_rope, dtype))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: only the MFMA attention shapes (bf16, Hm %% 16 == 0, Hm <= 64, "
+                                     "d_latent 512, d_rope 0 or 64); use dsa_kpool_expand + dsa_sparse_mla_attn", fn);
+  const int top_k = (int)width;
+  if (n_split <= 0) n_split = dsa::mla_auto_splits(B, n_q, top_k);
+  if (n_split > top_k) n_split = top_k;
+  if ((long long)B * n_q * n_split * Hm > INT_MAX) return fail(DSA_ERR_SHAPE, "%s: B*n_q*n_split*Hm too large", fn);
+  const int chunk = (top_k + n_split - 1) / n_split;
+  if (chunk > 2048)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: %d index slots per part exceed 2048; use n_split >= %d", fn, chunk,
+                (top_k + 2047) / 2048);
+  if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: q_abs, latent and out must be 16-byte aligned", fn);
+  const int esz = row_dtype == DSA_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(packed) & (uintptr_t)(esz - 1)) != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: packed must be aligned to its element size", fn);
+  const size_t need = dsa::mla_workspace_bytes(B, n_q, Hm, top_k, d_latent, n_split);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  const dsa::KpoolSlots ks{pool_idx, static_cast<const uint8_t*>(packed), (long)row_stride * esz, 2 * D * esz,
+                           row_dtype == DSA_F32 ? 1 : 0, top_pools, kpool, q_pos};
+  return hip_status(dsa::launch_sparse_mla(q_abs, latent, nullptr, kv_len, out, lse, B, n_q, Hm, n_kv, top_k,
+                                           d_latent, d_rope, sm_scale, dtype, n_split, workspace, stream, &ks),
+                    "dsa_kpool_sparse_mla_attn launch");
+}
+
 }  // extern "C"
 

@@ -44,10 +44,26 @@ extern int g_mla_head_split;      // 64 heads as two 32-head workgroup rows: 0 a
 int mla_auto_splits(int B, int n_q, int top_k);
 size_t mla_workspace_bytes(int B, int n_q, int Hm, int top_k, int d_latent, int n_split);
 bool mla_mfma_supported(int Hm, int d_latent, int d_rope, int dtype);
+// Slot indices of the pooled indexer, made by the attention kernel itself while it stages
+// a part's slots: slot s < kpool * top_pools is token kpool * pool_idx[s / kpool] + s % kpool,
+// the last kpool - 1 slots are the tail kpool * floor((pos + 1) / kpool) .. pos; a token is
+// kept only if it is in the cache and its packed row's valid entry is nonzero (the same rule
+// as launch_kpool_expand). top_k of the attention is then kpool * top_pools + kpool - 1.
+struct KpoolSlots {
+  const int* pool_idx;    // [B * n_q][top_pools]
+  const uint8_t* packed;  // packed k | gate | valid rows, [B][n_kv]
+  long row_bytes;         // bytes per packed row
+  int valid_off;          // byte offset of the valid entry in a row
+  int valid_f32;          // 1: the valid entry is fp32, else 16-bit
+  int top_pools;
+  int kpool;
+  const int* q_pos;       // [B * n_q] or null (query i of a sequence at len - n_q + i)
+};
 hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* idx,
                              const int* kv_len, float* out, float* lse, int B, int n_q, int Hm,
                              int n_kv, int top_k, int d_latent, int d_rope, float sm_scale,
-                             int dtype, int n_split, void* workspace, hipStream_t stream);
+                             int dtype, int n_split, void* workspace, hipStream_t stream,
+                             const KpoolSlots* kp = nullptr);  // kp: MFMA shapes only, idx unused
 
 // indexer-input preparation (rope + Hadamard + cache append)
 hipError_t launch_indexer_prep(const float* q_in, const float* k_in, const void* latent_in, const int* pos,

@@ -305,12 +305,33 @@ __device__ __forceinline__ int frag_slot(int pq, int ht, int n_ht, int dt, int c
   return (((pq * n_ht + ht) * 4 + dt) * 4 + c) * 64 + lane;
 }
 
-template <int DR, int NHT, int TPS>
+// The token of slot s of query row bq under the pooled indexer (KpoolSlots), or -1.
+__device__ __forceinline__ int kpool_slot_token(const KpoolSlots& ks, int bq, int s, int b, int n_q, int n_kv,
+                                                int len) {
+  const int np = ks.kpool * ks.top_pools;
+  long t;
+  if (s < np) {
+    const int p = ks.pool_idx[(long)bq * ks.top_pools + s / ks.kpool];
+    t = p < 0 ? -1 : (long)ks.kpool * p + s % ks.kpool;
+  } else {
+    const long pos = ks.q_pos ? (long)ks.q_pos[bq] : (long)len - n_q + (bq - b * n_q);
+    const long first = pos + 1 >= 0 ? (pos + 1) / ks.kpool * ks.kpool : -1;  // tail start
+    t = first < 0 ? -1 : first + (s - np);
+    if (t > pos) t = -1;
+  }
+  if (t < 0 || t >= len) return -1;
+  const uint8_t* v = ks.packed + ((long)b * n_kv + t) * ks.row_bytes + ks.valid_off;
+  const bool ok = ks.valid_f32 ? (*reinterpret_cast<const uint32_t*>(v) & 0x7fffffffu) != 0u
+                               : (*reinterpret_cast<const uint16_t*>(v) & 0x7fffu) != 0u;
+  return ok ? (int)t : -1;
+}
+
+template <int DR, int NHT, int TPS, bool KP = false>
 __global__ __launch_bounds__(512) void sparse_mla_mfma(
     const bf16_t* __restrict__ qa, const bf16_t* __restrict__ lat, const int* __restrict__ idx,
     const int* __restrict__ kv_len, float* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, int n_q, int Hm, int n_kv, int top_k,
-    float sm_scale, int n_split, int chunk, int hsplit) {
+    float sm_scale, int n_split, int chunk, int hsplit, KpoolSlots ks) {
   constexpr int DL = 512;
   constexpr int DC = DL + DR;
   constexpr int ROWB = DC * 2;                  // bytes per row
@@ -356,7 +377,9 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   const int head = hg * 16 + r16;
 
   for (int j = tid; j < nslots; j += 512) {
-    const int r = idx[(long)bq * top_k + s0 + j];
+    int r;
+    if constexpr (KP) r = kpool_slot_token(ks, bq, s0 + j, b, n_q, n_kv, len);
+    else r = idx[(long)bq * top_k + s0 + j];
     s_idx[j] = (r >= 0 && r < len) ? r : -1;
   }
   {  // heads without a score wave keep zero probabilities
@@ -899,7 +922,8 @@ bool mla_mfma_supported(int Hm, int d_latent, int d_rope, int dtype) {
 hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* idx,
                              const int* kv_len, float* out, float* lse, int B, int n_q, int Hm,
                              int n_kv, int top_k, int d_latent, int d_rope, float sm_scale,
-                             int dtype, int n_split, void* workspace, hipStream_t stream) {
+                             int dtype, int n_split, void* workspace, hipStream_t stream,
+                             const KpoolSlots* kp) {
   const int chunk = (top_k + n_split - 1) / n_split;
   const long rows = (long)B * n_q;
   float* ws_o = nullptr;
@@ -914,14 +938,20 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
     const int hs = mla_head_split(Hm, rows, n_split);
     const int Hk = Hm / hs;  // heads per workgroup row; the [query][head] arrays are read as [query * hs][Hk]
     const unsigned blocks = (unsigned)(rows * hs * n_split);
-    auto kernel = g_mla_tiles_per_step == 2
+    // the pooled-indexer slots (kp) run with two tiles per step whatever the tuning
+    auto kernel = kp
+        ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2, true> : sparse_mla_mfma<64, 1, 2, true>)
+                        : (Hk > 32 ? sparse_mla_mfma<0, 2, 2, true> : sparse_mla_mfma<0, 1, 2, true>))
+        : g_mla_tiles_per_step == 2
         ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2> : sparse_mla_mfma<64, 1, 2>)
                         : (Hk > 32 ? sparse_mla_mfma<0, 2, 2> : sparse_mla_mfma<0, 1, 2>))
         : (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 1> : sparse_mla_mfma<64, 1, 1>)
                         : (Hk > 32 ? sparse_mla_mfma<0, 2, 1> : sparse_mla_mfma<0, 1, 1>));
+    const KpoolSlots ks = kp ? *kp : KpoolSlots{nullptr, nullptr, 0, 0, 0, 0, 1, nullptr};
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(512), 0, stream, (const bf16_t*)q_abs, (const bf16_t*)latent,
-                       idx, kv_len, out, lse, ws_o, ws_ml, n_q, Hk, n_kv, top_k, sm_scale, n_split, chunk, hs);
+                       idx, kv_len, out, lse, ws_o, ws_ml, n_q, Hk, n_kv, top_k, sm_scale, n_split, chunk, hs, ks);
   } else {
+    if (kp) return hipErrorInvalidValue;  // the pooled-indexer slots exist on the MFMA kernel only
     const int Dc = d_latent + d_rope;
     dim3 grid(n_split, (unsigned)rows, (Hm + kPlainHeads - 1) / kPlainHeads);
     const size_t shm = (size_t)(kPlainHeads * Dc + kPlainRows * Dc + kPlainHeads * kPlainRows +

@@ -22,7 +22,7 @@ _DTYPE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.float16: DSA_F
 
 EXPORTED = ("dsa_index_score", "dsa_index_score_sink", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
             "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_indexer_prep", "dsa_layer_computes_topk", "dsa_topk_source_layer", "dsa_set_tuning",
-            "dsa_kpool_compress", "dsa_kpool_index_score", "dsa_kpool_expand",
+            "dsa_kpool_compress", "dsa_kpool_index_score", "dsa_kpool_expand", "dsa_kpool_sparse_mla_attn",
             "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -60,6 +60,9 @@ def _load() -> ctypes.CDLL:
     lib.dsa_kpool_index_score.restype = I
     lib.dsa_kpool_expand.argtypes = [P, P, I, I, I, P, P, P, I, I, I, I, I, P]
     lib.dsa_kpool_expand.restype = I
+    lib.dsa_kpool_sparse_mla_attn.argtypes = [P, P, P, P, I, I, I, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P,
+                                              S, P]
+    lib.dsa_kpool_sparse_mla_attn.restype = I
     lib.dsa_layer_computes_topk.argtypes = [I]
     lib.dsa_layer_computes_topk.restype = I
     lib.dsa_topk_source_layer.argtypes = [I]
@@ -326,3 +329,41 @@ def dsa_kpool_expand(pool_idx: torch.Tensor, packed: torch.Tensor, D: int, tok_i
                                 _ptr(kv_len), _ptr(q_pos), tok_idx.data_ptr(), B, n_q, n_kv, top_pools, int(kpool),
                                 _stream(stream)), "dsa_kpool_expand")
     return tok_idx
+
+
+def dsa_kpool_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, pool_idx: torch.Tensor,
+                              packed: torch.Tensor, D: int, kpool: int, out: torch.Tensor, d_latent: int,
+                              sm_scale: float, lse: Optional[torch.Tensor] = None,
+                              kv_len: Optional[torch.Tensor] = None, q_pos: Optional[torch.Tensor] = None,
+                              n_split: int = 0, workspace: Optional[torch.Tensor] = None,
+                              stream=None) -> torch.Tensor:
+    """dsa_kpool_expand + dsa_sparse_mla_attn in one call: q_abs [B][n_q][Hm][Dc] bf16, latent
+    [B][n_kv][Dc] bf16, pool_idx [B][n_q][top_pools] int32, packed [B][n_kv][row_stride],
+    out [B][n_q][Hm][d_latent] fp32 (output), lse [B][n_q][Hm] fp32 or None."""
+    B, n_q, Hm, Dc = q_abs.shape
+    n_kv = latent.shape[1]
+    top_pools = pool_idx.shape[-1]
+    for t, n in ((q_abs, "q_abs"), (latent, "latent"), (pool_idx, "pool_idx"), (packed, "packed"), (out, "out")):
+        _dev(t, n)
+    if tuple(latent.shape) != (B, n_kv, Dc) or tuple(pool_idx.shape) != (B, n_q, top_pools) \
+            or tuple(out.shape) != (B, n_q, Hm, d_latent) or latent.dtype != q_abs.dtype \
+            or packed.dim() != 3 or tuple(packed.shape[:2]) != (B, n_kv):
+        raise ValueError("dsa_kpool_sparse_mla_attn: inconsistent shapes or dtypes")
+    if pool_idx.dtype != torch.int32 or out.dtype != torch.float32:
+        raise ValueError("pool_idx must be int32 and out float32")
+    if lse is not None:
+        _dev(lse, "lse")
+    _int32_opt(kv_len, "kv_len")
+    _int32_opt(q_pos, "q_pos")
+    width = kpool * top_pools + kpool - 1
+    need = dsa_sparse_mla_workspace_size(B, n_q, Hm, width, d_latent, n_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_abs.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dsa_kpool_sparse_mla_attn(q_abs.data_ptr(), latent.data_ptr(), pool_idx.data_ptr(), packed.data_ptr(),
+                                         packed.shape[2], _DTYPE[packed.dtype], D, _ptr(kv_len), _ptr(q_pos),
+                                         out.data_ptr(), _ptr(lse), B, n_q, Hm, n_kv, top_pools, int(kpool),
+                                         d_latent, Dc - d_latent, float(sm_scale), _DTYPE[q_abs.dtype],
+                                         int(n_split), _ptr(workspace), wbytes, _stream(stream)),
+           "dsa_kpool_sparse_mla_attn")
+    return out

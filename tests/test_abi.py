@@ -254,3 +254,35 @@ def test_kpool_score_and_expand_validation(lib):
     assert g(FAKE, FAKE, 257, 2, 128, None, None, FAKE, 1, 1, 64, 4, 0, None) == E_SHAPE
     assert g(FAKE, FAKE, 257, 2, 128, None, None, FAKE, 300, 300, 64, 4, 4, None) == E_SHAPE
     assert g(FAKE, FAKE, 257, 5, 128, None, None, FAKE, 1, 1, 64, 4, 4, None) == E_DTYPE
+
+
+def _kpmla(lib, **kw):
+    a = dict(q=FAKE, lat=FAKE, pidx=FAKE, packed=FAKE, stride=257, rdt=2, D=128, kv_len=None, q_pos=None,
+             out=FAKE, lse=None, B=2, n_q=1, Hm=64, n_kv=4096, top_pools=512, kpool=4, dl=512, dr=0, sm=0.0625,
+             dt=1, ns=8, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.dsa_kpool_sparse_mla_attn(a["q"], a["lat"], a["pidx"], a["packed"], a["stride"], a["rdt"], a["D"],
+                                         a["kv_len"], a["q_pos"], a["out"], a["lse"], a["B"], a["n_q"], a["Hm"],
+                                         a["n_kv"], a["top_pools"], a["kpool"], a["dl"], a["dr"], a["sm"], a["dt"],
+                                         a["ns"], a["ws"], a["wsb"], None)
+
+
+def test_kpool_sparse_mla_validation(lib):
+    for k in ("q", "lat", "pidx", "packed", "out"):
+        assert _kpmla(lib, **{k: None}) == E_NULL, k
+    assert _kpmla(lib, stride=256) == E_SHAPE           # no room for the valid column
+    assert _kpmla(lib, kpool=0) == E_SHAPE
+    assert _kpmla(lib, kpool=9) == E_SHAPE
+    assert _kpmla(lib, top_pools=0) == E_SHAPE
+    assert _kpmla(lib, rdt=7) == E_DTYPE
+    assert _kpmla(lib, dt=2) == E_DTYPE                 # f16 attention
+    assert _kpmla(lib, dt=0) == E_UNSUP                 # fp32 attention: the two calls instead
+    assert _kpmla(lib, Hm=8) == E_UNSUP
+    assert _kpmla(lib, dr=32) == E_UNSUP
+    assert _kpmla(lib, ns=1) == E_UNSUP                 # 2051 slots in one part
+    assert _kpmla(lib, q=FAKE + 8) == E_UNSUP           # 16-byte alignment
+    assert _kpmla(lib, packed=FAKE + 1) == E_UNSUP      # element alignment of the packed rows
+    assert _kpmla(lib, ws=None) == E_WS
+    need = lib.dsa_sparse_mla_workspace_size(2, 1, 64, 4 * 512 + 3, 512, 8)
+    assert need > 0
+    assert _kpmla(lib, wsb=need - 1) == E_WS

@@ -160,8 +160,10 @@ def test_expand_bit_exact():
         assert np.array_equal(host(tok), want), f"expansion n_q={n_q} top_k={top_k}"
 
 
-def run_kpool_chain(wl, inp):
-    """compress every complete pool -> pool scores -> top-k over pools -> tokens -> attention."""
+def run_kpool_chain(wl, inp, fused=False):
+    """compress every complete pool -> pool scores -> top-k over pools -> tokens -> attention
+    (fused: the attention call makes the tokens itself; the expansion still runs for the
+    token checks)."""
     L = binding()
     packed, pooled = _compress(inp, wl)
     rows, n_pool, kp = wl.B * wl.n_q, wl.n_kv // wl.kpool, wl.top_k // wl.kpool
@@ -176,8 +178,12 @@ def run_kpool_chain(wl, inp):
     L.dsa_kpool_expand(pidx, packed, wl.D, tok, wl.kpool, kv_len=kv_len)
     out = torch.empty((wl.B, wl.n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
     lse = torch.empty((wl.B, wl.n_q, wl.Hm), dtype=torch.float32, device="cuda")
-    L.dsa_sparse_mla_attn(dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype), tok, out, wl.d_latent,
-                          wl.sm_scale, lse=lse, kv_len=kv_len)
+    if fused:
+        L.dsa_kpool_sparse_mla_attn(dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype), pidx, packed,
+                                    wl.D, wl.kpool, out, wl.d_latent, wl.sm_scale, lse=lse, kv_len=kv_len)
+    else:
+        L.dsa_sparse_mla_attn(dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype), tok, out,
+                              wl.d_latent, wl.sm_scale, lse=lse, kv_len=kv_len)
     torch.cuda.synchronize()
     return host(scores), host(pidx), host(tok), host(out), host(lse)
 
@@ -209,10 +215,11 @@ def _check_chain(wl, inp, res, seqs):
         assert_rowwise(lse[sl], o_lse, RTOL[wl.mla_dtype], f"{wl.name} lse b={b}")
 
 
-def test_chain_small():
+@pytest.mark.parametrize("fused", [False, True])
+def test_chain_small(fused):
     wl = KP.scaled(B=4, n_kv=3000, top_k=256)
     inp = workloads.gen_kpool(wl, 8, hole_frac=0.05)
-    _check_chain(wl, inp, run_kpool_chain(wl, inp), range(wl.B))
+    _check_chain(wl, inp, run_kpool_chain(wl, inp, fused), range(wl.B))
 
 
 def test_chain_full_sequences():
@@ -227,13 +234,74 @@ def test_chain_full_sequences():
 
 def test_chain_bench_launch_configuration():
     """The bench's pooled leg launch configuration: 32 sequences of 32768 tokens (8 MLA parts
-    per query, 64-head workgroups); sequences 0, 13 and 31 (tails of 0, 1 and 3 tokens) drawn
-    from their own streams and compared with the oracle, the others valid zero rows."""
+    per query, 64-head workgroups, the fused expansion + attention call); sequences 0, 13 and
+    31 (tails of 0, 1 and 3 tokens) drawn from their own streams and compared with the oracle,
+    the others valid zero rows."""
     wl = KP
     sel = (0, 13, 31)
     inp = workloads.gen_kpool(wl, 11, seqs=sel)
-    res = run_kpool_chain(wl, inp)
+    res = run_kpool_chain(wl, inp, fused=True)
     _check_chain(wl, inp, res, sel)
+
+
+def _random_pools(wl, seed, pad_rows=()):
+    """Ascending distinct pool indices per query row (any set is a valid input of the
+    expansion); rows in pad_rows end with -1 padding."""
+    rng = np.random.default_rng(seed)
+    n_pool, kp = wl.n_kv // wl.kpool, wl.top_k // wl.kpool
+    out = np.empty((wl.B * wl.n_q, kp), np.int32)
+    for r in range(wl.B * wl.n_q):
+        n = kp // 2 if r in pad_rows else kp
+        row = np.sort(rng.choice(n_pool, size=n, replace=False)).astype(np.int32)
+        out[r] = np.concatenate([row, np.full(kp - n, -1, np.int32)])
+    return out.reshape(wl.B, wl.n_q, kp)
+
+
+@pytest.mark.parametrize("case", ["nope", "rope_qpos", "hm32", "f32_rows", "bf16_rows", "heads_together",
+                                  "rope_together", "nsplit3"])
+def test_fused_equals_expand_then_attention(case):
+    """dsa_kpool_sparse_mla_attn gives the bits of dsa_kpool_expand + dsa_sparse_mla_attn with
+    the same parts: holes, padded pool rows, tails of 0..3 tokens, explicit positions (one
+    before the first complete pool, one past the cache), 16-bit and fp32 valid entries."""
+    L = binding()
+    kw = dict(B=4, n_kv=1100, top_k=256)
+    if case in ("rope_qpos", "rope_together"):
+        kw.update(n_q=3, d_rope=64)
+    if case == "hm32":
+        kw.update(Hm=32)
+    if case == "f32_rows":
+        kw.update(idx_dtype=workloads.F32)
+    if case == "bf16_rows":
+        kw.update(idx_dtype=workloads.BF16)
+    wl = KP.scaled(**kw)
+    inp = workloads.gen_kpool(wl, 21, hole_frac=0.15)
+    pidx = dev(_random_pools(wl, 22, pad_rows=(1, 2)))
+    q_pos = None
+    if case in ("rope_qpos", "rope_together"):
+        rng = np.random.default_rng(23)
+        qp = np.stack([rng.integers(0, int(n), size=wl.n_q) for n in inp["kv_len"]]).astype(np.int32)
+        qp[1, 0], qp[2, 1] = 1, int(inp["kv_len"][2]) + 5
+        q_pos = dev(qp)
+    packed, kv_len = dev(inp["packed"], wl.idx_dtype), dev(inp["kv_len"])
+    qa, lat = dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype)
+    width = wl.kpool * (wl.top_k // wl.kpool) + wl.kpool - 1
+    ns = 3 if case == "nsplit3" else 0
+    if case in ("heads_together", "rope_together"):  # small cases split the 64 heads by themselves
+        L.dsa_set_tuning("mla_head_split", 1)
+    try:
+        tok = torch.empty((wl.B, wl.n_q, width), dtype=torch.int32, device="cuda")
+        L.dsa_kpool_expand(pidx, packed, wl.D, tok, wl.kpool, kv_len=kv_len, q_pos=q_pos)
+        shape = (wl.B, wl.n_q, wl.Hm, wl.d_latent)
+        out_a, out_b = (torch.full(shape, 7.0, device="cuda") for _ in range(2))
+        lse_a, lse_b = (torch.full(shape[:3], 7.0, device="cuda") for _ in range(2))
+        L.dsa_sparse_mla_attn(qa, lat, tok, out_a, wl.d_latent, wl.sm_scale, lse=lse_a, kv_len=kv_len, n_split=ns)
+        L.dsa_kpool_sparse_mla_attn(qa, lat, pidx, packed, wl.D, wl.kpool, out_b, wl.d_latent, wl.sm_scale,
+                                    lse=lse_b, kv_len=kv_len, q_pos=q_pos, n_split=ns)
+        torch.cuda.synchronize()
+    finally:
+        L.dsa_set_tuning("mla_head_split", 0)
+    assert np.array_equal(host(out_a).view(np.uint32), host(out_b).view(np.uint32)), case
+    assert np.array_equal(host(lse_a).view(np.uint32), host(lse_b).view(np.uint32)), case
 
 
 def test_graph_replays_match_eager():
