@@ -306,8 +306,9 @@ def test_fused_equals_expand_then_attention(case):
 
 def test_graph_replays_match_eager():
     """The pooled chain (compression, pool scores, top-k over pools, expansion, NoPE MLA with a
-    head split and a merge) captured in a HIP graph gives the eager bits on every replay, with
-    eager work and synchronisations between the replays."""
+    head split and a merge, and the attention call that expands the pools itself) captured in
+    a HIP graph gives the eager bits on every replay, with eager work and synchronisations
+    between the replays."""
     L = binding()
     wl = KP.scaled(B=3, n_kv=4100, top_k=512)
     inp = workloads.gen_kpool(wl, 12, hole_frac=0.05)
@@ -321,6 +322,7 @@ def test_graph_replays_match_eager():
     pidx = torch.empty((wl.B, 1, kp), dtype=torch.int32, device="cuda")
     tok = torch.empty((wl.B, 1, width), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.B, 1, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
+    out_f = torch.empty_like(out)
     ws_t = torch.empty(max(1, L.dsa_topk_workspace_size(wl.B, n_pool, kp)), dtype=torch.uint8, device="cuda")
     ns = L.dsa_sparse_mla_num_splits(wl.B, 1, width)
     ws_m = torch.empty(max(1, L.dsa_sparse_mla_workspace_size(wl.B, 1, wl.Hm, width, wl.d_latent, ns)),
@@ -333,11 +335,14 @@ def test_graph_replays_match_eager():
         L.dsa_kpool_expand(pidx, packed, wl.D, tok, wl.kpool, kv_len=kv_len)
         L.dsa_sparse_mla_attn(qa, lat, tok, out, wl.d_latent, wl.sm_scale, kv_len=kv_len, n_split=ns,
                               workspace=ws_m)
+        L.dsa_kpool_sparse_mla_attn(qa, lat, pidx, packed, wl.D, wl.kpool, out_f, wl.d_latent, wl.sm_scale,
+                                    kv_len=kv_len, n_split=ns, workspace=ws_m)
 
     step()
     torch.cuda.synchronize()
-    outs = (pooled, scores, pidx, tok, out)
+    outs = (pooled, scores, pidx, tok, out, out_f)
     ref = [host(t.view(torch.int16) if t.dtype == torch.float16 else t).copy() for t in outs]
+    assert np.array_equal(ref[5].view(np.uint32), ref[4].view(np.uint32)), "fused attention differs"
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -353,7 +358,7 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, t, r in zip(("pooled", "scores", "pidx", "tok", "out"), outs, ref):
+        for name, t, r in zip(("pooled", "scores", "pidx", "tok", "out", "out_fused"), outs, ref):
             got = host(t.view(torch.int16) if t.dtype == torch.float16 else t)
             assert np.array_equal(got.view(np.uint32) if got.dtype == np.float32 else got,
                                   r.view(np.uint32) if r.dtype == np.float32 else r), f"replay {rep}: {name}"
