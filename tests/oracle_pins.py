@@ -569,3 +569,98 @@ def pins_kpool_select(fn, scores_fn, dense_fn, sparse_fn):
         tail = [t for t in got[0, 0].tolist() if t >= 0]
         m, r = divmod(pos, kp)
         assert tail == (list(range(kp * m, pos + 1)) if r < kp - 1 else []), f"tail at pos {pos}"
+    # a query before the first token (pos < 0) sees no pool and no tail token: every slot -1
+    for pos in range(-9, 0):
+        got = fn(np.full((1, 1, 3), -np.inf), np.ones((1, 12), bool), np.array([12]), np.array([[pos]]), 4, kp)
+        assert np.array_equal(got, np.full_like(got, -1)), f"no tokens before the first at pos {pos}"
+
+
+# ----------------------------------------------------------------------------
+# storage rounding: fn(x64, dtype) -> float32 array, or bf16 / f16 bit patterns (uint16)
+# ----------------------------------------------------------------------------
+# The reading the oracle states for its expected 16-bit values (the kernels compute in fp32 and
+# store the cache dtype; ik_llama_opt log, "decode-correct via persistent indexer-K cache": the
+# rotated keys are stored as F16): round the float64 value to float32, to nearest even, then
+# that float32 to the 16-bit format, to nearest even (IEEE 754 roundTiesToEven, overflow to
+# infinity). The pin below finds the expected code by brute force over the format's whole code
+# table, so it shares nothing with the bit tricks of the implementation.
+_FMT = {  # dtype code: (decode of a uint16 code table to float64, first code past the largest
+    #        finite one (the infinity), the value IEEE rounding gives that code: 2^(emax + 1))
+    1: (lambda c: (c.astype(np.uint32) << 16).view(np.float32).astype(np.float64), 0x7F80, 2.0 ** 128),
+    2: (lambda c: c.astype(np.uint16).view(np.float16).astype(np.float64), 0x7C00, 2.0 ** 16),
+}
+
+
+def _brute_round(x32: np.ndarray, dtype: int) -> np.ndarray:
+    """The nearest code to each finite float32 value among the codes of its sign (zero and the
+    infinity included, the infinity standing at 2^(emax + 1)); ties to the code with an even
+    last bit."""
+    dec, inf_code, inf_at = _FMT[dtype]
+    mags = np.arange(inf_code + 1, dtype=np.uint32)           # +0 .. +inf
+    vals = dec(mags.astype(np.uint16))
+    vals[-1] = inf_at
+    out = np.empty(x32.shape, np.uint16)
+    flat = x32.reshape(-1).astype(np.float64)
+    res = out.reshape(-1)
+    for s in range(0, flat.size, 64):
+        a = np.abs(flat[s:s + 64])
+        dist = np.abs(vals[None, :] - a[:, None])
+        best = dist.min(axis=1, keepdims=True)
+        cand = dist == best
+        # among equal distances the even code (two at most: neighbours differ in the last bit)
+        even = cand & ((mags[None, :] & 1) == 0)
+        pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+        # at or past 2^(emax + 1) (float32 infinity included) the nearest is the infinity; the
+        # distances there would lose their low bits in float64
+        pick = np.where(a >= inf_at, inf_code, mags[pick])
+        sign = np.signbit(flat[s:s + 64]).astype(np.uint32) << 15
+        res[s:s + 64] = (pick | sign).astype(np.uint16)
+    return out
+
+
+def _encode_cases(dtype: int, rng) -> np.ndarray:
+    dec, inf_code, inf_at = _FMT[dtype]
+    xs = [rng.standard_normal(300) * 10.0 ** rng.integers(-6, 5, 300),
+          np.array([0.0, -0.0, 1.0, -1.0, 1e-30, -1e-30, 1e30, -1e30])]
+    # exact midpoints between neighbouring codes (each is a float32 value), with the lower
+    # code even and odd, in the normal and (f16) subnormal range, and just beside them
+    codes = rng.integers(1, inf_code - 1, 200).astype(np.uint16)
+    lo, hi = dec(codes), dec(codes + 1)
+    mid = (lo + hi) / 2.0
+    assert np.array_equal(mid.astype(np.float32).astype(np.float64), mid), "midpoints are float32 values"
+    xs += [mid, -mid, np.nextafter(mid.astype(np.float32), np.float32(np.inf)).astype(np.float64),
+           np.nextafter(mid.astype(np.float32), np.float32(0)).astype(np.float64)]
+    # around the overflow threshold (half an ulp above the largest finite value)
+    top = dec(np.array([inf_code - 1], np.uint16))[0]
+    thr = (top + inf_at) / 2.0
+    xs.append(np.array([top, thr, -thr, np.nextafter(np.float32(thr), np.float32(0)), 2.0 * inf_at]))
+    return np.concatenate(xs)
+
+
+def pins_encode(fn):
+    from oracle import F32, BF16, F16  # dtype codes only
+    rng = _rng(71)
+    for dtype in (BF16, F16):
+        x64 = _encode_cases(dtype, rng)
+        with np.errstate(over="ignore"):
+            got = np.asarray(fn(x64, dtype))
+        assert got.dtype == np.uint16 and got.shape == x64.shape, f"dtype {dtype}: uint16 codes"
+        with np.errstate(over="ignore"):
+            x32 = x64.astype(np.float32)  # float64 -> float32, nearest even (numpy's IEEE conversion)
+        want = _brute_round(x32, dtype)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (f"dtype {dtype}: {bad.size} codes differ, e.g. x={x64[bad[0]]!r} "
+                               f"got {got[bad[0]]:#06x} want {want[bad[0]]:#06x}")
+        # the float64 value is rounded to float32 first: a midpoint between two codes plus far
+        # less than half a float32 ulp is a tie after that step, so it takes the even code
+        dec, inf_code, _ = _FMT[dtype]
+        c = (rng.integers(100, inf_code // 2 - 1, 50) * 2).astype(np.uint16)  # even lower codes
+        mid = (dec(c) + dec(c + 1)) / 2.0
+        nudged = mid + np.abs(mid) * 2.0 ** -40
+        assert np.array_equal(np.asarray(fn(nudged, dtype)), c), f"dtype {dtype}: rounded via float32"
+        # NaN stays NaN
+        nan = np.asarray(fn(np.array([np.nan]), dtype))
+        assert np.isnan(dec(nan.astype(np.uint16)))[0], f"dtype {dtype}: NaN"
+    # float32 storage is numpy's float64 -> float32 conversion
+    x64 = rng.standard_normal(100) * 1e3
+    assert np.array_equal(np.asarray(fn(x64, F32)), x64.astype(np.float32)), "float32 storage"

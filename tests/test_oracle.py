@@ -403,6 +403,12 @@ def _select_mutant(kind):
                 pos = int(np.asarray(q_pos)[b, i])
                 if kind == "no_tail":
                     out[b, i, kpool * kp:] = -1
+                if kind == "tail_no_lower_bound":  # the tail rule without t >= 0
+                    t0 = kpool * ((pos + 1) // kpool)
+                    for j in range(kpool - 1):
+                        t = t0 + j
+                        if t <= pos and t < int(np.asarray(kv_len)[b]) and valid[b, t]:
+                            out[b, i, kpool * kp + j] = t
                 if kind == "tail_floor":
                     t0 = kpool * (pos // kpool)
                     for j in range(kpool - 1):
@@ -424,7 +430,8 @@ def test_kpool_score_pins_catch(kind):
         pins_kpool_select(oracle.kpool_select, _kscores_mutant(kind), oracle.dense_mla_f64, oracle.sparse_mla_f64)
 
 
-@pytest.mark.parametrize("kind", ["pools_as_tokens", "no_tail", "tail_floor", "keep_invalid"])
+@pytest.mark.parametrize("kind", ["pools_as_tokens", "no_tail", "tail_floor", "keep_invalid",
+                                  "tail_no_lower_bound"])
 def test_kpool_select_pins_catch(kind):
     with pytest.raises(AssertionError):
         pins_kpool_select(_select_mutant(kind), oracle.kpool_scores, oracle.dense_mla_f64, oracle.sparse_mla_f64)
@@ -452,3 +459,71 @@ def test_kpool_generator_sequence_subset():
             assert not others.any(), name
     for name in ("ape", "kv_len", "q_pos"):
         assert np.array_equal(a[name], b[name])
+
+
+# ---------------------------------------------------------------------------
+# storage rounding (the expected values of the indexer-prep and pool-compression parity tests)
+# ---------------------------------------------------------------------------
+from oracle_pins import pins_encode  # noqa: E402
+
+
+def test_encode_pins():
+    pins_encode(oracle.encode)
+
+
+def _encode_mutant(kind):
+    def away(x32, dtype):
+        """the next 16-bit code away from zero of the code that truncation gives"""
+        return _toward_zero(x32, dtype) + np.uint16(1)
+
+    def _toward_zero(x32, dtype):
+        if dtype == oracle.BF16:
+            return (x32.view(np.uint32) >> 16).astype(np.uint16)
+        r = x32.astype(np.float16)
+        over = np.abs(r.astype(np.float64)) > np.abs(x32.astype(np.float64))
+        r[over] = np.nextafter(r[over], np.float16(0))
+        return r.view(np.uint16)
+
+    def fn(x64, dtype):
+        x64 = np.asarray(x64, np.float64)
+        if dtype == oracle.F32 or kind == "none":
+            return oracle.encode(x64, dtype)
+        x32 = x64.astype(np.float32)
+        if kind == "truncate":
+            out = _toward_zero(x32, dtype)
+        elif kind == "half_up":  # ties away from zero
+            lo = _toward_zero(x32, dtype)
+            hi = away(x32, dtype)
+            dlo = np.abs(np.abs(x32.astype(np.float64)) - np.abs(oracle.decode(lo, dtype)))
+            dhi = np.abs(np.abs(oracle.decode(hi, dtype)) - np.abs(x32.astype(np.float64)))
+            out = np.where(dhi <= dlo, hi, lo)
+        elif kind == "skip_f32":  # rounds the float64 value straight to 16 bits
+            lo = _toward_zero(x32, dtype)
+            sign = lo & np.uint16(0x8000)
+            mag = (lo & np.uint16(0x7FFF)).astype(np.int64)
+            # float32 may have lost the float64 value's low bits: take the neighbouring
+            # magnitudes of that code and compare them with the float64 value itself
+            cands = np.stack([np.maximum(mag - 1, 0), mag, mag + 1]).astype(np.uint16)
+            d = np.abs(oracle.decode(cands, dtype) - np.abs(x64)[None])
+            best = d.min(axis=0, keepdims=True)
+            even = (d == best) & ((cands & 1) == 0)
+            pick = np.where(even.any(axis=0), even.argmax(axis=0), (d == best).argmax(axis=0))
+            out = np.take_along_axis(cands, pick[None], 0)[0] | sign
+            big = np.abs(x64) >= float(np.finfo(np.float16).max if dtype == oracle.F16 else 3.38e38)
+            out[big] = oracle.encode(x64[big], dtype)  # overflow as the oracle: only the rounding step differs
+        nan = np.isnan(x64)
+        out = out.copy()
+        out[nan] = 0x7FC0 if dtype == oracle.BF16 else 0x7E00
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["truncate", "half_up", "skip_f32"])
+def test_encode_pins_catch(kind):
+    with np.errstate(over="ignore", invalid="ignore"):
+        with pytest.raises(AssertionError):
+            pins_encode(_encode_mutant(kind))
+
+
+def test_encode_mutant_harness_is_faithful():
+    pins_encode(_encode_mutant("none"))
