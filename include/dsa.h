@@ -17,8 +17,11 @@
  *     detected on the host before anything is launched; the call then writes nothing.
  *     DSA_ERR_HIP reports a failed kernel launch. No call synchronises the host or the
  *     stream: faults inside a kernel surface at the caller's next synchronisation.
- *   - Calls are stateless and may be made from several host threads at once
- *     (dsa_last_error is per thread). Two calls that share a workspace must not
+ *   - Calls keep no state from one call to the next and may be made from several host
+ *     threads at once (dsa_last_error is per thread). The one process-wide state is the
+ *     set of tuning switches of dsa_set_tuning: each call reads them once when it starts,
+ *     they only choose between kernels that give the results stated for the call, and
+ *     they may be changed from any thread. Two calls that share a workspace must not
  *     overlap in time on the device.
  *   - bf16 and f16 data are 16-bit IEEE bit patterns (bfloat16: top half of an fp32).
  */
@@ -64,7 +67,8 @@ enum {
  * scale    factor applied after the head sum
  * Sizes: B, n_q, H, D, n_kv >= 1, n_kv <= 2^30. q_dtype must equal k_dtype (F32, BF16 or F16).
  * bf16/f16 with D = 128 and H <= 32 run on MFMA; other shapes run a plain kernel that
- * needs H * D <= 16384.
+ * needs H * D <= 16384. Launch grid: B * n_q <= 65535, except on MFMA with n_q >= 8 (the
+ * prefill kernel), where B <= 65535; larger shapes return DSA_ERR_UNSUPPORTED.
  */
 int dsa_index_score(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
                     const int32_t* q_pos, float* scores, int B, int n_q, int H, int D, int n_kv,
@@ -135,7 +139,7 @@ int dsa_topk(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, v
  *            same B, n_q, Hm, top_k, d_latent, n_split (NULL allowed when that is 0)
  * dtype: F32 or BF16. BF16 with Hm a multiple of 16 (<= 64), d_latent = 512 and
  * d_rope in {0, 64} runs on MFMA; other shapes run a plain kernel that needs
- * Dc <= 1024 and d_latent <= 1024.
+ * Dc <= 1024, d_latent <= 1024 and B * n_q <= 65535 (DSA_ERR_UNSUPPORTED otherwise).
  */
 int dsa_sparse_mla_num_splits(int B, int n_q, int top_k);
 size_t dsa_sparse_mla_workspace_size(int B, int n_q, int Hm, int top_k, int d_latent, int n_split);
@@ -207,7 +211,8 @@ int dsa_topk_source_layer(int layer);
  * "mla_head_split": run each query's 64 heads as two 32-head workgroups sharing the query's
  * selected rows (0 = automatic: when 64-head workgroups would fill at most half of the 256
  * CUs; 1 = never; 2 = always for 64 heads). Returns DSA_OK,
- * or DSA_ERR_SHAPE for an unknown key or value. Process-wide; set it before launching work.
+ * or DSA_ERR_SHAPE for an unknown key or value. The switches are process-wide state (atomic);
+ * every call reads the ones it uses once, when it starts, so a change applies to later calls.
  */
 int dsa_set_tuning(const char* key, int value);
 

@@ -80,24 +80,24 @@ int dsa_set_tuning(const char* key, int value) {
   }
   if (std::strcmp(key, "score_chunks_per_wave") == 0) {
     if (value < 0 || value > 64) return fail(DSA_ERR_SHAPE, "score_chunks_per_wave must be 0..64 (got %d)", value);
-    dsa::g_score_cpw = value;
+    dsa::g_score_cpw.store(value);
     return ok();
   }
   if (std::strcmp(key, "score_prefill_waves") == 0) {
     if (value != 0 && value != 4 && value != 8)
       return fail(DSA_ERR_SHAPE, "score_prefill_waves must be 0, 4 or 8 (got %d)", value);
-    dsa::g_score_prefill_waves = value;
+    dsa::g_score_prefill_waves.store(value);
     return ok();
   }
   if (std::strcmp(key, "mla_tiles_per_step") == 0) {
     if (value != 1 && value != 2)
       return fail(DSA_ERR_SHAPE, "mla_tiles_per_step must be 1 or 2 (got %d)", value);
-    dsa::g_mla_tiles_per_step = value;
+    dsa::g_mla_tiles_per_step.store(value);
     return ok();
   }
   if (std::strcmp(key, "mla_head_split") == 0) {
     if (value < 0 || value > 2) return fail(DSA_ERR_SHAPE, "mla_head_split must be 0, 1 or 2 (got %d)", value);
-    dsa::g_mla_head_split = value;
+    dsa::g_mla_head_split.store(value);
     return ok();
   }
   return fail(DSA_ERR_SHAPE, "dsa_set_tuning: unknown key '%s'", key);
@@ -118,6 +118,11 @@ static int index_score_checked(const char* fn, const void* q, const void* k_cach
   if (q_dtype != k_dtype)
     return fail(DSA_ERR_DTYPE, "%s: q_dtype (%d) must equal k_dtype (%d)", fn, q_dtype, k_dtype);
   const bool mfma = D == 128 && H <= 32 && q_dtype != DSA_F32;
+  // grid limits: the decode and plain kernels put B * n_q on the grid's y dimension, the
+  // prefill kernel (16-bit, D = 128, n_q >= 8) puts B on its z dimension
+  if ((mfma && n_q >= 8) ? B > 65535 : (long long)B * n_q > 65535)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: B=%d n_q=%d exceed the launch grid (%s <= 65535)", fn, B, n_q,
+                (mfma && n_q >= 8) ? "B" : "B * n_q");
   if (mfma && (!aligned16(q) || !aligned16(k_cache)))
     return fail(DSA_ERR_UNSUPPORTED, "%s: q and k_cache must be 16-byte aligned", fn);
   if (!mfma && (long long)H * D > 16384)
@@ -202,6 +207,9 @@ int dsa_sparse_mla_attn(const void* q_abs, const void* latent, const int32_t* id
                   chunk, (top_k + 2047) / 2048);
     if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out))
       return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_mla_attn: q_abs, latent and out must be 16-byte aligned");
+  } else if ((long long)B * n_q > 65535) {
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_mla_attn: B * n_q = %lld exceeds the plain kernel's launch grid "
+                "(<= 65535 outside the MFMA shape)", (long long)B * n_q);
   } else if (d_latent + d_rope > 1024 || d_latent > 1024) {
     return fail(DSA_ERR_UNSUPPORTED,
                 "dsa_sparse_mla_attn: d_latent + d_rope = %d exceeds 1024 outside the MFMA shape "

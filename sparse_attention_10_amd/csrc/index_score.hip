@@ -19,8 +19,8 @@
 
 namespace dsa {
 
-int g_score_cpw = 0;            // 64-key chunks per wave of the decode kernel (0 automatic)
-int g_score_prefill_waves = 0;  // waves per block of the prefill kernel (0 automatic)
+std::atomic<int> g_score_cpw{0};            // 64-key chunks per wave of the decode kernel (0 automatic)
+std::atomic<int> g_score_prefill_waves{0};  // waves per block of the prefill kernel (0 automatic)
 constexpr int kPrefillWaves = 8;
 
 // Attention-sink range [lo, hi) of sequence b (ik_llama_opt log, "per-sequence attention sink"
@@ -456,7 +456,8 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
                               const int* q_pos, float* scores, int B, int n_q, int H, int n_kv,
                               float scale, ScoreArgs sink, hipStream_t stream) {
   if (n_q >= 8) {
-    const int nwv = g_score_prefill_waves > 0 ? g_score_prefill_waves : kPrefillWaves;
+    const int tuned = g_score_prefill_waves.load(std::memory_order_relaxed);
+    const int nwv = tuned > 0 ? tuned : kPrefillWaves;
     const int qb = nwv * kPreQPW;
     const int qblocks = (n_q + qb - 1) / qb;
     int spans = 2048 / max(1, qblocks * B);
@@ -482,7 +483,8 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
     const long rows = (long)B * n_q;
     // about 2048 blocks: short-lived waves of two chunks each measured fastest (more
     // independent streams in flight than a few long-lived waves)
-    long want = g_score_cpw > 0 ? g_score_cpw : (chunks * rows) / 2048;
+    const int cpw = g_score_cpw.load(std::memory_order_relaxed);
+    long want = cpw > 0 ? cpw : (chunks * rows) / 2048;
     const int iters = want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
     const long xblocks = (chunks + iters - 1) / iters;
     dim3 grid((unsigned)xblocks, (unsigned)rows);

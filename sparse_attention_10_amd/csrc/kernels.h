@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+
+#include <atomic>
 #include <stdint.h>
 
 namespace dsa {
@@ -20,8 +22,9 @@ struct ScoreArgs {
   int kpool;
 };
 
-extern int g_score_cpw;  // 64-key chunks per wave of the decode scoring kernel, 0 automatic
-extern int g_score_prefill_waves;  // waves per block of the prefill scoring kernel (4 or 8), 0 automatic
+// Tuning switches (dsa_set_tuning): process-wide, each read once per call.
+extern std::atomic<int> g_score_cpw;            // 64-key chunks per wave of the decode scoring kernel, 0 automatic
+extern std::atomic<int> g_score_prefill_waves;  // waves per block of the prefill scoring kernel (4 or 8), 0 automatic
 hipError_t launch_index_score(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int D,
                               int n_kv, int dtype, float scale, ScoreArgs sink, hipStream_t stream);
@@ -39,8 +42,8 @@ hipError_t launch_topk(const float* scores, int* idx, int rows, int n_kv, int to
                        const TopkPlan& plan, void* workspace, hipStream_t stream);
 
 // sparse MLA
-extern int g_mla_tiles_per_step;  // 16-row tiles per step of the 16-bit MLA kernel (1 or 2, default 2)
-extern int g_mla_head_split;      // 64 heads as two 32-head workgroup rows: 0 automatic, 1 never, 2 always
+extern std::atomic<int> g_mla_tiles_per_step;  // 16-row tiles per step of the 16-bit MLA kernel (1 or 2, default 2)
+extern std::atomic<int> g_mla_head_split;      // 64 heads as two 32-head workgroup rows: 0 automatic, 1 never, 2 always
 int mla_auto_splits(int B, int n_q, int top_k);
 size_t mla_workspace_bytes(int B, int n_q, int Hm, int top_k, int d_latent, int n_split);
 bool mla_mfma_supported(int Hm, int d_latent, int d_rope, int dtype);

@@ -881,14 +881,14 @@ __global__ __launch_bounds__(256) void mla_merge(const float* __restrict__ ws_o,
 // ---------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-int g_mla_tiles_per_step = 2;
-int g_mla_head_split = 0;
+std::atomic<int> g_mla_tiles_per_step{2};
+std::atomic<int> g_mla_head_split{0};
 
 // Workgroup rows per query of the MFMA kernel: 2 (32 heads each) when 64 heads would leave
 // at least half of the 256 CUs without a workgroup, else 1. Partials keep the same bytes.
-static int mla_head_split(int Hm, long rows, int n_split) {
-  if (Hm != 64 || g_mla_head_split == 1) return 1;
-  if (g_mla_head_split == 2) return 2;
+static int mla_head_split(int Hm, long rows, int n_split, int tuned) {
+  if (Hm != 64 || tuned == 1) return 1;
+  if (tuned == 2) return 2;
   return rows * n_split <= 128 ? 2 : 1;
 }  // measured faster on every workload (fewer barrier steps)
 
@@ -934,15 +934,17 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
     ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                      align256((size_t)rows * n_split * hpad * d_latent * sizeof(float)));
   }
+  // the tuning switches are read once, so the attention kernel and its merge agree on the layout
+  const int hs = mla_head_split(Hm, rows, n_split, g_mla_head_split.load(std::memory_order_relaxed));
+  const int tps = g_mla_tiles_per_step.load(std::memory_order_relaxed);
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
-    const int hs = mla_head_split(Hm, rows, n_split);
     const int Hk = Hm / hs;  // heads per workgroup row; the [query][head] arrays are read as [query * hs][Hk]
     const unsigned blocks = (unsigned)(rows * hs * n_split);
     // the pooled-indexer slots (kp) run with two tiles per step whatever the tuning
     auto kernel = kp
         ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2, true> : sparse_mla_mfma<64, 1, 2, true>)
                         : (Hk > 32 ? sparse_mla_mfma<0, 2, 2, true> : sparse_mla_mfma<0, 1, 2, true>))
-        : g_mla_tiles_per_step == 2
+        : tps == 2
         ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2> : sparse_mla_mfma<64, 1, 2>)
                         : (Hk > 32 ? sparse_mla_mfma<0, 2, 2> : sparse_mla_mfma<0, 1, 2>))
         : (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 1> : sparse_mla_mfma<64, 1, 1>)
@@ -974,7 +976,6 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
-    const int hs = mla_head_split(Hm, rows, n_split);
     const int n_ht = (Hm / hs + 31) / 32;
     const long total = rows * hs * n_ht * kFragSlots;
     hipLaunchKernelGGL(mla_merge_frag, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws_o,

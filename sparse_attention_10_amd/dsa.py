@@ -97,6 +97,22 @@ def _dev(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _opt(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape) -> None:
+    """An optional device tensor of exactly this dtype and shape (or None)."""
+    if t is None:
+        return
+    _dev(t, name)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)} (got {t.dtype} {tuple(t.shape)})")
+
+
+def _workspace_bytes(workspace: Optional[torch.Tensor]) -> int:
+    if workspace is None:
+        return 0
+    _dev(workspace, "workspace")
+    return workspace.numel() * workspace.element_size()
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -119,11 +135,8 @@ def dsa_index_score(q: torch.Tensor, k_cache: torch.Tensor, w: torch.Tensor, sco
         raise ValueError("dsa_index_score: inconsistent shapes")
     if w.dtype != torch.float32 or scores.dtype != torch.float32:
         raise ValueError("w and scores must be float32")
-    for t, n in ((kv_len, "kv_len"), (q_pos, "q_pos")):
-        if t is not None:
-            _dev(t, n)
-            if t.dtype != torch.int32:
-                raise ValueError(f"{n} must be int32")
+    _opt(kv_len, "kv_len", torch.int32, (B,))
+    _opt(q_pos, "q_pos", torch.int32, (B, n_q))
     if n_sink:
         if sink_start is not None:
             _dev(sink_start, "sink_start")
@@ -156,7 +169,7 @@ def dsa_topk(scores: torch.Tensor, idx: torch.Tensor, top_k: int,
     need = dsa_topk_workspace_size(rows, n_kv, top_k)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wbytes = _workspace_bytes(workspace)
     _check(lib.dsa_topk(scores.data_ptr(), idx.data_ptr(), rows, n_kv, top_k, _ptr(workspace), wbytes,
                         _stream(stream)), "dsa_topk")
     return idx
@@ -186,14 +199,12 @@ def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, idx: torch.Te
         raise ValueError("dsa_sparse_mla_attn: inconsistent shapes or dtypes")
     if idx.dtype != torch.int32 or out.dtype != torch.float32:
         raise ValueError("idx must be int32 and out float32")
-    if lse is not None:
-        _dev(lse, "lse")
-    if kv_len is not None:
-        _dev(kv_len, "kv_len")
+    _opt(lse, "lse", torch.float32, (B, n_q, Hm))
+    _opt(kv_len, "kv_len", torch.int32, (B,))
     need = dsa_sparse_mla_workspace_size(B, n_q, Hm, top_k, d_latent, n_split)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_abs.device)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wbytes = _workspace_bytes(workspace)
     _check(lib.dsa_sparse_mla_attn(q_abs.data_ptr(), latent.data_ptr(), idx.data_ptr(), _ptr(kv_len),
                                    out.data_ptr(), _ptr(lse), B, n_q, Hm, n_kv, top_k, d_latent,
                                    Dc - d_latent, float(sm_scale), _DTYPE[q_abs.dtype], int(n_split),
@@ -268,13 +279,6 @@ def dsa_set_tuning(key: str, value: int) -> None:
     _check(lib.dsa_set_tuning(key.encode(), int(value)), "dsa_set_tuning")
 
 
-def _int32_opt(t: Optional[torch.Tensor], name: str) -> None:
-    if t is not None:
-        _dev(t, name)
-        if t.dtype != torch.int32:
-            raise ValueError(f"{name} must be int32")
-
-
 def dsa_kpool_compress(packed: torch.Tensor, ape: torch.Tensor, pooled: torch.Tensor, D: int, kpool: int,
                        pool_begin: int = 0, pool_end: Optional[int] = None, stream=None) -> torch.Tensor:
     """packed [B][n_kv][row_stride] (k | gate | valid, row_stride >= 2 D + 1), ape [kpool][D] fp32,
@@ -303,8 +307,8 @@ def dsa_kpool_index_score(q: torch.Tensor, pooled: torch.Tensor, w: torch.Tensor
     if tuple(pooled.shape) != (B, n_pool, D) or tuple(w.shape) != (B, n_q, H) \
             or tuple(scores.shape) != (B, n_q, n_pool) or w.dtype != torch.float32 or scores.dtype != torch.float32:
         raise ValueError("dsa_kpool_index_score: inconsistent shapes or dtypes")
-    _int32_opt(kv_len, "kv_len")
-    _int32_opt(q_pos, "q_pos")
+    _opt(kv_len, "kv_len", torch.int32, (B,))
+    _opt(q_pos, "q_pos", torch.int32, (B, n_q))
     _check(lib.dsa_kpool_index_score(q.data_ptr(), pooled.data_ptr(), w.data_ptr(), _ptr(kv_len), _ptr(q_pos),
                                      scores.data_ptr(), B, n_q, H, D, n_pool, int(kpool), _DTYPE[q.dtype],
                                      _DTYPE[pooled.dtype], float(scale), _stream(stream)), "dsa_kpool_index_score")
@@ -323,8 +327,8 @@ def dsa_kpool_expand(pool_idx: torch.Tensor, packed: torch.Tensor, D: int, tok_i
     if pool_idx.dtype != torch.int32 or tok_idx.dtype != torch.int32 or packed.shape[0] != B \
             or tuple(tok_idx.shape) != (B, n_q, kpool * top_pools + kpool - 1):
         raise ValueError("dsa_kpool_expand: inconsistent shapes or dtypes")
-    _int32_opt(kv_len, "kv_len")
-    _int32_opt(q_pos, "q_pos")
+    _opt(kv_len, "kv_len", torch.int32, (B,))
+    _opt(q_pos, "q_pos", torch.int32, (B, n_q))
     _check(lib.dsa_kpool_expand(pool_idx.data_ptr(), packed.data_ptr(), stride, _DTYPE[packed.dtype], D,
                                 _ptr(kv_len), _ptr(q_pos), tok_idx.data_ptr(), B, n_q, n_kv, top_pools, int(kpool),
                                 _stream(stream)), "dsa_kpool_expand")
@@ -351,15 +355,14 @@ def dsa_kpool_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, pool_id
         raise ValueError("dsa_kpool_sparse_mla_attn: inconsistent shapes or dtypes")
     if pool_idx.dtype != torch.int32 or out.dtype != torch.float32:
         raise ValueError("pool_idx must be int32 and out float32")
-    if lse is not None:
-        _dev(lse, "lse")
-    _int32_opt(kv_len, "kv_len")
-    _int32_opt(q_pos, "q_pos")
+    _opt(lse, "lse", torch.float32, (B, n_q, Hm))
+    _opt(kv_len, "kv_len", torch.int32, (B,))
+    _opt(q_pos, "q_pos", torch.int32, (B, n_q))
     width = kpool * top_pools + kpool - 1
     need = dsa_sparse_mla_workspace_size(B, n_q, Hm, width, d_latent, n_split)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_abs.device)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wbytes = _workspace_bytes(workspace)
     _check(lib.dsa_kpool_sparse_mla_attn(q_abs.data_ptr(), latent.data_ptr(), pool_idx.data_ptr(), packed.data_ptr(),
                                          packed.shape[2], _DTYPE[packed.dtype], D, _ptr(kv_len), _ptr(q_pos),
                                          out.data_ptr(), _ptr(lse), B, n_q, Hm, n_kv, top_pools, int(kpool),

@@ -286,3 +286,27 @@ def test_kpool_sparse_mla_validation(lib):
     need = lib.dsa_sparse_mla_workspace_size(2, 1, 64, 4 * 512 + 3, 512, 8)
     assert need > 0
     assert _kpmla(lib, wsb=need - 1) == E_WS
+
+
+def test_launch_grid_limits_rejected_on_host(lib):
+    # decode / plain score kernels: B * n_q on the grid's y dimension
+    assert _score(lib, B=65536, n_q=1) == E_UNSUP
+    assert b"launch grid" in lib.dsa_last_error()
+    assert _score(lib, B=16384, n_q=4) == E_UNSUP
+    assert _score(lib, B=70000, n_q=1, qd=0, kd=0) == E_UNSUP         # plain kernel
+    # prefill kernel (16-bit, D = 128, n_q >= 8): B on the grid's z dimension
+    # (only rejected calls here: an accepted one would launch on the fake pointers)
+    assert _score(lib, B=65536, n_q=8) == E_UNSUP
+    # plain MLA kernel: B * n_q on the grid's y dimension
+    assert _mla(lib, B=65536, Hm=8, dl=64, dr=0, dtype=0, top_k=16) == E_UNSUP
+    assert b"launch grid" in lib.dsa_last_error()
+
+
+def test_tuning_is_read_once_per_call_source():
+    """The head-split switch is read once per attention call, so the kernel and its merge
+    always agree on the layout (a source check: the switch's only reads are at the call's
+    start)."""
+    src = open(os.path.join(ROOT, "sparse_attention_10_amd", "csrc", "sparse_mla.hip")).read()
+    assert src.count("g_mla_head_split.load") == 1
+    assert src.count("g_mla_tiles_per_step.load") == 1
+    assert "mla_head_split(Hm, rows, n_split)" not in src
