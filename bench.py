@@ -5,12 +5,18 @@ dsa_topk -> dsa_sparse_mla_attn on the batched-decode workload (32 sequences x
 32768 cached rows, 32 indexer heads x 128, top-k 2048, 64 MLA heads over a 576-wide
 bf16 latent cache), inputs resident in HBM. Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode graph|eager]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layers L]
 
-value = decode tokens/s (sequences per step / step time). The roofline object is for
-the dominant kernel (the indexer-score kernel, HBM-bound): algorithmic bytes per launch
-/ its average duration measured with HIP events on the launch stream over the timed
-region. cpu_baseline is the CPU oracle timed on a bounded sample of the same workload.
+value = decode tokens/s (sequences per step / step time), with the steps rotating over L
+layers (default 4) that each hold their own key and latent caches, as consecutive layers of
+a model do, so no step finds its keys left in the 256 MB Infinity Cache by the step before;
+the same figures with every step on one layer are reported beside them. The roofline
+object is for the dominant kernel (the indexer-score kernel, HBM-bound): algorithmic bytes
+per launch / its average duration measured with HIP events on the launch stream over the
+rotating steps. The chunked-prefill leg reports the scoring kernel against the bf16 MFMA
+peak, the long-decode leg the 8 x 128K step against the HBM peak. cpu_baseline is the CPU
+oracle timed on a bounded sample of the same workload, in processes over independent
+sequences.
 """
 from __future__ import annotations
 
@@ -130,7 +136,8 @@ def write_traffic(wl_name, fetch_csv, write_csv, copy_mib):
 
 
 def kpool_bytes(wl, width):
-    """Algorithmic bytes of one pooled-indexer decode step: pool keys, q, w, the pool scores
+    """Algorithmic bytes of one pooled-indexer decode step (the one-pool compression is added by
+    the caller): pool keys, q, w, the pool scores
     written and read, pool indices written and read, the valid entries of the selected tokens,
     token indices written and read, the absorbed query, the selected latent rows, out, lse."""
     rows = wl.B * wl.n_q
@@ -204,6 +211,12 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
                                                       kv_len=kv_len, n_split=ns, workspace=ws_m),
     }
 
+    # a decode step also compresses the pool its new token completes (the last pool here)
+    compress_one = lambda: dsa.dsa_kpool_compress(packed, ape, pooled, D, kpool, pool_begin=n_pool - 1,  # noqa: E731
+                                                  pool_end=n_pool)
+    calls = {"compress": compress_one, **calls}
+    two_calls = {"compress": compress_one, **two_calls}
+
     def kstep():
         for f in calls.values():
             f()
@@ -258,8 +271,12 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
     two_s = graph_time(kstep_two)
     ab = kpool_bytes(wl, width)
     ab["sparse_mla"] = ab["fused_sparse_mla"]
+    # the one-pool compression: each sequence's 4 packed rows read, its pool key written
+    ab["compress"] = B * (kpool * (2 * D + 1) * 2 + D * 2)
+    ab["fused_step"] += ab["compress"]
     return {"workload": wl.name, "B": B, "n_kv": n_kv, "kpool": kpool, "top_k_tokens": wl.top_k,
             "pools_selected": kp, "attended_width": width, "d_rope": wl.d_rope, "indexer_dtype": "f16",
+            "step": "compress the completed pool, pool scores, top-k over pools, attention with the expansion",
             "ms_per_step": round(step_s * 1e3, 4), "tokens_per_s": round(B / step_s, 1),
             "step_algorithmic_bytes": ab["fused_step"], "step_hbm_gbs": round(ab["fused_step"] / step_s / 1e9, 1),
             "step_hbm_frac": round(ab["fused_step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -271,37 +288,249 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
                                    "frac": round(compress_b / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
-def cpu_baseline(wl, inp, seconds_target=15.0):
-    """The oracle chain on whole sequences of the workload, cycling over the batch, until about
-    seconds_target of work."""
-    import numpy as np
+def _oracle_chain_worker(args):
+    """One CPU worker of the oracle baseline: the oracle chain on whole sequences b0, b0 + stride,
+    ... (cycling over the batch) until `seconds` have passed, with BLAS held to one thread.
+    Returns the number of sequences done and the seconds taken."""
+    wl_name, b0, stride, seconds = args
+    import threadpoolctl
     import oracle
-    try:
-        import threadpoolctl
-        cores = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) \
-            if threadpoolctl.threadpool_info() else 1
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
-    done = 0
+    import workloads
+    wl = workloads.WORKLOADS[wl_name]
+    inp = _CPU_INPUTS
+    done, b = 0, b0
+    with threadpoolctl.threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            sl = slice(b, b + 1)
+            S = oracle.index_score(inp["q"][sl], inp["k"][sl], inp["w"][sl], inp["kv_len"][sl],
+                                   inp["q_pos"][sl] if wl.q_pos_start is not None else None,
+                                   wl.scale, wl.idx_dtype, wl.idx_dtype)
+            idx = oracle.topk(S.reshape(-1, wl.n_kv), wl.top_k).reshape(1, wl.n_q, wl.top_k)
+            oracle.sparse_mla(inp["qa"][sl], inp["latent"][sl], idx, wl.sm_scale, wl.d_latent, wl.mla_dtype,
+                              inp["kv_len"][sl])
+            done += 1
+            b = (b + stride) % wl.B
+            if time.perf_counter() - t0 > seconds:
+                break
+        return done, time.perf_counter() - t0
+
+
+_CPU_INPUTS = None  # the workload's host inputs, inherited by the forked workers
+
+
+def cpu_baseline(wl, inp, seconds_target=15.0, workers=None):
+    """The oracle (as it stands: float64 numpy, one BLAS thread per process) timed on the host's
+    cores: `workers` processes run the oracle chain on independent sequences of the workload
+    (the unit the method is data-parallel over) for about seconds_target each. Forked before
+    the GPU is touched. tokens/s = sequences done x queries per sequence / wall time."""
+    import multiprocessing
+    global _CPU_INPUTS
+    _CPU_INPUTS = inp
+    host = os.cpu_count() or 1
+    # a one-GPU box's CPU share is 16 cores whatever the host reports
+    P = workers if workers else max(1, min(16, host))
+    ctx = multiprocessing.get_context("fork")
     t0 = time.perf_counter()
-    while True:
-        b = done % wl.B
-        sl = slice(b, b + 1)
-        sub = {k: v[sl] for k, v in inp.items() if k != "kv_len"}
-        sub["kv_len"] = inp["kv_len"][sl]
-        S = oracle.index_score(sub["q"], sub["k"], sub["w"], sub["kv_len"], sub["q_pos"] if wl.q_pos_start is not None else None,
-                               wl.scale, wl.idx_dtype, wl.idx_dtype)
-        idx = oracle.topk(S.reshape(-1, wl.n_kv), wl.top_k).reshape(1, wl.n_q, wl.top_k)
-        oracle.sparse_mla(sub["qa"], sub["latent"], idx, wl.sm_scale, wl.d_latent, wl.mla_dtype, sub["kv_len"])
-        done += 1
-        if time.perf_counter() - t0 > seconds_target:
-            break
-    dt = time.perf_counter() - t0
+    with ctx.Pool(P) as pool:
+        res = pool.map(_oracle_chain_worker, [(wl.name, j % wl.B, P, seconds_target) for j in range(P)])
+    wall = time.perf_counter() - t0
+    done = sum(r[0] for r in res)
+    busy = max(r[1] for r in res)
     tokens = done * wl.n_q
-    seqs = f"sequences 0..{done - 1}" if done <= wl.B else f"{done} sequences ({done / wl.B:.1f} passes over the {wl.B})"
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle chain (score, top-k, sparse MLA) on {seqs} of {wl.name} "
-                      f"({tokens} tokens, {dt:.1f} s, float64 numpy with {cores} BLAS threads)"}
+    return {"value": tokens / busy, "unit": "tokens/s", "cores": P, "kind": "oracle",
+            "host_cpus": host,
+            "sample": f"oracle chain (score, top-k, sparse MLA; float64 numpy, one BLAS thread each) in "
+                      f"{P} processes over independent sequences of {wl.name}: {done} sequences "
+                      f"({done / wl.B:.1f} passes over the {wl.B}), {tokens} tokens in {busy:.1f} s "
+                      f"({wall:.1f} s with process start)"}
+
+
+class Chain:
+    """The three calls of one DSA step over one batch, with its outputs and workspaces, for a
+    set of layers that each hold their own key and latent caches (the same shapes; the other
+    inputs are shared). step(l) runs layer l."""
+
+    def __init__(self, dsa, wl, dev, q, w, qa, kv_len, q_pos, keys, lats):
+        import torch
+        self.dsa, self.wl = dsa, wl
+        self.q, self.w, self.qa, self.kv_len, self.q_pos = q, w, qa, kv_len, q_pos
+        self.keys, self.lats = keys, lats
+        rows = wl.B * wl.n_q
+        self.scores = torch.empty((wl.B, wl.n_q, wl.n_kv), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((wl.B, wl.n_q, wl.top_k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((wl.B, wl.n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((wl.B, wl.n_q, wl.Hm), dtype=torch.float32, device=dev)
+        self.n_split = dsa.dsa_sparse_mla_num_splits(wl.B, wl.n_q, wl.top_k)
+        self.ws_t = torch.empty(max(1, dsa.dsa_topk_workspace_size(rows, wl.n_kv, wl.top_k)), dtype=torch.uint8,
+                                device=dev)
+        self.ws_m = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(wl.B, wl.n_q, wl.Hm, wl.top_k, wl.d_latent,
+                                                                         self.n_split)),
+                                dtype=torch.uint8, device=dev)
+
+    @property
+    def layers(self):
+        return len(self.keys)
+
+    def score(self, l):
+        self.dsa.dsa_index_score(self.q, self.keys[l], self.w, self.scores, kv_len=self.kv_len, q_pos=self.q_pos,
+                                 scale=self.wl.scale)
+
+    def topk(self, l):
+        self.dsa.dsa_topk(self.scores, self.idx, self.wl.top_k, workspace=self.ws_t)
+
+    def mla(self, l):
+        wl = self.wl
+        self.dsa.dsa_sparse_mla_attn(self.qa, self.lats[l], self.idx, self.out, wl.d_latent, wl.sm_scale,
+                                     lse=self.lse, kv_len=self.kv_len, n_split=self.n_split, workspace=self.ws_m)
+
+    def step(self, l):
+        self.score(l)
+        self.topk(l)
+        self.mla(l)
+
+
+def time_calls(chain, steps, layer_of):
+    """Average duration (ms) of each call over `steps` eager steps, from HIP events recorded on
+    the launch stream around every call; step s runs layer layer_of(s)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    names = ("index_score", "topk", "sparse_mla")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        l = layer_of(s)
+        ev[s][0].record(stream)
+        chain.score(l)
+        ev[s][1].record(stream)
+        chain.topk(l)
+        ev[s][2].record(stream)
+        chain.mla(l)
+        ev[s][3].record(stream)
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t0) / steps
+    per = {n: sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)) / steps for j, n in enumerate(names)}
+    return per, eager_s
+
+
+def graph_seconds(fn_steps, steps, warmup):
+    """Seconds per step of `steps` steps captured in one HIP graph (fn_steps(n) issues n steps)
+    and replayed once, after a warmup graph of `warmup` steps and one untimed replay."""
+    import torch
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn_steps(1)  # first calls outside capture
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        fn_steps(max(1, warmup))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn_steps(steps)
+    gw.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def device_inputs(wl, dev, seed, layers):
+    """Inputs of a workload drawn on the device from torch's seeded generator, with the
+    distributions of workloads.gen_all (indexer q and k N(0, 1) / sqrt(128), which a Hadamard
+    rotation leaves i.i.d. N(0, 1) / sqrt(128), so no rotation is drawn; weights U(0, 1) x
+    w_scale; absorbed query N(0, 1); latent N(0, latent_std)), for workloads whose host draw
+    would take minutes. Layers after the first hold copies of the first layer's caches at
+    their own addresses."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(seed * 1000 + wl.wid)
+    it = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}
+    s = wl.D ** -0.5
+    q = (torch.randn((wl.B, wl.n_q, wl.H, wl.D), generator=g, device=dev) * s).to(it[wl.idx_dtype])
+    k = (torch.randn((wl.B, wl.n_kv, wl.D), generator=g, device=dev) * s).to(it[wl.idx_dtype])
+    w = torch.rand((wl.B, wl.n_q, wl.H), generator=g, device=dev) * wl.w_scale
+    qa = torch.randn((wl.B, wl.n_q, wl.Hm, wl.Dc), generator=g, device=dev).to(it[wl.mla_dtype])
+    lat = torch.empty((wl.B, wl.n_kv, wl.Dc), dtype=it[wl.mla_dtype], device=dev)
+    for b in range(wl.B):  # per sequence, to bound the float32 temporary
+        lat[b] = (torch.randn((wl.n_kv, wl.Dc), generator=g, device=dev) * wl.latent_std).to(it[wl.mla_dtype])
+    kv_len = torch.full((wl.B,), wl.n_kv, dtype=torch.int32, device=dev)
+    q_pos = torch.from_numpy(wl.q_pos()).to(dev) if wl.q_pos_start is not None else None
+    keys = [k] + [k.clone() for _ in range(layers - 1)]
+    lats = [lat] + [lat.clone() for _ in range(layers - 1)]
+    return q, w, qa, kv_len, q_pos, keys, lats
+
+
+def decode_leg(dsa, chain, steps, warmup):
+    """Timings of a decode chain: eager per-call events and graph step times with the layers in
+    rotation, and the same with every step on layer 0."""
+    L = chain.layers
+    for s in range(max(1, warmup)):
+        chain.step(s % L)
+    per_rot, eager_s = time_calls(chain, steps, lambda s: s % L)
+    per_one, _ = time_calls(chain, steps, lambda s: 0)
+    step_rot = graph_seconds(lambda n: [chain.step(s % L) for s in range(n)], steps, warmup)
+    step_one = graph_seconds(lambda n: [chain.step(0) for s in range(n)], steps, warmup)
+    # a layer that reuses the last full layer's indices (IndexShare) runs the attention only
+    shared = graph_seconds(lambda n: [chain.mla(s % L) for s in range(n)], steps, warmup)
+    return {"per_rot": per_rot, "per_one": per_one, "eager_s": eager_s, "step_rot": step_rot,
+            "step_one": step_one, "shared": shared}
+
+
+def prefill_leg(dsa, dev, steps, warmup, seed):
+    """The chunked-prefill workload (4096 queries after 12288 cached rows): per-call events and
+    the graph step time. The scoring kernel is the MFMA-bound part: its causal flops per launch
+    over its event-measured duration, against the dense bf16 MFMA peak."""
+    import workloads
+    wl = workloads.CHUNKED_PREFILL_16K
+    ins = device_inputs(wl, dev, seed, 1)
+    chain = Chain(dsa, wl, dev, *ins)
+    n = max(3, steps // 20)
+    for _ in range(max(1, warmup // 10)):
+        chain.step(0)
+    per, _ = time_calls(chain, n, lambda s: 0)
+    step_s = graph_seconds(lambda m: [chain.step(0) for _ in range(m)], n, 1)
+    fl = score_flops(wl)
+    tfl = fl / (per["index_score"] * 1e-3) / 1e12
+    dense = score_flops(wl, causal=False) / (per["index_score"] * 1e-3) / 1e12
+    out = {"workload": wl.name, "n_q": wl.n_q, "n_kv": wl.n_kv, "q_pos_start": wl.q_pos_start,
+           "ms_per_step": round(step_s * 1e3, 4), "tokens_per_s": round(wl.n_q / step_s, 1),
+           "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
+           "score_roofline": {"bound": "mfma", "achieved": round(tfl, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "flops_per_launch": fl, "dense_equivalent_frac": round(dense / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "kernel": "index_score_prefill_mfma", "target_frac": 0.40},
+           "steps_timed": n, "inputs": "drawn on the device (torch generator), same distributions"}
+    del chain, ins
+    return out
+
+
+def long_decode_leg(dsa, dev, steps, warmup, seed, layers):
+    """The long-context decode workload (8 sequences x 131072 rows, f16 indexer keys) with its
+    layers' caches in rotation: step time, tokens/s, the step's algorithmic bytes against the
+    HBM peak, and the score kernel against it."""
+    import workloads
+    wl = workloads.LONG_DECODE_128K
+    chain = Chain(dsa, wl, dev, *device_inputs(wl, dev, seed, layers))
+    n = max(layers, steps // 4 // layers * layers)
+    t = decode_leg(dsa, chain, n, max(layers, warmup // 4))
+    ab = algorithmic_bytes(wl)
+    sc = ab["index_score"] / (t["per_rot"]["index_score"] * 1e-3) / 1e9
+    out = {"workload": wl.name, "B": wl.B, "n_kv": wl.n_kv, "layers_rotated": layers,
+           "ms_per_step": round(t["step_rot"] * 1e3, 4), "tokens_per_s": round(wl.B / t["step_rot"], 1),
+           "step_hbm_gbs": round(ab["step"] / t["step_rot"] / 1e9, 1),
+           "step_hbm_frac": round(ab["step"] / t["step_rot"] / 1e9 / HBM_PEAK_GBS, 4), "target_frac": 0.60,
+           "step_algorithmic_bytes": ab["step"],
+           "kernels_ms": {k_: round(v, 4) for k_, v in t["per_rot"].items()},
+           "score_roofline": {"bound": "hbm", "achieved": round(sc, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(sc / HBM_PEAK_GBS, 4), "bytes_per_launch": ab["index_score"]},
+           "single_layer_ms_per_step": round(t["step_one"] * 1e3, 4),
+           "steps_timed": n, "inputs": "drawn on the device (torch generator), same distributions"}
+    del chain
+    return out
 
 
 def main():
@@ -310,17 +539,20 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers whose caches the decode steps rotate over (0: 4 for decode workloads, 1 for "
+                         "prefill); with more than one, no step finds its layer's caches left in the caches "
+                         "by the step before")
     ap.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
                     help="dsa_set_tuning before the run (repeatable)")
-    ap.add_argument("--pipelines", type=int, default=1,
-                    help="run the step as this many chains over equal slices of the batch, each on its "
-                         "own stream, so one slice's latency-bound stages overlap another's streaming")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=0, help="processes of the oracle baseline (0: up to 16)")
     ap.add_argument("--no-kpool", action="store_true",
                     help="skip the pooled-indexer (kpool) decode leg of the bench line")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the chunked-prefill and long-decode legs of the bench line")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--scrub-mib", type=int, default=0,
                     help="also time eager steps with a buffer of this many MiB written between them "
                          "(steps that start with cold caches)")
@@ -344,16 +576,27 @@ def main():
     import numpy as np
     import torch
     import workloads
-    from sparse_attention_10_amd import dsa
 
-    for kv_ in args.tune:
-        key_, val_ = kv_.split("=")
-        dsa.dsa_set_tuning(key_, int(val_))
     wl = workloads.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
+    prefill = wl.n_q > 1
+    L = args.layers if args.layers > 0 else (1 if prefill else 4)
     t_gen = time.perf_counter()
     inp = workloads.gen_all(wl, args.seed)
     print(f"[bench] generated {wl.name} inputs in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle first, in processes forked before anything touches the GPU
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds, args.cpu_workers or None)
+        one = cpu_baseline(wl, inp, max(1.0, args.cpu_seconds / 3), 1)
+        cpu["single_process"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+        print(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} processes", file=sys.stderr,
+              flush=True)
+
+    from sparse_attention_10_amd import dsa
+    for kv_ in args.tune:
+        key_, val_ = kv_.split("=")
+        dsa.dsa_set_tuning(key_, int(val_))
+    dev = torch.device("cuda:0")
 
     def to_dev(a, code=None):
         a = np.ascontiguousarray(a)
@@ -370,140 +613,21 @@ def main():
     lat = to_dev(inp["latent"], wl.mla_dtype)
     kv_len = to_dev(inp["kv_len"])
     q_pos = to_dev(inp["q_pos"]) if wl.q_pos_start is not None else None
+    keys = [k] + [k.clone() for _ in range(L - 1)]
+    lats = [lat] + [lat.clone() for _ in range(L - 1)]
+    chain = Chain(dsa, wl, dev, q, w, qa, kv_len, q_pos, keys, lats)
+    n_split = chain.n_split
     rows = wl.B * wl.n_q
-    scores = torch.empty((wl.B, wl.n_q, wl.n_kv), dtype=torch.float32, device=dev)
-    idx = torch.empty((wl.B, wl.n_q, wl.top_k), dtype=torch.int32, device=dev)
-    out = torch.empty((wl.B, wl.n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device=dev)
-    lse = torch.empty((wl.B, wl.n_q, wl.Hm), dtype=torch.float32, device=dev)
-    n_split = dsa.dsa_sparse_mla_num_splits(wl.B, wl.n_q, wl.top_k)
-    ws_t = torch.empty(max(1, dsa.dsa_topk_workspace_size(rows, wl.n_kv, wl.top_k)), dtype=torch.uint8, device=dev)
-    ws_m = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(wl.B, wl.n_q, wl.Hm, wl.top_k, wl.d_latent, n_split)),
-                       dtype=torch.uint8, device=dev)
+    steps = args.steps // L * L if args.steps >= L else args.steps
     torch.cuda.synchronize()
-
-    def call_score():
-        dsa.dsa_index_score(q, k, w, scores, kv_len=kv_len, q_pos=q_pos, scale=wl.scale)
-
-    def call_topk():
-        dsa.dsa_topk(scores, idx, wl.top_k, workspace=ws_t)
-
-    def call_mla():
-        dsa.dsa_sparse_mla_attn(qa, lat, idx, out, wl.d_latent, wl.sm_scale, lse=lse, kv_len=kv_len,
-                                n_split=n_split, workspace=ws_m)
-
-    def step():
-        call_score()
-        call_topk()
-        call_mla()
-
-    # the step as P chains over batch slices on P streams (default priority), joined at the end
-    P = args.pipelines
-    if P < 1 or wl.B % P != 0:
-        print(f"--pipelines must divide B={wl.B}", file=sys.stderr)
-        sys.exit(2)
-    parts = []
-    if P > 1:
-        hb = wl.B // P
-        for p_ in range(P):
-            sl = slice(p_ * hb, (p_ + 1) * hb)
-            ns_p = dsa.dsa_sparse_mla_num_splits(hb, wl.n_q, wl.top_k)
-            parts.append({
-                "sl": sl, "ns": ns_p, "stream": torch.cuda.Stream(),
-                "ws_t": torch.empty(max(1, dsa.dsa_topk_workspace_size(hb * wl.n_q, wl.n_kv, wl.top_k)),
-                                    dtype=torch.uint8, device=dev),
-                "ws_m": torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(hb, wl.n_q, wl.Hm, wl.top_k,
-                                                                             wl.d_latent, ns_p)),
-                                    dtype=torch.uint8, device=dev)})
-
-    def pstep():
-        if P == 1:
-            step()
-            return
-        cur = torch.cuda.current_stream()
-        for part in parts:
-            sl, st = part["sl"], part["stream"]
-            st.wait_stream(cur)
-            with torch.cuda.stream(st):
-                dsa.dsa_index_score(q[sl], k[sl], w[sl], scores[sl], kv_len=kv_len[sl],
-                                    q_pos=q_pos[sl] if q_pos is not None else None, scale=wl.scale)
-                dsa.dsa_topk(scores[sl], idx[sl], wl.top_k, workspace=part["ws_t"])
-                dsa.dsa_sparse_mla_attn(qa[sl], lat[sl], idx[sl], out[sl], wl.d_latent, wl.sm_scale, lse=lse[sl],
-                                        kv_len=kv_len[sl], n_split=part["ns"], workspace=part["ws_m"])
-        for part in parts:
-            cur.wait_stream(part["stream"])
-
-    # warmup (also the eager reference of one step)
-    for _ in range(max(1, args.warmup)):
-        step()
-    torch.cuda.synchronize()
-
-    # per-call durations: HIP events on the launch stream around each call, eager, K steps
+    print(f"[bench] timing {wl.name}: {steps} steps over {L} layers", file=sys.stderr, flush=True)
+    t = decode_leg(dsa, chain, steps, args.warmup)
+    step_s = t["step_rot"]
+    per = t["per_rot"]
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        call_score()
-        ev[s][1].record(stream)
-        call_topk()
-        ev[s][2].record(stream)
-        call_mla()
-        ev[s][3].record(stream)
-    torch.cuda.synchronize()
-    eager_s = (time.perf_counter() - t0) / args.steps
-    per = {"index_score": 0.0, "topk": 0.0, "sparse_mla": 0.0}
-    for s in range(args.steps):
-        per["index_score"] += ev[s][0].elapsed_time(ev[s][1])
-        per["topk"] += ev[s][1].elapsed_time(ev[s][2])
-        per["sparse_mla"] += ev[s][2].elapsed_time(ev[s][3])
-    per = {k_: v / args.steps for k_, v in per.items()}  # ms
-
-    # the timed region: K steps, graph replay (launch overhead captured once) or eager
-    if args.mode == "graph":
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            pstep()  # first call outside capture
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            pstep()
-        for _ in range(max(1, args.warmup)):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
-        torch.cuda.synchronize()
-        step_s = (time.perf_counter() - t0) / args.steps
-        # a layer that shares the previous full layer's indices runs the attention only
-        gm = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gm):
-            call_mla()
-        for _ in range(max(1, args.warmup)):
-            gm.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            gm.replay()
-        torch.cuda.synchronize()
-        shared_s = (time.perf_counter() - t0) / args.steps
-    else:
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            pstep()
-        torch.cuda.synchronize()
-        step_s = (time.perf_counter() - t0) / args.steps
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            call_mla()
-        torch.cuda.synchronize()
-        shared_s = (time.perf_counter() - t0) / args.steps
 
     # indexer-input preparation of the step's new tokens (the stage upstream of the scores):
-    # timed on its own with HIP events, after the timed region, writing the same cache rows
+    # timed on its own, writing the same cache rows of layer 0
     prep_in = workloads.gen_prep(wl, args.seed)
     p_q = to_dev(prep_in["q_in"])
     p_k = to_dev(prep_in["k_in"])
@@ -517,33 +641,37 @@ def main():
 
     for _ in range(5):
         call_prep()
-    torch.cuda.synchronize()
-    # a few microseconds of GPU work per call: the host cannot queue single calls fast enough,
-    # so a graph of 20 calls is replayed and the time per call taken from that
-    pg = torch.cuda.CUDAGraph()
-    pside = torch.cuda.Stream()
-    pside.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(pside):
-        call_prep()
-    torch.cuda.current_stream().wait_stream(pside)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(pg):
-        for _ in range(20):
-            call_prep()
-    pg.replay()
-    torch.cuda.synchronize()
-    reps = max(1, args.steps // 20)
-    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    pe0.record(stream)
-    for _ in range(reps):
-        pg.replay()
-    pe1.record(stream)
-    torch.cuda.synchronize()
-    prep_ms = pe0.elapsed_time(pe1) / (reps * 20)
+    # a few microseconds of GPU work per call: a graph of the calls is replayed
+    prep_s = graph_seconds(lambda n: [call_prep() for _ in range(n)], max(20, steps // 2), 5)
+
+    scrub = None
+    if args.scrub_mib > 0:
+        buf = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device=dev)
+        se = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):  # the fill runs between the event pairs, outside them
+            buf.fill_(i & 255)
+            se[i][0].record(stream)
+            chain.step(0)
+            se[i][1].record(stream)
+        torch.cuda.synchronize()
+        scrub = {"scrub_mib": args.scrub_mib, "ms_per_step": round(sum(a.elapsed_time(b) for a, b in se) / steps, 4)}
+        del buf
 
     kpool = None
     if not args.no_kpool and wl.n_q == 1:
+        print("[bench] pooled-indexer leg", file=sys.stderr, flush=True)
         kpool = kpool_leg(dsa, dev, args.steps, args.warmup, args.seed)
+
+    legs = {}
+    if not args.no_legs:
+        del chain, keys, lats, q, k, w, qa, lat, p_q, p_k, p_lat, p_qout
+        torch.cuda.empty_cache()
+        print("[bench] chunked-prefill leg", file=sys.stderr, flush=True)
+        legs["chunked_prefill"] = prefill_leg(dsa, dev, args.steps, args.warmup, args.seed)
+        torch.cuda.empty_cache()
+        print("[bench] long-decode leg", file=sys.stderr, flush=True)
+        legs["long_decode"] = long_decode_leg(dsa, dev, args.steps, args.warmup, args.seed, 4)
+        torch.cuda.empty_cache()
 
     # a plain device-to-device copy of 1 GiB: the bandwidth a streaming kernel reaches here
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -558,31 +686,17 @@ def main():
     copy_gbs = 3 * 2 * (1 << 30) / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
     del csrc, cdst
 
-    scrub = None
-    if args.scrub_mib > 0:
-        buf = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device=dev)
-        se = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for i in range(args.steps):  # the fill runs between the event pairs, outside them
-            buf.fill_(i & 255)
-            se[i][0].record(stream)
-            step()
-            se[i][1].record(stream)
-        torch.cuda.synchronize()
-        tot = sum(a.elapsed_time(b) for a, b in se)
-        scrub = {"scrub_mib": args.scrub_mib, "ms_per_step": round(tot / args.steps, 4)}
-        del buf
-
     ab = algorithmic_bytes(wl)
     tokens = rows
     # IndexShare over GLM-5.2's 78 DSA layers: full layers run the whole step, shared layers
     # reuse the last full layer's indices and run the attention only
     n_full = sum(dsa.dsa_layer_computes_topk(l) for l in range(78))
-    per_layer_s = (n_full * step_s + (78 - n_full) * shared_s) / 78
+    per_layer_s = (n_full * step_s + (78 - n_full) * t["shared"]) / 78
     value = tokens / step_s
     score_ms = per["index_score"]
     achieved = ab["index_score"] / (score_ms * 1e-3) / 1e9
+    achieved_one = ab["index_score"] / (t["per_one"]["index_score"] * 1e-3) / 1e9
     traffic = load_traffic(wl.name)
-    prefill = wl.n_q > 1
     if prefill:
         fl = score_flops(wl)
         tfl = fl / (score_ms * 1e-3) / 1e12
@@ -593,13 +707,14 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "index_score_decode_mfma", "bytes_per_launch": ab["index_score"]}
+                "kernel": "index_score_decode_mfma", "bytes_per_launch": ab["index_score"],
+                "layers_rotated": L}
     result = {
         "metric": "DSA decode tokens/s at 32K ctx (batch 32) + achieved HBM GB/s vs peak",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True,
@@ -610,47 +725,46 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "n_q": wl.n_q, "n_kv": wl.n_kv, "H": wl.H, "D": wl.D,
                    "top_k": wl.top_k, "Hm": wl.Hm, "d_latent": wl.d_latent, "d_rope": wl.d_rope,
                    "indexer_dtype": workloads.DTYPE_NAMES[wl.idx_dtype],
-                   "latent_dtype": workloads.DTYPE_NAMES[wl.mla_dtype], "mode": args.mode,
-                   "mla_splits": n_split, "pipelines": P, "tuning": args.tune, "parallelism": "single GPU"},
+                   "latent_dtype": workloads.DTYPE_NAMES[wl.mla_dtype], "mode": "graph",
+                   "layers_rotated": L, "mla_splits": n_split,
+                   "tuning": args.tune, "parallelism": "single GPU"},
         "step_hbm_gbs": round(ab["step"] / step_s / 1e9, 1),
         "step_hbm_frac": round(ab["step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": ab["step"],
-        "eager_ms_per_step": round(eager_s * 1e3, 4),
+        "eager_ms_per_step": round(t["eager_s"] * 1e3, 4),
         "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
         "kernels_gbs": {k_: round(ab[k_] / (per[k_] * 1e-3) / 1e9, 1) for k_ in per},
         "roofline": roof,
+        "single_layer": {"ms_per_step": round(t["step_one"] * 1e3, 4),
+                         "tokens_per_s": round(tokens / t["step_one"], 1),
+                         "kernels_ms": {k_: round(v, 4) for k_, v in t["per_one"].items()},
+                         "score_gbs": round(achieved_one, 1),
+                         "score_frac": round(achieved_one / HBM_PEAK_GBS, 4) if not prefill else None,
+                         "note": "every step on one layer's caches, which partly stay in the 256 MB "
+                                 "Infinity Cache between steps"},
         "indexshare": {"full_layers": n_full, "shared_layers": 78 - n_full,
-                       "shared_layer_ms": round(shared_s * 1e3, 4),
+                       "shared_layer_ms": round(t["shared"] * 1e3, 4),
                        "ms_per_layer": round(per_layer_s * 1e3, 4),
                        "tokens_per_s_per_layer": round(tokens / per_layer_s, 1)},
         "copy_gbs": round(copy_gbs, 1),
         "score_frac_of_copy": round(achieved / copy_gbs, 4) if not prefill else None,
-        "indexer_prep": {"ms": round(prep_ms, 4), "bytes": prep_bytes(wl),
-                         "gbs": round(prep_bytes(wl) / (prep_ms * 1e-3) / 1e9, 1),
-                         "frac": round(prep_bytes(wl) / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "indexer_prep": {"ms": round(prep_s * 1e3, 4), "bytes": prep_bytes(wl),
+                         "gbs": round(prep_bytes(wl) / prep_s / 1e9, 1),
+                         "frac": round(prep_bytes(wl) / prep_s / 1e9 / HBM_PEAK_GBS, 4),
                          "tokens": rows},
         "context": "whole-model figures on other hardware (not comparable): GLM-5.2 IQ2_XXS greedy decode "
                    "~0.3-0.4 tokens/s and 200-token prefill ~3.2 tokens/s on an RTX 4060 Ti 16GB with SSD "
                    "expert streaming",
     }
+    result.update(legs)
     if kpool is not None:
         result["kpool"] = kpool
     if scrub is not None:
         result["cold_cache_eager"] = scrub
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
-        # the same oracle on one thread (BLAS limited to 1), a shorter sample
-        try:
-            import threadpoolctl
-            with threadpoolctl.threadpool_limits(limits=1):
-                one = cpu_baseline(wl, inp, max(1.0, args.cpu_seconds / 3))
-            result["cpu_baseline"]["single_thread"] = {"value": one["value"], "unit": one["unit"],
-                                                       "cores": one["cores"], "sample": one["sample"]}
-        except ImportError:
-            pass
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
     if args.copy_calibration_mib > 0:
-        del q, k, w, qa, lat, scores, idx, out, lse, ws_t, ws_m, p_q, p_k, p_lat, p_qout
         n = args.copy_calibration_mib * 1024 * 1024
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -48,3 +48,13 @@ def test_more_than_one_gpu_exits(argv, env):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_cpu_baseline_runs_in_processes():
+    """The oracle baseline forks worker processes over independent sequences and reports the
+    processes it used (a short run on the tiny workload)."""
+    wl = workloads.WORKLOADS["tiny_fp32_decode_256"]
+    inp = workloads.gen_all(wl, 0)
+    r = bench.cpu_baseline(wl, inp, seconds_target=0.3, workers=2)
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["value"] > 0
+    assert "2 processes" in r["sample"]
