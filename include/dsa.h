@@ -114,6 +114,22 @@ int dsa_topk(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, v
              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dsa_topk for callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, and harnesses that forbid hipMalloc. It computes exactly what dsa_topk computes (the
+ * same kernels, so the same idx), but takes no workspace: it uses a static device array of
+ * DSA_TOPK_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on every GPU it runs on until
+ * the process ends, and calls no allocating routine. The array keeps the last call's contents;
+ * nothing in it needs clearing between calls. All calls on one GPU share its array, so two
+ * calls that overlap in time on one GPU (other streams, other host threads) race: order them.
+ * Returns DSA_ERR_UNSUPPORTED, writing nothing, when dsa_topk_workspace_size(rows, n_kv, top_k)
+ * exceeds the array (call dsa_topk with a workspace then); other arguments and errors as in
+ * dsa_topk. The first call on a device looks up the array's address there (DSA_ERR_HIP if that
+ * fails).
+ */
+#define DSA_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int dsa_topk_noalloc(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, hipStream_t stream);
+
+/*
  * Sparse absorbed MLA over the selected latent rows (ds4 "hy3: Metal decode path" PR,
  * GLM CPU oracle section: cached rows are 512 latent + 64 already-rotated rope values,
  * one softmax over the candidate rows; ik_llama_opt "MLA tensor parallelism" sub-commit:

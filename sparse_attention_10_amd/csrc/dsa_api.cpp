@@ -12,6 +12,8 @@
 
 #include "kernels.h"
 
+static_assert(DSA_TOPK_NOALLOC_SCRATCH_BYTES == dsa::kTopkScratchBytes, "the header states the scratch size");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -155,13 +157,18 @@ size_t dsa_topk_workspace_size(int rows, int n_kv, int top_k) {
   return dsa::plan_topk(rows, n_kv, top_k, 0).ws_bytes;
 }
 
+static int topk_args(const char* fn, const float* scores, const int32_t* idx, int rows, int n_kv, int top_k) {
+  if (!scores || !idx) return fail(DSA_ERR_NULL, "%s: scores and idx must be non-NULL", fn);
+  if (rows < 1 || n_kv < 1 || top_k < 1)
+    return fail(DSA_ERR_SHAPE, "%s: rows=%d n_kv=%d top_k=%d must all be >= 1", fn, rows, n_kv, top_k);
+  if ((long long)rows * n_kv > (1LL << 40) || rows > 65535)
+    return fail(DSA_ERR_SHAPE, "%s: rows=%d x n_kv=%d out of range (rows <= 65535)", fn, rows, n_kv);
+  return DSA_OK;
+}
+
 int dsa_topk(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, void* workspace,
              size_t workspace_bytes, hipStream_t stream) {
-  if (!scores || !idx) return fail(DSA_ERR_NULL, "dsa_topk: scores and idx must be non-NULL");
-  if (rows < 1 || n_kv < 1 || top_k < 1)
-    return fail(DSA_ERR_SHAPE, "dsa_topk: rows=%d n_kv=%d top_k=%d must all be >= 1", rows, n_kv, top_k);
-  if ((long long)rows * n_kv > (1LL << 40) || rows > 65535)
-    return fail(DSA_ERR_SHAPE, "dsa_topk: rows=%d x n_kv=%d out of range (rows <= 65535)", rows, n_kv);
+  if (const int st = topk_args("dsa_topk", scores, idx, rows, n_kv, top_k)) return st;
   const size_t need = dsa_topk_workspace_size(rows, n_kv, top_k);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "dsa_topk: workspace of %zu bytes needed, got %zu%s", need,
@@ -169,6 +176,23 @@ int dsa_topk(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, v
   const dsa::TopkPlan plan = dsa::plan_topk(rows, n_kv, top_k, g_topk_path.load());
   return hip_status(dsa::launch_topk(scores, idx, rows, n_kv, top_k, plan, workspace, stream),
                     "dsa_topk launch");
+}
+
+int dsa_topk_noalloc(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, hipStream_t stream) {
+  if (const int st = topk_args("dsa_topk_noalloc", scores, idx, rows, n_kv, top_k)) return st;
+  const size_t need = dsa_topk_workspace_size(rows, n_kv, top_k);
+  if (need > dsa::kTopkScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_topk_noalloc: this shape needs %zu bytes of scratch and the library's static array holds "
+                "%zu; call dsa_topk with a workspace",
+                need, dsa::kTopkScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = dsa::topk_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "dsa_topk_noalloc: scratch address");
+  }
+  const dsa::TopkPlan plan = dsa::plan_topk(rows, n_kv, top_k, g_topk_path.load());
+  return hip_status(dsa::launch_topk(scores, idx, rows, n_kv, top_k, plan, ws, stream), "dsa_topk_noalloc launch");
 }
 
 int dsa_sparse_mla_num_splits(int B, int n_q, int top_k) {

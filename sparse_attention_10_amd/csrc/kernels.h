@@ -40,6 +40,9 @@ struct TopkPlan {
 TopkPlan plan_topk(int rows, int n_kv, int top_k, int path);
 hipError_t launch_topk(const float* scores, int* idx, int rows, int n_kv, int top_k,
                        const TopkPlan& plan, void* workspace, hipStream_t stream);
+// the static top-k scratch of the current device (its device address; looked up once per device)
+constexpr size_t kTopkScratchBytes = size_t(16) << 20;
+hipError_t topk_scratch(void** ptr);
 
 // sparse MLA
 extern std::atomic<int> g_mla_tiles_per_step;  // 16-row tiles per step of the 16-bit MLA kernel (1 or 2, default 2)

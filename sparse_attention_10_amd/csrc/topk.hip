@@ -24,6 +24,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 namespace dsa {
 
@@ -915,6 +917,43 @@ static void launch_rows_t(const float* vals, long row_stride, int seg_len, int n
   else if (n <= 512 * 32) DSA_TOPK_REG(512, 32);
   else DSA_TOPK_REG(1024, 32);
 #undef DSA_TOPK_REG
+}
+
+// ---------------------------------------------------------------------------------------
+// Scratch for callers that cannot allocate (dsa_topk_noalloc): a file-scope device array,
+// one copy per GPU, held from the library's load until the process ends. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for the symbol):
+// its device address is looked up with hipGetSymbolAddress once per device, with that device
+// current, and kept. Every path writes what it later reads (candidate keys and indices,
+// per-segment counts, stage-1 results), so nothing needs clearing between calls; calls that
+// overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kTopkScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t topk_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_topk(const float* scores, int* idx, int rows, int n_kv, int top_k,

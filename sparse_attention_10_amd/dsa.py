@@ -23,7 +23,7 @@ _DTYPE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.float16: DSA_F
 EXPORTED = ("dsa_index_score", "dsa_index_score_sink", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
             "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_indexer_prep", "dsa_layer_computes_topk", "dsa_topk_source_layer", "dsa_set_tuning",
             "dsa_kpool_compress", "dsa_kpool_index_score", "dsa_kpool_expand", "dsa_kpool_sparse_mla_attn",
-            "dsa_status_string", "dsa_last_error", "dsa_version")
+            "dsa_topk_noalloc", "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
 class DsaError(RuntimeError):
@@ -46,6 +46,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_topk_workspace_size.restype = S
     lib.dsa_topk.argtypes = [P, P, I, I, I, P, S, P]
     lib.dsa_topk.restype = I
+    lib.dsa_topk_noalloc.argtypes = [P, P, I, I, I, P]
+    lib.dsa_topk_noalloc.restype = I
     lib.dsa_sparse_mla_num_splits.argtypes = [I, I, I]
     lib.dsa_sparse_mla_num_splits.restype = I
     lib.dsa_sparse_mla_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -172,6 +174,24 @@ def dsa_topk(scores: torch.Tensor, idx: torch.Tensor, top_k: int,
     wbytes = _workspace_bytes(workspace)
     _check(lib.dsa_topk(scores.data_ptr(), idx.data_ptr(), rows, n_kv, top_k, _ptr(workspace), wbytes,
                         _stream(stream)), "dsa_topk")
+    return idx
+
+
+TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20  # DSA_TOPK_NOALLOC_SCRATCH_BYTES
+
+
+def dsa_topk_noalloc(scores: torch.Tensor, idx: torch.Tensor, top_k: int, stream=None) -> torch.Tensor:
+    """dsa_topk without a workspace: the library's static per-GPU scratch array is used, and
+    nothing is allocated (for callers under graph capture or that cannot allocate). Calls that
+    overlap on one GPU share that array and race."""
+    _dev(scores, "scores")
+    _dev(idx, "idx")
+    n_kv = scores.shape[-1]
+    rows = scores.numel() // n_kv
+    if idx.numel() != rows * top_k or idx.dtype != torch.int32 or scores.dtype != torch.float32:
+        raise ValueError("dsa_topk_noalloc: idx must be int32 [rows][top_k], scores float32")
+    _check(lib.dsa_topk_noalloc(scores.data_ptr(), idx.data_ptr(), rows, n_kv, top_k, _stream(stream)),
+           "dsa_topk_noalloc")
     return idx
 
 

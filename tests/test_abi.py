@@ -310,3 +310,13 @@ def test_tuning_is_read_once_per_call_source():
     assert src.count("g_mla_head_split.load") == 1
     assert src.count("g_mla_tiles_per_step.load") == 1
     assert "mla_head_split(Hm, rows, n_split)" not in src
+
+
+def test_topk_noalloc_rejects_on_host(lib):
+    assert lib.dsa_topk_noalloc(None, FAKE, 1, 10, 2, None) == E_NULL
+    assert lib.dsa_topk_noalloc(FAKE, FAKE, 0, 10, 2, None) == E_SHAPE
+    assert lib.dsa_topk_noalloc(FAKE, FAKE, 70000, 10, 2, None) == E_SHAPE
+    # a shape whose workspace exceeds the static scratch array
+    assert lib.dsa_topk_workspace_size(256, 1 << 20, 2048) > (16 << 20)
+    assert lib.dsa_topk_noalloc(FAKE, FAKE, 256, 1 << 20, 2048, None) == E_UNSUP
+    assert b"static array" in lib.dsa_last_error()
