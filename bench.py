@@ -367,6 +367,9 @@ class Chain:
         self.ws_m = torch.empty(max(1, dsa.dsa_sparse_mla_workspace_size(wl.B, wl.n_q, wl.Hm, wl.top_k, wl.d_latent,
                                                                          self.n_split)),
                                 dtype=torch.uint8, device=dev)
+        self.ws_f = torch.empty(max(1, dsa.dsa_index_score_topk_workspace_size(wl.B, wl.n_q, wl.H, wl.D, wl.n_kv,
+                                                                               wl.top_k, wl.idx_dtype)),
+                                dtype=torch.uint8, device=dev)
 
     @property
     def layers(self):
@@ -379,35 +382,47 @@ class Chain:
     def topk(self, l):
         self.dsa.dsa_topk(self.scores, self.idx, self.wl.top_k, workspace=self.ws_t)
 
+    def score_topk(self, l):
+        """the fused call: the same scores and indices as score() then topk()"""
+        self.dsa.dsa_index_score_topk(self.q, self.keys[l], self.w, self.idx, self.wl.top_k, scores=self.scores,
+                                      kv_len=self.kv_len, q_pos=self.q_pos, scale=self.wl.scale,
+                                      workspace=self.ws_f)
+
     def mla(self, l):
         wl = self.wl
         self.dsa.dsa_sparse_mla_attn(self.qa, self.lats[l], self.idx, self.out, wl.d_latent, wl.sm_scale,
                                      lse=self.lse, kv_len=self.kv_len, n_split=self.n_split, workspace=self.ws_m)
 
-    def step(self, l):
-        self.score(l)
-        self.topk(l)
+    def step(self, l, fused=True):
+        if fused:
+            self.score_topk(l)
+        else:
+            self.score(l)
+            self.topk(l)
         self.mla(l)
 
 
-def time_calls(chain, steps, layer_of):
+def time_calls(chain, steps, layer_of, fused=False):
     """Average duration (ms) of each call over `steps` eager steps, from HIP events recorded on
-    the launch stream around every call; step s runs layer layer_of(s)."""
+    the launch stream around every call; step s runs layer layer_of(s). fused: the step is the
+    fused score -> top-k call and the attention, else the three separate calls."""
     import torch
     stream = torch.cuda.current_stream()
-    names = ("index_score", "topk", "sparse_mla")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    if fused:
+        names = ("index_score_topk", "sparse_mla")
+        fns = (chain.score_topk, chain.mla)
+    else:
+        names = ("index_score", "topk", "sparse_mla")
+        fns = (chain.score, chain.topk, chain.mla)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         l = layer_of(s)
         ev[s][0].record(stream)
-        chain.score(l)
-        ev[s][1].record(stream)
-        chain.topk(l)
-        ev[s][2].record(stream)
-        chain.mla(l)
-        ev[s][3].record(stream)
+        for j, f in enumerate(fns):
+            f(l)
+            ev[s][j + 1].record(stream)
     torch.cuda.synchronize()
     eager_s = (time.perf_counter() - t0) / steps
     per = {n: sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)) / steps for j, n in enumerate(names)}
@@ -466,18 +481,23 @@ def device_inputs(wl, dev, seed, layers):
 
 def decode_leg(dsa, chain, steps, warmup):
     """Timings of a decode chain: eager per-call events and graph step times with the layers in
-    rotation, and the same with every step on layer 0."""
+    rotation, and the same with every step on layer 0. The step is the fused score -> top-k
+    call and the attention; the three separate calls are timed beside it (their score kernel is
+    the fused call's without its candidate epilogue)."""
     L = chain.layers
     for s in range(max(1, warmup)):
         chain.step(s % L)
-    per_rot, eager_s = time_calls(chain, steps, lambda s: s % L)
+        chain.step(s % L, fused=False)
+    per_rot, _ = time_calls(chain, steps, lambda s: s % L)
+    per_fused, eager_s = time_calls(chain, steps, lambda s: s % L, fused=True)
     per_one, _ = time_calls(chain, steps, lambda s: 0)
     step_rot = graph_seconds(lambda n: [chain.step(s % L) for s in range(n)], steps, warmup)
+    step_sep = graph_seconds(lambda n: [chain.step(s % L, fused=False) for s in range(n)], steps, warmup)
     step_one = graph_seconds(lambda n: [chain.step(0) for s in range(n)], steps, warmup)
     # a layer that reuses the last full layer's indices (IndexShare) runs the attention only
     shared = graph_seconds(lambda n: [chain.mla(s % L) for s in range(n)], steps, warmup)
-    return {"per_rot": per_rot, "per_one": per_one, "eager_s": eager_s, "step_rot": step_rot,
-            "step_one": step_one, "shared": shared}
+    return {"per_rot": per_rot, "per_fused": per_fused, "per_one": per_one, "eager_s": eager_s,
+            "step_rot": step_rot, "step_sep": step_sep, "step_one": step_one, "shared": shared}
 
 
 def prefill_leg(dsa, dev, steps, warmup, seed):
@@ -524,7 +544,9 @@ def long_decode_leg(dsa, dev, steps, warmup, seed, layers):
            "step_hbm_gbs": round(ab["step"] / t["step_rot"] / 1e9, 1),
            "step_hbm_frac": round(ab["step"] / t["step_rot"] / 1e9 / HBM_PEAK_GBS, 4), "target_frac": 0.60,
            "step_algorithmic_bytes": ab["step"],
-           "kernels_ms": {k_: round(v, 4) for k_, v in t["per_rot"].items()},
+           "kernels_ms": {k_: round(v, 4) for k_, v in t["per_fused"].items()},
+           "unfused": {"ms_per_step": round(t["step_sep"] * 1e3, 4),
+                       "kernels_ms": {k_: round(v, 4) for k_, v in t["per_rot"].items()}},
            "score_roofline": {"bound": "hbm", "achieved": round(sc, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(sc / HBM_PEAK_GBS, 4), "bytes_per_launch": ab["index_score"]},
            "single_layer_ms_per_step": round(t["step_one"] * 1e3, 4),
@@ -708,7 +730,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "index_score_decode_mfma", "bytes_per_launch": ab["index_score"],
-                "layers_rotated": L}
+                "layers_rotated": L,
+                "measured_in": "the separate-call steps (dsa_index_score); the fused call runs the same "
+                               "kernel with a candidate epilogue"}
     result = {
         "metric": "DSA decode tokens/s at 32K ctx (batch 32) + achieved HBM GB/s vs peak",
         "value": round(value, 1),
@@ -732,8 +756,13 @@ def main():
         "step_hbm_frac": round(ab["step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": ab["step"],
         "eager_ms_per_step": round(t["eager_s"] * 1e3, 4),
-        "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
-        "kernels_gbs": {k_: round(ab[k_] / (per[k_] * 1e-3) / 1e9, 1) for k_ in per},
+        "step": "dsa_index_score_topk (fused score -> top-k) then dsa_sparse_mla_attn",
+        "kernels_ms": {k_: round(v, 4) for k_, v in t["per_fused"].items()},
+        "unfused": {"step": "dsa_index_score, dsa_topk, dsa_sparse_mla_attn",
+                    "ms_per_step": round(t["step_sep"] * 1e3, 4),
+                    "tokens_per_s": round(tokens / t["step_sep"], 1),
+                    "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
+                    "kernels_gbs": {k_: round(ab[k_] / (per[k_] * 1e-3) / 1e9, 1) for k_ in per}},
         "roofline": roof,
         "single_layer": {"ms_per_step": round(t["step_one"] * 1e3, 4),
                          "tokens_per_s": round(tokens / t["step_one"], 1),

@@ -114,6 +114,34 @@ int dsa_topk(const float* scores, int32_t* idx, int rows, int n_kv, int top_k, v
              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Fused score -> top-k (ik_llama_opt log, "decode-correct via persistent indexer-K cache":
+ * every cached key is scored, then the top_k are taken; the two steps of dsa_index_score and
+ * dsa_topk in one call). Results are exactly those of dsa_index_score followed by dsa_topk
+ * over its scores: the same scores (bit for bit) and the same idx.
+ *
+ * For decode rows (bf16/f16, D = 128, H <= 32, n_q < 8) the scoring kernel also writes, for
+ * each wave's range of keys, that range's largest keys as candidates, and one selection kernel
+ * takes the top-k from their union; it reads a range's stored scores again only where the
+ * range held more of the answer than it kept, and the whole row only when that set outgrows
+ * one workgroup. So the score rows are written but, in the common case, not read back, and the
+ * separate filter pass of dsa_topk is gone. Other shapes run dsa_index_score then dsa_topk.
+ *
+ * Arguments as in dsa_index_score, plus:
+ * scores     device, [B][n_q][n_kv] fp32 out, or NULL (the workspace then holds the scores)
+ * idx        device, [B][n_q][top_k] int32 out, as dsa_topk writes it
+ * top_k      >= 1 (top_k > n_kv allowed)
+ * workspace  device scratch of at least dsa_index_score_topk_workspace_size(B, n_q, H, D, n_kv,
+ *            top_k, q_dtype, scores == NULL) bytes
+ * B * n_q <= 65535.
+ */
+size_t dsa_index_score_topk_workspace_size(int B, int n_q, int H, int D, int n_kv, int top_k, int dtype,
+                                           int scores_in_workspace);
+int dsa_index_score_topk(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
+                         const int32_t* q_pos, float* scores, int32_t* idx, int B, int n_q, int H, int D, int n_kv,
+                         int top_k, int q_dtype, int k_dtype, float scale, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * dsa_topk for callers that cannot allocate: code under HIP graph capture, tight serving
  * loops, and harnesses that forbid hipMalloc. It computes exactly what dsa_topk computes (the
  * same kernels, so the same idx), but takes no workspace: it uses a static device array of
@@ -226,7 +254,9 @@ int dsa_topk_source_layer(int layer);
  * both give results within the same tolerance, with a different summation order). key
  * "mla_head_split": run each query's 64 heads as two 32-head workgroups sharing the query's
  * selected rows (0 = automatic: when 64-head workgroups would fill at most half of the 256
- * CUs; 1 = never; 2 = always for 64 heads). Returns DSA_OK,
+ * CUs; 1 = never; 2 = always for 64 heads). key "topk_cand_block": threads of the workgroup that
+ * selects a row's top-k among the candidates of dsa_index_score_topk (0 = automatic (1024),
+ * 256, 512 or 1024). Returns DSA_OK,
  * or DSA_ERR_SHAPE for an unknown key or value. The switches are process-wide state (atomic);
  * every call reads the ones it uses once, when it starts, so a change applies to later calls.
  */

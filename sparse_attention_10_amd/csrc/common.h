@@ -41,6 +41,21 @@ template <> __device__ __forceinline__ float load_as_f32<f16_t>(const f16_t* p, 
   return f16_bits_to_f32(p[i].bits);
 }
 
+// Scores as order-preserving uint32 keys for selection: a larger score gives a larger key;
+// -0.0 maps like +0.0; NaN and -inf map to 0, which marks "not a valid entry".
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (!(f == f)) return 0u;          // NaN
+  if (u == 0xff800000u) return 0u;   // -inf
+  if (u == 0x80000000u) u = 0u;      // -0.0 == +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Lanes below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Cross-lane helpers (wave64). xor 16 / 32 move data between the four 16-lane rows.
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 

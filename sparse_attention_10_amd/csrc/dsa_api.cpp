@@ -97,6 +97,12 @@ int dsa_set_tuning(const char* key, int value) {
     dsa::g_mla_tiles_per_step.store(value);
     return ok();
   }
+  if (std::strcmp(key, "topk_cand_block") == 0) {
+    if (value != 0 && value != 256 && value != 512 && value != 1024)
+      return fail(DSA_ERR_SHAPE, "topk_cand_block must be 0, 256, 512 or 1024 (got %d)", value);
+    dsa::g_topk_cand_block.store(value);
+    return ok();
+  }
   if (std::strcmp(key, "mla_head_split") == 0) {
     if (value < 0 || value > 2) return fail(DSA_ERR_SHAPE, "mla_head_split must be 0, 1 or 2 (got %d)", value);
     dsa::g_mla_head_split.store(value);
@@ -108,7 +114,7 @@ int dsa_set_tuning(const char* key, int value) {
 static int index_score_checked(const char* fn, const void* q, const void* k_cache, const float* w,
                                const int32_t* kv_len, const int32_t* q_pos, float* scores, int B, int n_q,
                                int H, int D, int n_kv, int q_dtype, int k_dtype, float scale,
-                               dsa::ScoreArgs sink, hipStream_t stream) {
+                               dsa::ScoreArgs sink, hipStream_t stream, bool launch = true) {
   if (!q || !k_cache || !w || !scores)
     return fail(DSA_ERR_NULL, "%s: q, k_cache, w and scores must be non-NULL", fn);
   if (B < 1 || n_q < 1 || H < 1 || D < 1 || n_kv < 1)
@@ -130,6 +136,7 @@ static int index_score_checked(const char* fn, const void* q, const void* k_cach
   if (!mfma && (long long)H * D > 16384)
     return fail(DSA_ERR_UNSUPPORTED, "%s: H*D = %lld exceeds 16384 outside the MFMA shape (16-bit, D=128, H<=32)",
                 fn, (long long)H * D);
+  if (!launch) return DSA_OK;
   return hip_status(dsa::launch_index_score(q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv, q_dtype,
                                             scale, sink, stream),
                     fn);
@@ -150,6 +157,65 @@ int dsa_index_score_sink(const void* q, const void* k_cache, const float* w, con
   if (!std::isfinite(sink_boost)) return fail(DSA_ERR_SHAPE, "dsa_index_score_sink: sink_boost must be finite");
   return index_score_checked("dsa_index_score_sink", q, k_cache, w, kv_len, q_pos, scores, B, n_q, H, D, n_kv,
                              q_dtype, k_dtype, scale, dsa::ScoreArgs{sink_start, n_sink, sink_boost, 1}, stream);
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the fused call: the candidates (fused path) or the top-k workspace (score and
+// top-k one after the other), then the score rows when the caller passes no score array.
+static size_t score_topk_bytes(const dsa::ScoreTopkPlan& p, int B, int n_q, int n_kv, int top_k,
+                               bool scores_in_ws) {
+  const long rows = (long)B * n_q;
+  const size_t sel = p.ok ? p.cand_bytes : dsa::plan_topk((int)rows, n_kv, top_k, 0).ws_bytes;
+  return align256(sel) + (scores_in_ws ? align256((size_t)rows * n_kv * sizeof(float)) : 0);
+}
+
+size_t dsa_index_score_topk_workspace_size(int B, int n_q, int H, int D, int n_kv, int top_k, int dtype,
+                                           int scores_in_workspace) {
+  if (B < 1 || n_q < 1 || H < 1 || D < 1 || n_kv < 1 || top_k < 1 || (long long)B * n_q > 65535) return 0;
+  return score_topk_bytes(dsa::plan_score_topk(B, n_q, H, D, n_kv, top_k, dtype), B, n_q, n_kv, top_k,
+                          scores_in_workspace != 0);
+}
+
+int dsa_index_score_topk(const void* q, const void* k_cache, const float* w, const int32_t* kv_len,
+                         const int32_t* q_pos, float* scores, int32_t* idx, int B, int n_q, int H, int D, int n_kv,
+                         int top_k, int q_dtype, int k_dtype, float scale, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  const char* fn = "dsa_index_score_topk";
+  if (!q || !k_cache || !w || !idx) return fail(DSA_ERR_NULL, "%s: q, k_cache, w and idx must be non-NULL", fn);
+  if (top_k < 1) return fail(DSA_ERR_SHAPE, "%s: top_k=%d must be >= 1", fn, top_k);
+  if (B >= 1 && n_q >= 1 && (long long)B * n_q > 65535)
+    return fail(DSA_ERR_SHAPE, "%s: B * n_q = %lld rows exceed 65535", fn, (long long)B * n_q);
+  // the score arguments are checked as dsa_index_score checks them, without launching (a NULL
+  // score array is allowed here: the workspace then holds the scores)
+  if (const int st = index_score_checked(fn, q, k_cache, w, kv_len, q_pos, scores ? scores : const_cast<float*>(w), B,
+                                         n_q, H, D, n_kv, q_dtype, k_dtype, scale,
+                                         dsa::ScoreArgs{nullptr, 0, 0.f, 1}, stream, false))
+    return st;
+  const dsa::ScoreTopkPlan plan = dsa::plan_score_topk(B, n_q, H, D, n_kv, top_k, q_dtype);
+  const size_t need = score_topk_bytes(plan, B, n_q, n_kv, top_k, scores == nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu%s", fn, need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  const int rows = B * n_q;
+  char* ws = static_cast<char*>(workspace);
+  const size_t sel_bytes = align256(plan.ok ? plan.cand_bytes : dsa::plan_topk(rows, n_kv, top_k, 0).ws_bytes);
+  float* sc = scores ? scores : reinterpret_cast<float*>(ws + sel_bytes);
+  if (!plan.ok) {  // score, then top-k over the stored rows
+    hipError_t e = dsa::launch_index_score(q, k_cache, w, kv_len, q_pos, sc, B, n_q, H, D, n_kv, q_dtype, scale,
+                                           dsa::ScoreArgs{nullptr, 0, 0.f, 1}, stream);
+    if (e != hipSuccess) return hip_status(e, "dsa_index_score_topk score launch");
+    const dsa::TopkPlan tp = dsa::plan_topk(rows, n_kv, top_k, g_topk_path.load());
+    return hip_status(dsa::launch_topk(sc, idx, rows, n_kv, top_k, tp, ws, stream), "dsa_index_score_topk top-k launch");
+  }
+  const size_t slots = (size_t)rows * plan.n_w * plan.m;
+  dsa::CandOut cand{reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int*>(ws + align256(slots * 4)),
+                    reinterpret_cast<uint4*>(ws + 2 * align256(slots * 4)), plan.m};
+  hipError_t e = dsa::launch_index_score_cand(q, k_cache, w, kv_len, q_pos, sc, B, n_q, H, n_kv, q_dtype, scale, plan,
+                                              cand, stream);
+  if (e != hipSuccess) return hip_status(e, "dsa_index_score_topk score launch");
+  return hip_status(dsa::launch_topk_cand(sc, idx, rows, n_kv, top_k, plan, cand, stream),
+                    "dsa_index_score_topk select launch");
 }
 
 size_t dsa_topk_workspace_size(int rows, int n_kv, int top_k) {

@@ -214,11 +214,16 @@ __device__ __forceinline__ void wave_lds_order() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename T16, int ITERS, bool FULLH>
+//
+// With CAND (the fused score -> top-k call) each wave walks ITERS consecutive chunks, so that a
+// wave's keys form one range, and after its stores it also writes that range's m largest keys
+// as candidates for the selection (the keys of the stored scores, so the selection over the
+// candidates and over the stored row agree bit for bit).
+template <typename T16, int ITERS, bool FULLH, bool CAND>
 __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
     const int* __restrict__ kv_len, const int* __restrict__ q_pos, float* __restrict__ scores,
-    int n_q, int H, int n_kv, float scale, ScoreArgs sink) {
+    int n_q, int H, int n_kv, float scale, ScoreArgs sink, CandOut cand) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDecWaves][64 * 256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -231,7 +236,10 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
   uint8_t* my = lds[wave];
 
   // chunk it of this wave starts at key kb(it)
-  auto kb_of = [&](int it) { return ((int)(blockIdx.x * ITERS + it) * kDecWaves + wave) * 64; };
+  auto kb_of = [&](int it) {
+    return CAND ? ((int)(blockIdx.x * kDecWaves + wave) * ITERS + it) * 64
+                : ((int)(blockIdx.x * ITERS + it) * kDecWaves + wave) * 64;
+  };
   const int last = max(limit - 1, 0);
   auto fetch = [&](int kb, i32x4(&pre)[16]) {
 #pragma unroll
@@ -289,6 +297,55 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
   for (int it = 0; it < ITERS; ++it) {
     const int t = kb_of(it) + lane;
     if (t < n_kv) out[t] = t < limit ? sk.add(t, scale * res[it]) : -INFINITY;
+  }
+  if constexpr (CAND) {
+    // keys of the stored scores (0: masked or past the row)
+    uint32_t key[ITERS];
+    uint32_t nv = 0;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int t = kb_of(it) + lane;
+      key[it] = (t < n_kv && t < limit) ? score_key(sk.add(t, scale * res[it])) : 0u;
+      nv += (uint32_t)__popcll(__ballot(key[it] != 0u));
+    }
+    // the m-th largest key tau, by deciding its bits from the top: the largest prefix with at
+    // least m keys at or above it (with nv <= m every valid key is kept: tau = 1)
+    const uint32_t m = (uint32_t)cand.m;
+    uint32_t tau = 1u, take_eq = 0xffffffffu;
+    if (nv > m) {
+      uint32_t pre = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = pre | (1u << bit);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) cnt += (uint32_t)__popcll(__ballot(key[it] >= c));
+        if (cnt >= m) pre = c;
+      }
+      tau = pre;
+      uint32_t ngt = 0;
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) ngt += (uint32_t)__popcll(__ballot(key[it] > tau));
+      take_eq = m - ngt;  // keys equal to tau that are kept, the lowest indices first
+    }
+    const int nw = (int)gridDim.x * kDecWaves;
+    const long slot = (long)bi * nw + (long)blockIdx.x * kDecWaves + wave;
+    uint32_t* ok = cand.key + slot * m;
+    int* oi = cand.idx + slot * m;
+    uint32_t eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const uint64_t eqm = __ballot(key[it] == tau);
+      const bool sel = key[it] > tau || (key[it] == tau && eq_before + mbcnt(eqm) < take_eq);
+      const uint64_t selm = __ballot(sel);
+      if (sel) {
+        const uint32_t p = sel_before + mbcnt(selm);
+        ok[p] = key[it];
+        oi[p] = kb_of(it) + lane;
+      }
+      eq_before += (uint32_t)__popcll(eqm);
+      sel_before += (uint32_t)__popcll(selm);
+    }
+    if (lane == 0) cand.hdr[slot] = make_uint4(min(nv, m), nv, nv > m ? tau : 0u, 0u);
   }
 }
 
@@ -449,8 +506,81 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
 }
 
 // ---------------------------------------------------------------------------------------
-// launcher
+// launchers
 // ---------------------------------------------------------------------------------------
+// 64-key chunks per wave of the decode kernel: about 2048 blocks (short-lived waves of two
+// chunks each measured fastest: more independent streams in flight than a few long-lived
+// waves), or the tuning switch when `tuned`.
+static int decode_iters(long rows, int n_kv, bool tuned = true) {
+  const long chunks = (n_kv + 255) / 256;  // 256-key block steps per query
+  const int cpw = tuned ? g_score_cpw.load(std::memory_order_relaxed) : 0;
+  const long want = cpw > 0 ? cpw : (chunks * rows) / 2048;
+  return want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
+}
+
+// Candidates per wave: the wave's expected share of the top-k if the chosen keys were spread
+// evenly, mu = G top_k / n_kv, plus 4 standard deviations and 4, so that a wave seldom holds
+// more of the top-k than it keeps (the selection then re-reads that wave's scores, and the
+// select kernel lasts as long as its slowest row: at 2.5 deviations about one row in five of
+// the batched decode shape needed a re-read). Waves take more chunks while the union of the
+// candidates would not fit one select workgroup.
+ScoreTopkPlan plan_score_topk(int B, int n_q, int H, int D, int n_kv, int top_k, int dtype) {
+  ScoreTopkPlan p{false, 0, 0, 0, 0};
+  const long rows = (long)B * n_q;
+  if (!(D == 128 && H >= 1 && H <= 32 && (dtype == kBF16 || dtype == kF16) && n_q < 8 && rows <= 65535))
+    return p;
+  const long chunks = (n_kv + 255) / 256;
+  // the automatic rule only, so that the workspace size does not depend on tuning switches
+  for (int iters = decode_iters(rows, n_kv, false); iters <= 8; iters *= 2) {
+    const long n_w = (chunks + iters - 1) / iters * 4;
+    const int G = 64 * iters;
+    const double mu = top_k >= n_kv ? (double)G : (double)G * top_k / n_kv;
+    int m = (int)ceil(mu + 4.0 * sqrt(mu) + 4.0);
+    m = m > G ? G : m;
+    if (n_w <= kCandMaxWaves && n_w * m <= kCandCap) {
+      p.ok = true;
+      p.iters = iters;
+      p.m = m;
+      p.n_w = (int)n_w;
+      const size_t slots = (size_t)rows * n_w * m;
+      p.cand_bytes = (slots * 4 + 255) / 256 * 256 * 2 + (size_t)rows * n_w * 16;
+      return p;
+    }
+  }
+  return p;
+}
+
+template <typename T16>
+static hipError_t launch_cand_t(const void* q, const void* k, const float* w, const int* kv_len, const int* q_pos,
+                                float* scores, int B, int n_q, int H, int n_kv, float scale,
+                                const ScoreTopkPlan& plan, CandOut cand, hipStream_t stream) {
+  const dim3 grid((unsigned)(plan.n_w / kDecWaves), (unsigned)((long)B * n_q));
+  const ScoreArgs none{nullptr, 0, 0.f, 1};
+#define DSA_CAND_LAUNCH(N)                                                                      \
+  if (H == 32)                                                                                  \
+    hipLaunchKernelGGL((index_score_decode_mfma<T16, N, true, true>), grid, dim3(256), 0, stream,  \
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, none, cand); \
+  else                                                                                          \
+    hipLaunchKernelGGL((index_score_decode_mfma<T16, N, false, true>), grid, dim3(256), 0, stream, \
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, none, cand)
+  switch (plan.iters) {
+    case 8: DSA_CAND_LAUNCH(8); break;
+    case 4: DSA_CAND_LAUNCH(4); break;
+    case 2: DSA_CAND_LAUNCH(2); break;
+    default: DSA_CAND_LAUNCH(1); break;
+  }
+#undef DSA_CAND_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score_cand(const void* q, const void* k, const float* w, const int* kv_len,
+                                   const int* q_pos, float* scores, int B, int n_q, int H, int n_kv, int dtype,
+                                   float scale, const ScoreTopkPlan& plan, CandOut cand, hipStream_t stream) {
+  if (dtype == kBF16)
+    return launch_cand_t<bf16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, plan, cand, stream);
+  return launch_cand_t<f16_t>(q, k, w, kv_len, q_pos, scores, B, n_q, H, n_kv, scale, plan, cand, stream);
+}
+
 template <typename T16>
 static hipError_t launch_mfma(const void* q, const void* k, const float* w, const int* kv_len,
                               const int* q_pos, float* scores, int B, int n_q, int H, int n_kv,
@@ -481,20 +611,18 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
   } else {
     const long chunks = (n_kv + 255) / 256;  // 256-key block steps per query
     const long rows = (long)B * n_q;
-    // about 2048 blocks: short-lived waves of two chunks each measured fastest (more
-    // independent streams in flight than a few long-lived waves)
-    const int cpw = g_score_cpw.load(std::memory_order_relaxed);
-    long want = cpw > 0 ? cpw : (chunks * rows) / 2048;
-    const int iters = want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
+    const int iters = decode_iters(rows, n_kv);
     const long xblocks = (chunks + iters - 1) / iters;
     dim3 grid((unsigned)xblocks, (unsigned)rows);
 #define DSA_DECODE_LAUNCH(N)                                                                  \
   if (H == 32)                                                                                \
-    hipLaunchKernelGGL((index_score_decode_mfma<T16, N, true>), grid, dim3(256), 0, stream,     \
-                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, sink); \
+    hipLaunchKernelGGL((index_score_decode_mfma<T16, N, true, false>), grid, dim3(256), 0, stream, \
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, sink, \
+                       CandOut{nullptr, nullptr, nullptr, 0});                                \
   else                                                                                        \
-    hipLaunchKernelGGL((index_score_decode_mfma<T16, N, false>), grid, dim3(256), 0, stream,    \
-                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, sink)
+    hipLaunchKernelGGL((index_score_decode_mfma<T16, N, false, false>), grid, dim3(256), 0, stream, \
+                       (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, sink, \
+                       CandOut{nullptr, nullptr, nullptr, 0})
     switch (iters) {
       case 8: DSA_DECODE_LAUNCH(8); break;
       case 4: DSA_DECODE_LAUNCH(4); break;

@@ -23,6 +23,34 @@ struct ScoreArgs {
 };
 
 // Tuning switches (dsa_set_tuning): process-wide, each read once per call.
+// Candidate output of the decode score kernel for the fused score -> top-k call: every wave
+// (n_w per row, each over its own G = ITERS * 64 consecutive keys) writes its m largest valid
+// keys (order-preserving keys, ties to the lower index) in index order, and a header
+// {kept, valid keys, m-th largest key when valid > m (else 0), 0}.
+struct CandOut {
+  uint32_t* key;  // [rows][n_w * m]
+  int* idx;       // [rows][n_w * m]
+  uint4* hdr;     // [rows][n_w]
+  int m;
+};
+// Plan of the fused score -> top-k path for decode rows (16-bit, D = 128, H <= 32, n_q < 8):
+// chunks per wave, candidates per wave, waves per row; ok = false when the shape is not one
+// the fused kernels take (then the call runs the score and top-k kernels one after the other).
+struct ScoreTopkPlan {
+  bool ok;
+  int iters, m, n_w;
+  size_t cand_bytes;  // candidate keys, indices and headers
+};
+constexpr int kCandCap = 8192;       // candidates one select workgroup holds in registers
+constexpr int kCandMaxWaves = 1024;  // candidate ranges (waves) per row
+extern std::atomic<int> g_topk_cand_block;  // threads of the candidate select workgroup (0: 1024)
+ScoreTopkPlan plan_score_topk(int B, int n_q, int H, int D, int n_kv, int top_k, int dtype);
+hipError_t launch_index_score_cand(const void* q, const void* k, const float* w, const int* kv_len,
+                                   const int* q_pos, float* scores, int B, int n_q, int H, int n_kv, int dtype,
+                                   float scale, const ScoreTopkPlan& plan, CandOut cand, hipStream_t stream);
+hipError_t launch_topk_cand(const float* scores, int* idx, int rows, int n_kv, int top_k,
+                            const ScoreTopkPlan& plan, const CandOut& cand, hipStream_t stream);
+
 extern std::atomic<int> g_score_cpw;            // 64-key chunks per wave of the decode scoring kernel, 0 automatic
 extern std::atomic<int> g_score_prefill_waves;  // waves per block of the prefill scoring kernel (4 or 8), 0 automatic
 hipError_t launch_index_score(const void* q, const void* k, const float* w, const int* kv_len,

@@ -29,21 +29,9 @@
 
 namespace dsa {
 
-__device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (!(f == f)) return 0u;          // NaN
-  if (u == 0xff800000u) return 0u;   // -inf
-  if (u == 0x80000000u) u = 0u;      // -0.0 == +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __device__ __forceinline__ float key_value(uint32_t key) {
   const uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
   return __uint_as_float(u);
-}
-
-__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Exclusive prefix sum over the threads of the block (thread order); *total gets the sum.
@@ -381,67 +369,28 @@ struct ResidentSmem {
   uint32_t eq_take;
 };
 
-template <int BLOCK, int ITEMS, typename IdOf>
-__device__ __forceinline__ void select_resident(ResidentSmem<BLOCK, ITEMS>& sm, const uint32_t (&key)[ITEMS],
-                                                int top_k, IdOf id_of, int* __restrict__ o_idx,
-                                                float* __restrict__ o_val) {
-  constexpr int NW = BLOCK / 64;
+// The K-th largest of the nonzero keys held in key[] (1 <= K <= n_valid, their count; kmin and
+// kmax their extremes): radix rounds on the live range [lo, lo + span], at most 8192 LDS bins
+// each, narrowed to the bin holding the K-th key. Uniform over the workgroup.
+template <int BLOCK, int ITEMS>
+__device__ __forceinline__ uint32_t resident_kth(ResidentSmem<BLOCK, ITEMS>& sm, const uint32_t (&key)[ITEMS],
+                                                 uint32_t K, uint32_t n_valid, uint32_t kmin, uint32_t kmax) {
   constexpr int NB = 8192;
-  constexpr int NCH = ITEMS * NW;  // chunks of 64
-  constexpr int CPL = (NCH + 63) / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
   uint4* h4 = reinterpret_cast<uint4*>(sm.hist);
-  for (int i = tid; i < NB / 4; i += BLOCK) h4[i] = make_uint4(0u, 0u, 0u, 0u);
-  uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    if (key[j]) {
-      ++cnt;
-      kmin = min(kmin, key[j]);
-      kmax = max(kmax, key[j]);
-    }
-  }
-  wave_count_min_max(cnt, kmin, kmax);
-  if (lane == 0) {
-    sm.wa[wave] = cnt;
-    sm.wb[wave] = kmin;
-    sm.wc[wave] = kmax;
-  }
-  if (tid == 0) {
-    sm.mm[0] = 0u;
-    sm.mm[1] = 0xffffffffu;
-    sm.nlist = 0u;
-  }
-  __syncthreads();
-  uint32_t n_valid = 0;
-  kmin = 0xffffffffu;
-  kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    n_valid += sm.wa[w];
-    kmin = min(kmin, sm.wb[w]);
-    kmax = max(kmax, sm.wc[w]);
-  }
-  const uint32_t K = min((uint32_t)top_k, n_valid);
-  if (K == 0) {
-    for (int p = tid; p < top_k; p += BLOCK) {
-      o_idx[p] = -1;
-      if (o_val) o_val[p] = -INFINITY;
-    }
-    return;
-  }
-
   uint32_t T = kmin;  // every valid key is taken when K == n_valid
   if (K < n_valid) {
     uint32_t need = K;
     uint32_t lo = kmin, span = kmax - kmin;
     for (int round = 0; round < 4; ++round) {  // uniform over the workgroup
       const int shift = max(0, bit_width(span) - 13);
-      if (round > 0) {
-        for (int i = tid; i < NB / 4; i += BLOCK) h4[i] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
+      for (int i = tid; i < NB / 4; i += BLOCK) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (tid == 0) {
+        sm.mm[0] = 0u;
+        sm.mm[1] = 0xffffffffu;
+        sm.nlist = 0u;
       }
+      __syncthreads();
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
         const uint32_t rel = key[j] - lo;
@@ -498,6 +447,19 @@ __device__ __forceinline__ void select_resident(ResidentSmem<BLOCK, ITEMS>& sm, 
     }
   }
 
+  return T;
+}
+
+// Writes the K chosen keys' ids in item order (item j * BLOCK + tid of key[j]): every key > T
+// and the first K - count(> T) keys == T, through ballot compaction, then -1 up to top_k.
+template <int BLOCK, int ITEMS, typename IdOf>
+__device__ __forceinline__ void resident_write(ResidentSmem<BLOCK, ITEMS>& sm, const uint32_t (&key)[ITEMS],
+                                               uint32_t T, uint32_t K, int top_k, IdOf id_of,
+                                               int* __restrict__ o_idx, float* __restrict__ o_val) {
+  constexpr int NW = BLOCK / 64;
+  constexpr int NCH = ITEMS * NW;  // chunks of 64
+  constexpr int CPL = (NCH + 63) / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // per-chunk counts of keys > T and == T
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
@@ -551,6 +513,51 @@ __device__ __forceinline__ void select_resident(ResidentSmem<BLOCK, ITEMS>& sm, 
     o_idx[p] = -1;
     if (o_val) o_val[p] = -INFINITY;
   }
+}
+
+template <int BLOCK, int ITEMS, typename IdOf>
+__device__ __forceinline__ void select_resident(ResidentSmem<BLOCK, ITEMS>& sm, const uint32_t (&key)[ITEMS],
+                                                int top_k, IdOf id_of, int* __restrict__ o_idx,
+                                                float* __restrict__ o_val) {
+  constexpr int NW = BLOCK / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    if (key[j]) {
+      ++cnt;
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  }
+  wave_count_min_max(cnt, kmin, kmax);
+  if (lane == 0) {
+    sm.wa[wave] = cnt;
+    sm.wb[wave] = kmin;
+    sm.wc[wave] = kmax;
+  }
+  __syncthreads();
+  uint32_t n_valid = 0;
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    n_valid += sm.wa[w];
+    kmin = min(kmin, sm.wb[w]);
+    kmax = max(kmax, sm.wc[w]);
+  }
+  const uint32_t K = min((uint32_t)top_k, n_valid);
+  if (K == 0) {
+    for (int p = tid; p < top_k; p += BLOCK) {
+      o_idx[p] = -1;
+      if (o_val) o_val[p] = -INFINITY;
+    }
+    return;
+  }
+
+  const uint32_t T = K < n_valid ? resident_kth<BLOCK, ITEMS>(sm, key, K, n_valid, kmin, kmax) : kmin;
+  resident_write<BLOCK, ITEMS>(sm, key, T, K, top_k, id_of, o_idx, o_val);
 }
 
 // One workgroup per (segment, row) of the scores (stage 1 of the two-stage path, or the
@@ -839,6 +846,179 @@ __global__ __launch_bounds__(BLOCK) void topk_filtered_select(const float* __res
       if ((uint32_t)(j * BLOCK + tid) >= T) key[j] = 0u;
   }
   select_resident<BLOCK, ITEMS>(sm.res, key, top_k, [&](int j) { return ci[j]; }, o_idx, nullptr);
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection over the candidates of the fused score -> top-k call: one workgroup per row.
+//
+// The score kernel left, for each wave w of the row (keys [w G, w G + G)), its e_w = min(v_w, m)
+// largest valid keys in index order, its valid count v_w and, when it held more than m valid
+// keys (truncated), its m-th largest key tau_w. Let K = min(top_k, sum v_w) and T the K-th
+// largest of the union U of the kept keys. A key a truncated wave did not keep is at most
+// tau_w, so when tau_w < T it is below K keys of U and cannot be chosen: if every truncated
+// wave has tau_w < T, the top-k of U is the top-k of the row. Otherwise the waves with
+// tau_w >= T (all truncated waves when U holds fewer than K keys) are re-read whole from the
+// stored scores and the selection runs again over that larger set; its K-th key is at least T,
+// so every other truncated wave still lies below it and one re-read suffices. A set larger
+// than the workgroup holds falls back to the streaming select over the stored row. Every
+// route gives the row's unique answer. Candidates are concatenated in wave order, so in
+// ascending index order, which the ordered output keeps.
+// ---------------------------------------------------------------------------------------
+template <int BLOCK, int ITEMS>
+__global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restrict__ scores, int n_kv, int top_k,
+                                                          int n_w, int m, int G, const uint32_t* __restrict__ ckey,
+                                                          const int* __restrict__ cidx,
+                                                          const uint4* __restrict__ chdr, int* __restrict__ out_idx) {
+  constexpr int NW = BLOCK / 64;
+  constexpr int WPT = (kCandMaxWaves + BLOCK - 1) / BLOCK;  // waves (headers) per thread: tid * WPT + i
+  __shared__ FilterSelectSmem<BLOCK, ITEMS> sm;
+  __shared__ uint32_t s_keep[kCandMaxWaves];  // kept candidates of each wave
+  __shared__ uint32_t s_pre[kCandMaxWaves + 1];
+  __shared__ uint8_t s_off[kCandMaxWaves];    // wave re-read whole
+  __shared__ uint32_t s_red[NW][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long row = blockIdx.x;
+  int* o_idx = out_idx + row * top_k;
+  const int slots = n_w * m;
+  const long cbase = row * (long)slots;
+
+  // candidates (issued first) and headers
+  uint32_t key[ITEMS];
+  int ci[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int e = j * BLOCK + tid;
+    key[j] = e < slots ? ckey[cbase + e] : 0u;
+    ci[j] = e < slots ? cidx[cbase + e] : -1;
+  }
+  uint4 h[WPT];
+  uint32_t vsum = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    h[i] = w < n_w ? chdr[row * n_w + w] : make_uint4(0u, 0u, 0u, 0u);
+    if (w < n_w) s_keep[w] = h[i].x;
+    vsum += h[i].y;
+  }
+  __syncthreads();
+  // a wave's slots past its kept count hold stale values
+  uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int e = j * BLOCK + tid;
+    const int w = e / m;
+    if (e >= slots || (uint32_t)(e - w * m) >= s_keep[min(w, n_w - 1)]) key[j] = 0u;
+    if (key[j]) {
+      ++cnt;
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  }
+  wave_count_min_max(cnt, kmin, kmax);
+  vsum = lane_value(wave_scan(vsum, 0u, OpAdd()), 63);
+  if (lane == 0) {
+    s_red[wave][0] = cnt;
+    s_red[wave][1] = kmin;
+    s_red[wave][2] = kmax;
+    s_red[wave][3] = vsum;
+  }
+  __syncthreads();
+  uint32_t n_u = 0, n_valid = 0;
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    n_u += s_red[w][0];
+    kmin = min(kmin, s_red[w][1]);
+    kmax = max(kmax, s_red[w][2]);
+    n_valid += s_red[w][3];
+  }
+  const uint32_t K = min((uint32_t)top_k, n_valid);
+  if (K == 0) {
+    for (int p = tid; p < top_k; p += BLOCK) o_idx[p] = -1;
+    return;
+  }
+  uint32_t T = 0u;
+  bool refine = n_u < K;  // uniform
+  if (!refine) {
+    T = K < n_u ? resident_kth<BLOCK, ITEMS>(sm.res, key, K, n_u, kmin, kmax) : kmin;
+    bool mine = false;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) mine |= h[i].y > h[i].x && h[i].z >= T;  // truncated at or above T
+    refine = __syncthreads_or(mine) != 0;
+  }
+  if (!refine) {
+    resident_write<BLOCK, ITEMS>(sm.res, key, T, K, top_k, [&](int j) { return ci[j]; }, o_idx, nullptr);
+    return;
+  }
+  // re-read the offending waves whole: wave w then contributes its whole key range
+  uint32_t c[WPT], local = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    const bool off = h[i].y > h[i].x && (n_u < K || h[i].z >= T);
+    c[i] = w < n_w ? (off ? (uint32_t)min(G, n_kv - w * G) : h[i].x) : 0u;
+    if (w < n_w) s_off[w] = off ? 1 : 0;
+    local += c[i];
+  }
+  uint32_t total;
+  uint32_t before = block_exclusive_scan<BLOCK>(local, sm.str.wsum, &total);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    if (w < n_w) s_pre[w] = before;
+    before += c[i];
+  }
+  if (tid == 0) s_pre[n_w] = total;
+  __syncthreads();
+  if (total > (uint32_t)(BLOCK * ITEMS)) {  // uniform
+    select_streaming<BLOCK>(sm.str, scores + row * n_kv, n_kv, top_k, o_idx);
+    return;
+  }
+  const int top_bit = 1 << (31 - __clz(n_w));
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const uint32_t e = (uint32_t)(j * BLOCK + tid);
+    key[j] = 0u;
+    ci[j] = -1;
+    if (e < total) {
+      int w = 0;
+      for (int bb = top_bit; bb > 0; bb >>= 1)
+        if (w + bb < n_w && s_pre[w + bb] <= e) w += bb;
+      const int slot = (int)(e - s_pre[w]);
+      if (s_off[w]) {
+        const int t = w * G + slot;
+        key[j] = score_key(scores[row * n_kv + t]);
+        ci[j] = t;
+      } else {
+        key[j] = ckey[cbase + (long)w * m + slot];
+        ci[j] = cidx[cbase + (long)w * m + slot];
+      }
+    }
+  }
+  __syncthreads();
+  select_resident<BLOCK, ITEMS>(sm.res, key, top_k, [&](int j) { return ci[j]; }, o_idx, nullptr);
+}
+
+std::atomic<int> g_topk_cand_block{0};
+
+hipError_t launch_topk_cand(const float* scores, int* idx, int rows, int n_kv, int top_k,
+                            const ScoreTopkPlan& plan, const CandOut& cand, hipStream_t stream) {
+  const int tuned = g_topk_cand_block.load(std::memory_order_relaxed);
+  const int G = 64 * plan.iters;
+#define DSA_CAND_SELECT(BL, IT)                                                                      \
+  static_assert(BL * IT == kCandCap, "one select workgroup holds the candidate union");             \
+  hipLaunchKernelGGL((topk_cand_select<BL, IT>), dim3(rows), dim3(BL), 0, stream, scores, n_kv, top_k, \
+                     plan.n_w, plan.m, G, cand.key, cand.idx, cand.hdr, idx)
+  if (tuned == 256) {
+    DSA_CAND_SELECT(256, 32);
+  } else if (tuned == 512) {
+    DSA_CAND_SELECT(512, 16);
+  } else {
+    DSA_CAND_SELECT(1024, 8);
+  }
+#undef DSA_CAND_SELECT
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------

@@ -23,7 +23,8 @@ _DTYPE = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.float16: DSA_F
 EXPORTED = ("dsa_index_score", "dsa_index_score_sink", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_num_splits",
             "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn", "dsa_indexer_prep", "dsa_layer_computes_topk", "dsa_topk_source_layer", "dsa_set_tuning",
             "dsa_kpool_compress", "dsa_kpool_index_score", "dsa_kpool_expand", "dsa_kpool_sparse_mla_attn",
-            "dsa_topk_noalloc", "dsa_status_string", "dsa_last_error", "dsa_version")
+            "dsa_topk_noalloc", "dsa_index_score_topk_workspace_size", "dsa_index_score_topk",
+            "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
 class DsaError(RuntimeError):
@@ -48,6 +49,10 @@ def _load() -> ctypes.CDLL:
     lib.dsa_topk.restype = I
     lib.dsa_topk_noalloc.argtypes = [P, P, I, I, I, P]
     lib.dsa_topk_noalloc.restype = I
+    lib.dsa_index_score_topk_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+    lib.dsa_index_score_topk_workspace_size.restype = S
+    lib.dsa_index_score_topk.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, S, P]
+    lib.dsa_index_score_topk.restype = I
     lib.dsa_sparse_mla_num_splits.argtypes = [I, I, I]
     lib.dsa_sparse_mla_num_splits.restype = I
     lib.dsa_sparse_mla_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -153,6 +158,39 @@ def dsa_index_score(q: torch.Tensor, k_cache: torch.Tensor, w: torch.Tensor, sco
                                scores.data_ptr(), B, n_q, H, D, n_kv, _DTYPE[q.dtype], _DTYPE[k_cache.dtype],
                                float(scale), _stream(stream)), "dsa_index_score")
     return scores
+
+
+def dsa_index_score_topk_workspace_size(B: int, n_q: int, H: int, D: int, n_kv: int, top_k: int, dtype,
+                                        scores_in_workspace: bool = False) -> int:
+    code = _DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.dsa_index_score_topk_workspace_size(B, n_q, H, D, n_kv, top_k, code, 1 if scores_in_workspace else 0))
+
+
+def dsa_index_score_topk(q: torch.Tensor, k_cache: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, top_k: int,
+                         scores: Optional[torch.Tensor] = None, kv_len: Optional[torch.Tensor] = None,
+                         q_pos: Optional[torch.Tensor] = None, scale: float = 1.0,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Scores and top-k in one call: q [B][n_q][H][D], k_cache [B][n_kv][D] (same dtype), w [B][n_q][H]
+    fp32, idx [B][n_q][top_k] int32 (output); scores [B][n_q][n_kv] fp32 (output) or None (kept in
+    the workspace); kv_len [B] / q_pos [B][n_q] int32 or None."""
+    B, n_q, H, D = q.shape
+    n_kv = k_cache.shape[1]
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (w, "w"), (idx, "idx")):
+        _dev(t, n)
+    if tuple(k_cache.shape) != (B, n_kv, D) or tuple(w.shape) != (B, n_q, H) \
+            or tuple(idx.shape) != (B, n_q, top_k) or idx.dtype != torch.int32 or w.dtype != torch.float32:
+        raise ValueError("dsa_index_score_topk: inconsistent shapes or dtypes")
+    _opt(scores, "scores", torch.float32, (B, n_q, n_kv))
+    _opt(kv_len, "kv_len", torch.int32, (B,))
+    _opt(q_pos, "q_pos", torch.int32, (B, n_q))
+    need = dsa_index_score_topk_workspace_size(B, n_q, H, D, n_kv, top_k, q.dtype, scores is None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.dsa_index_score_topk(q.data_ptr(), k_cache.data_ptr(), w.data_ptr(), _ptr(kv_len), _ptr(q_pos),
+                                    _ptr(scores), idx.data_ptr(), B, n_q, H, D, n_kv, int(top_k), _DTYPE[q.dtype],
+                                    _DTYPE[k_cache.dtype], float(scale), workspace.data_ptr(),
+                                    _workspace_bytes(workspace), _stream(stream)), "dsa_index_score_topk")
+    return idx
 
 
 def dsa_topk_workspace_size(rows: int, n_kv: int, top_k: int) -> int:

@@ -153,6 +153,10 @@ def test_tuning_switch(lib):
         assert lib.dsa_set_tuning(b"score_prefill_waves", v) == OK
     for v in (1, 2, 12, 16, -4):
         assert lib.dsa_set_tuning(b"score_prefill_waves", v) == E_SHAPE
+    for v in (256, 512, 1024, 0):
+        assert lib.dsa_set_tuning(b"topk_cand_block", v) == OK
+    for v in (128, 2048, -1):
+        assert lib.dsa_set_tuning(b"topk_cand_block", v) == E_SHAPE
     assert lib.dsa_set_tuning(b"no_such_key", 1) == E_SHAPE
     assert lib.dsa_set_tuning(None, 1) == E_NULL
 
