@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
 }
 
 // ---------------------------------------------------------------------------------------
-// prefill: grid (ceil(n_q / 8), key spans, B), 4 waves x 2 queries. Every block walks its key
+// prefill: grid (query blocks, key spans, B), NWV waves x 2 queries. Every block walks its key
 // span in 64-key tiles held in two LDS buffers; the next tile is fetched into registers while
 // the current one feeds the MFMAs.
 // ---------------------------------------------------------------------------------------
@@ -370,7 +370,11 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
   const int wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.z;
-  const int q0 = blockIdx.x * kPreQB;
+  // query blocks in descending order: workgroups are dispatched x fastest, and with queries at
+  // increasing positions (a causal prefill chunk) the later query blocks hold more keys of the
+  // diagonal key spans, so the heaviest workgroups of a span start first and the lightest (down
+  // to spans wholly past every query of the block) fill the last gaps
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kPreQB;
   if (tid < kPreQB) {
     const int qi = q0 + tid;
     s_limit[tid] = qi < n_q ? key_limit(kv_len, q_pos, (long)b * n_q + qi, b, qi, n_q, n_kv, sink.kpool) : 0;
