@@ -428,6 +428,51 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
   };
   const int ntiles = kc_end > kbeg ? (kc_end - kbeg + 63) / 64 : 0;
   if (ntiles > 0) issue(kbeg);
+  // Software pipeline over the four 16-key N tiles of a key tile: the 16 MFMAs of N tile nt are
+  // issued one by one, each followed by two VALU operations (relu, weighted add) of N tile
+  // nt - 1's epilogue, so the matrix pipe and the vector ALU work at the same time within the
+  // wave; the operands of N tile nt + 1 are read from LDS while N tile nt computes. The last N
+  // tile's epilogue, the head-sum reduction and the stores of a key tile run during the next key
+  // tile's first 16 MFMAs, so that between two barriers no epilogue is left without products to
+  // hide behind. sched_barrier pins this order.
+  static_assert(kPreQPW == 2, "the pipeline pairs 16 MFMAs with 16 epilogue steps");
+  float sc[kPreQPW][4];
+  i32x4 kv[2][4];
+  f32x4 acc[2][kPreQPW][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int qq = 0; qq < kPreQPW; ++qq)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) acc[a][qq][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto read_tile = [&](const uint8_t* buf, int nt, i32x4(&dst)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      dst[s] = *reinterpret_cast<const i32x4*>(buf + key_lds_off(nt * 16 + r16, 4 * s + g));
+  };
+  // MFMA i of an N tile: k-step i / 4, query (i / 2) % 2, head tile i % 2
+  auto mma_step = [&](int i, const i32x4(&op)[4], f32x4(&a)[kPreQPW][2]) {
+    const int s = i >> 2, qq = (i >> 1) & 1, mt = i & 1;
+    a[qq][mt] = Mma16<T16>::run(qa[qq][mt][s], op[s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : a[qq][mt]);
+  };
+  // epilogue step i of an N tile: query i / 8, head tile i % 2, accumulator row (i / 2) % 4
+  auto epi_step = [&](int i, const f32x4(&a)[kPreQPW][2], float(&p)[kPreQPW]) {
+    const int qq = i >> 3, mt = i & 1, e = (i >> 1) & 3;
+    const float v = relu(a[qq][mt][e]);
+    if (FULLH) p[qq] = fmaf(wr[qq][mt][e], v, p[qq]);
+    else p[qq] += 16 * mt + 4 * g + e < H ? wr[qq][mt][e] * v : 0.f;
+  };
+  // the finished key tile at kb_done: head sums across lanes, then the stores
+  auto finish = [&](int kb_done) {
+    const int t = kb_done + lane;
+#pragma unroll
+    for (int qq = 0; qq < kPreQPW; ++qq) {
+      // cross-lane, so outside the store guard: every lane takes part
+      const float v = tile_reduce(sc[qq][0], sc[qq][1], sc[qq][2], sc[qq][3]);
+      if (qi[qq] < n_q && t < kend)
+        scores[((long)b * n_q + qi[qq]) * n_kv + t] = t < lim[qq] ? sk.add(t, scale * v) : -INFINITY;
+    }
+  };
   for (int tile = 0; tile < ntiles; ++tile) {
     const int kb = kbeg + tile * 64;
     uint8_t* buf = lds[tile & 1];
@@ -438,40 +483,27 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
     }
     __syncthreads();
     if (tile + 1 < ntiles) issue(kb + 64);
-    // Software pipeline over the four 16-key N tiles: the 16 MFMAs of tile nt are issued one
-    // by one, each followed by two VALU operations (relu, weighted add) of tile nt - 1's
-    // epilogue, so the matrix pipe and the vector ALU work at the same time within the wave.
-    // The operands of tile nt + 1 are read from LDS while tile nt computes. sched_barrier
-    // pins this order.
-    static_assert(kPreQPW == 2, "the pipeline pairs 16 MFMAs with 16 epilogue steps");
-    float sc[kPreQPW][4];
-    i32x4 kv[2][4];
-    f32x4 acc[2][kPreQPW][2];
-    auto read_tile = [&](int nt, i32x4(&dst)[4]) {
+    read_tile(buf, 0, kv[0]);
+    read_tile(buf, 1, kv[1]);
+    {
+      // N tile 0, with the previous key tile's last epilogue (on the first key tile it works on
+      // the zeroed accumulators and its result is never stored)
+      float p[kPreQPW] = {0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dst[s] = *reinterpret_cast<const i32x4*>(buf + key_lds_off(nt * 16 + r16, 4 * s + g));
-    };
-    // MFMA i of a tile: k-step i / 4, query (i / 2) % 2, head tile i % 2
-    auto mma_step = [&](int i, const i32x4(&op)[4], f32x4(&a)[kPreQPW][2]) {
-      const int s = i >> 2, qq = (i >> 1) & 1, mt = i & 1;
-      a[qq][mt] = Mma16<T16>::run(qa[qq][mt][s], op[s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : a[qq][mt]);
-    };
-    // epilogue step i of a tile: query i / 8, head tile i % 2, accumulator row (i / 2) % 4
-    auto epi_step = [&](int i, const f32x4(&a)[kPreQPW][2], float(&p)[kPreQPW]) {
-      const int qq = i >> 3, mt = i & 1, e = (i >> 1) & 3;
-      const float v = relu(a[qq][mt][e]);
-      if (FULLH) p[qq] = fmaf(wr[qq][mt][e], v, p[qq]);
-      else p[qq] += 16 * mt + 4 * g + e < H ? wr[qq][mt][e] * v : 0.f;
-    };
-    read_tile(0, kv[0]);
-    read_tile(1, kv[1]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mma_step(i, kv[0], acc[0]);
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(i, kv[0], acc[0]);
+        epi_step(i, acc[1], p);
+      }
+      sc[0][3] = p[0];
+      sc[1][3] = p[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (tile > 0) finish(kb - 64);
 #pragma unroll
     for (int nt = 1; nt < 4; ++nt) {
       __builtin_amdgcn_sched_barrier(0);
-      if (nt + 1 < 4) read_tile(nt + 1, kv[(nt + 1) & 1]);  // tile nt - 1's operands are consumed
+      if (nt + 1 < 4) read_tile(buf, nt + 1, kv[(nt + 1) & 1]);  // N tile nt - 1's operands are consumed
       float p[kPreQPW] = {0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -482,22 +514,15 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
       sc[0][nt - 1] = p[0];
       sc[1][nt - 1] = p[1];
     }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      float p[kPreQPW] = {0.f, 0.f};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (ntiles > 0) {  // the last key tile's last epilogue and its stores
+    float p[kPreQPW] = {0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) epi_step(i, acc[1], p);
-      sc[0][3] = p[0];
-      sc[1][3] = p[1];
-    }
-    const int t = kb + lane;
-#pragma unroll
-    for (int qq = 0; qq < kPreQPW; ++qq) {
-      // cross-lane, so outside the store guard: every lane takes part
-      const float v = tile_reduce(sc[qq][0], sc[qq][1], sc[qq][2], sc[qq][3]);
-      if (qi[qq] < n_q && t < kend)
-        scores[((long)b * n_q + qi[qq]) * n_kv + t] = t < lim[qq] ? sk.add(t, scale * v) : -INFINITY;
-    }
+    for (int i = 0; i < 16; ++i) epi_step(i, acc[1], p);
+    sc[0][3] = p[0];
+    sc[1][3] = p[1];
+    finish(kbeg + (ntiles - 1) * 64);
   }
   // keys of the span past every query's limit are masked for all of them
   const int mstart = max(kbeg, kbeg + ntiles * 64);
