@@ -11,6 +11,41 @@ RTOL = {workloads.F32: 1e-5, workloads.BF16: 2e-3, workloads.F16: 2e-3}
 EDGE_RTOL = 1e-4  # end-to-end index rule: oracle score within 1e-4 relative of the k-th
 
 
+# Guard zones: outputs and workspaces of the parity tests are carved out of larger buffers
+# whose first and last 4 KiB hold a canary byte; after the calls every canary must be intact,
+# so a kernel that writes past either end of what it was given fails the test.
+_GUARD = 4096
+_CANARY = 0xA5
+_guarded = []
+
+
+def guarded(shape, dtype, fill=None) -> torch.Tensor:
+    """A contiguous device tensor with 4 KiB of canary bytes before and after it (checked and
+    forgotten by check_guards). fill: the tensor's own initial value (else the canary bytes)."""
+    shape = tuple(int(x) for x in shape)
+    es = torch.empty((), dtype=dtype).element_size()
+    n = int(np.prod(shape)) if shape else 1
+    raw = torch.full((n * es + 2 * _GUARD,), _CANARY, dtype=torch.uint8, device="cuda")
+    t = raw[_GUARD:_GUARD + n * es].view(dtype).view(shape)
+    if fill is not None:
+        t.fill_(fill)
+    _guarded.append(raw)
+    return t
+
+
+def guarded_workspace(nbytes: int) -> torch.Tensor:
+    return guarded((max(1, int(nbytes)),), torch.uint8)
+
+
+def check_guards(what: str) -> None:
+    """Every canary zone handed out since the last check is intact."""
+    torch.cuda.synchronize()
+    bad = [i for i, raw in enumerate(_guarded)
+           if not (bool((raw[:_GUARD] == _CANARY).all()) and bool((raw[-_GUARD:] == _CANARY).all()))]
+    _guarded.clear()
+    assert not bad, f"{what}: a kernel wrote past the end of an output or workspace ({len(bad)} buffers)"
+
+
 def binding():
     if not torch.cuda.is_available():
         raise RuntimeError("GPU tests need an MI355X; none is visible")
@@ -110,15 +145,20 @@ def run_chain(wl: workloads.Workload, d: dict, ws_topk=None, ws_mla=None, n_spli
     """Scores -> top-k -> sparse MLA through the C ABI, default (bench) launch configuration."""
     L = binding()
     B, n_q = wl.B, wl.n_q
-    scores = torch.empty((B, n_q, wl.n_kv), dtype=torch.float32, device="cuda")
-    idx = torch.empty((B, n_q, wl.top_k), dtype=torch.int32, device="cuda")
-    out = torch.empty((B, n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
-    lse = torch.empty((B, n_q, wl.Hm), dtype=torch.float32, device="cuda")
+    scores = guarded((B, n_q, wl.n_kv), torch.float32)
+    idx = guarded((B, n_q, wl.top_k), torch.int32)
+    out = guarded((B, n_q, wl.Hm, wl.d_latent), torch.float32)
+    lse = guarded((B, n_q, wl.Hm), torch.float32)
+    if ws_topk is None:
+        ws_topk = guarded_workspace(L.dsa_topk_workspace_size(B * n_q, wl.n_kv, wl.top_k))
+    if ws_mla is None:
+        ws_mla = guarded_workspace(L.dsa_sparse_mla_workspace_size(B, n_q, wl.Hm, wl.top_k, wl.d_latent, n_split))
     q_pos = d.get("q_pos") if wl.q_pos_start is not None else None
     L.dsa_index_score(d["q"], d["k"], d["w"], scores, kv_len=d.get("kv_len"), q_pos=q_pos, scale=wl.scale)
     L.dsa_topk(scores, idx, wl.top_k, workspace=ws_topk)
     L.dsa_sparse_mla_attn(d["qa"], d["latent"], idx, out, wl.d_latent, wl.sm_scale, lse=lse,
                           kv_len=d.get("kv_len"), n_split=n_split, workspace=ws_mla)
+    check_guards(f"{wl.name} chain")
     return scores, idx, out, lse
 
 

@@ -1,8 +1,10 @@
 """The whole chain (score -> top-k -> sparse MLA) on the GPU against the oracle.
 
 Small cases are compared in full. The five workloads run at full size in the launch
-configuration the bench times; sampled rows are compared with the oracle and every row is
-checked for the properties a correct selection has at any size.
+configuration the bench times: every sequence of the decode workloads, and for the chunked
+prefill the first 64 queries, the last 64 and every 32nd, are compared with the oracle; every
+row is checked for the properties a correct selection has at any size; the fused score ->
+top-k call the bench times gives the same scores and indices as the two calls.
 Rules: S1 scores within tolerance; S2 top-k fed the oracle's scores is bit-exact; S3 an
 end-to-end index may differ only where its oracle score is within 1e-4 relative of the
 k-th; S5 outputs within tolerance of the oracle evaluated on the GPU's own indices.
@@ -12,8 +14,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import (RTOL, assert_rowwise, binding, check_index_rule, check_topk_properties, dev, host,
-                      run_chain, to_device_inputs)
+from gpu_util import (RTOL, assert_rowwise, binding, check_guards, check_index_rule, check_topk_properties, dev,
+                      guarded, guarded_workspace, host, run_chain, to_device_inputs)
 
 pytestmark = pytest.mark.gpu
 import torch  # noqa: E402
@@ -72,6 +74,18 @@ def _full(name, sel_b, sel_i):
     scores_t, idx_t, out_t, lse_t = run_chain(wl, d)
     torch.cuda.synchronize()
     check_topk_properties(scores_t, idx_t, wl.top_k, name)
+    # the fused score -> top-k call of the bench's step: the same scores and indices, bit for bit
+    f_idx = guarded(tuple(idx_t.shape), torch.int32, fill=-3)
+    f_sc = guarded(tuple(scores_t.shape), torch.float32, fill=-3.0)
+    q_pos = d["q_pos"] if wl.q_pos_start is not None else None
+    L.dsa_index_score_topk(d["q"], d["k"], d["w"], f_idx, wl.top_k, scores=f_sc, kv_len=d["kv_len"], q_pos=q_pos,
+                           scale=wl.scale,
+                           workspace=guarded_workspace(L.dsa_index_score_topk_workspace_size(
+                               wl.B, wl.n_q, wl.H, wl.D, wl.n_kv, wl.top_k, wl.idx_dtype)))
+    check_guards(f"{name} fused score -> top-k")
+    assert torch.equal(f_sc.view(torch.int32), scores_t.view(torch.int32)), f"{name}: fused scores differ"
+    assert torch.equal(f_idx, idx_t), f"{name}: fused indices differ"
+    del f_idx, f_sc
     assert torch.isfinite(out_t).all() and torch.isfinite(lse_t).all()
     scores, idx, out, lse = (host(t) for t in (scores_t, idx_t, out_t, lse_t))
     print(f"[full-size] {name}: oracle on the sample", flush=True)
@@ -95,15 +109,16 @@ def test_full_glm_decode_b1_8k():
 
 
 def test_full_batched_decode_b32_32k():
-    _full("batched_decode_b32_32k", [0, 17, 31], [0])
+    _full("batched_decode_b32_32k", range(32), [0])
 
 
 def test_full_long_decode_b8_128k():
-    _full("long_decode_b8_128k", [0, 5], [0])
+    _full("long_decode_b8_128k", range(8), [0])
 
 
 def test_full_chunked_prefill():
-    sel = sorted(set(range(0, 16)) | set(range(4080, 4096)) | set(range(0, 4096, 256)))
+    # the first 64 queries, the last 64 and every 32nd (252 of the 4096)
+    sel = sorted(set(range(64)) | set(range(4032, 4096)) | set(range(0, 4096, 32)))
     _full("chunked_prefill_4096_after_12288", [0], sel)
 
 

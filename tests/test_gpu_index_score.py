@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import RTOL, assert_rowwise, binding, dev, host
+from gpu_util import RTOL, assert_rowwise, binding, check_guards, dev, guarded, host
 
 pytestmark = pytest.mark.gpu
 import torch  # noqa: E402
@@ -19,11 +19,11 @@ def _run(wl, seed, kv_len=None, q_pos=None, scale=None):
     if qp is None and wl.q_pos_start is not None:
         qp = inp["q_pos"]
     sc = wl.scale if scale is None else scale
-    out = torch.full((wl.B, wl.n_q, wl.n_kv), 7.0, dtype=torch.float32, device="cuda")
+    out = guarded((wl.B, wl.n_q, wl.n_kv), torch.float32, fill=7.0)
     L.dsa_index_score(dev(inp["q"], wl.idx_dtype), dev(inp["k"], wl.idx_dtype), dev(inp["w"]), out,
                       kv_len=dev(kv) if kv_len is not None else None,
                       q_pos=dev(np.asarray(qp, np.int32)) if qp is not None else None, scale=sc)
-    torch.cuda.synchronize()
+    check_guards(f"{wl.name} scores")
     want = oracle.index_score(inp["q"], inp["k"], inp["w"], kv, qp, sc, wl.idx_dtype, wl.idx_dtype)
     assert_rowwise(host(out), want, RTOL[wl.idx_dtype], wl.name)
     return host(out), want
@@ -118,12 +118,12 @@ def _run_sink(wl, seed, sink_start, n_sink, kv_len=None):
     inp = workloads.gen_all(wl, seed, parts=("q", "k", "w"))
     kv = inp["kv_len"] if kv_len is None else np.asarray(kv_len, np.int32)
     qp = inp["q_pos"] if wl.q_pos_start is not None else None
-    out = torch.full((wl.B, wl.n_q, wl.n_kv), 7.0, dtype=torch.float32, device="cuda")
+    out = guarded((wl.B, wl.n_q, wl.n_kv), torch.float32, fill=7.0)
     L.dsa_index_score(dev(inp["q"], wl.idx_dtype), dev(inp["k"], wl.idx_dtype), dev(inp["w"]), out,
                       kv_len=dev(kv) if kv_len is not None else None,
                       q_pos=dev(np.asarray(qp, np.int32)) if qp is not None else None, scale=wl.scale,
                       n_sink=n_sink, sink_start=dev(np.asarray(sink_start, np.int32)) if sink_start is not None else None)
-    torch.cuda.synchronize()
+    check_guards(f"{wl.name} scores with sink")
     want = oracle.index_score_sink(inp["q"], inp["k"], inp["w"], kv, qp, wl.scale, wl.idx_dtype, wl.idx_dtype,
                                    sink_start, n_sink, 1e20)
     got = host(out)

@@ -15,7 +15,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import RTOL, assert_rowwise, binding, check_index_rule, dev, host
+from gpu_util import (RTOL, assert_rowwise, binding, check_guards, check_index_rule, dev, guarded, guarded_workspace,
+                      host)
 
 pytestmark = pytest.mark.gpu
 import torch  # noqa: E402
@@ -59,9 +60,9 @@ def _compress(inp, wl, out_dtype=None, p0=0, p1=None, fill=None):
     packed = dev(inp["packed"], wl.idx_dtype)
     odt = wl.idx_dtype if out_dtype is None else out_dtype
     shape = (wl.B, wl.n_kv // wl.kpool, wl.D)
-    pooled = torch.full(shape, fill, dtype=TORCH[odt], device="cuda") if fill is not None else \
-        torch.empty(shape, dtype=TORCH[odt], device="cuda")
+    pooled = guarded(shape, TORCH[odt], fill=fill)
     L.dsa_kpool_compress(packed, dev(inp["ape"]), pooled, wl.D, wl.kpool, p0, p1)
+    check_guards(f"{wl.name} pool compression")
     return packed, pooled
 
 
@@ -168,23 +169,25 @@ def run_kpool_chain(wl, inp, fused=False):
     packed, pooled = _compress(inp, wl)
     rows, n_pool, kp = wl.B * wl.n_q, wl.n_kv // wl.kpool, wl.top_k // wl.kpool
     kv_len = dev(inp["kv_len"])
-    scores = torch.empty((wl.B, wl.n_q, n_pool), dtype=torch.float32, device="cuda")
+    scores = guarded((wl.B, wl.n_q, n_pool), torch.float32)
     L.dsa_kpool_index_score(dev(inp["q"], wl.idx_dtype), pooled, dev(inp["w"]), scores, wl.kpool, kv_len=kv_len,
                             scale=wl.scale)
-    pidx = torch.empty((wl.B, wl.n_q, kp), dtype=torch.int32, device="cuda")
-    L.dsa_topk(scores, pidx, kp)
+    pidx = guarded((wl.B, wl.n_q, kp), torch.int32)
+    L.dsa_topk(scores, pidx, kp, workspace=guarded_workspace(L.dsa_topk_workspace_size(rows, n_pool, kp)))
     width = wl.kpool * kp + wl.kpool - 1
-    tok = torch.empty((wl.B, wl.n_q, width), dtype=torch.int32, device="cuda")
+    tok = guarded((wl.B, wl.n_q, width), torch.int32)
     L.dsa_kpool_expand(pidx, packed, wl.D, tok, wl.kpool, kv_len=kv_len)
-    out = torch.empty((wl.B, wl.n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
-    lse = torch.empty((wl.B, wl.n_q, wl.Hm), dtype=torch.float32, device="cuda")
+    out = guarded((wl.B, wl.n_q, wl.Hm, wl.d_latent), torch.float32)
+    lse = guarded((wl.B, wl.n_q, wl.Hm), torch.float32)
+    ws_m = guarded_workspace(L.dsa_sparse_mla_workspace_size(wl.B, wl.n_q, wl.Hm, width, wl.d_latent, 0))
     if fused:
         L.dsa_kpool_sparse_mla_attn(dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype), pidx, packed,
-                                    wl.D, wl.kpool, out, wl.d_latent, wl.sm_scale, lse=lse, kv_len=kv_len)
+                                    wl.D, wl.kpool, out, wl.d_latent, wl.sm_scale, lse=lse, kv_len=kv_len,
+                                    workspace=ws_m)
     else:
         L.dsa_sparse_mla_attn(dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype), tok, out,
-                              wl.d_latent, wl.sm_scale, lse=lse, kv_len=kv_len)
-    torch.cuda.synchronize()
+                              wl.d_latent, wl.sm_scale, lse=lse, kv_len=kv_len, workspace=ws_m)
+    check_guards(f"{wl.name} pooled chain")
     return host(scores), host(pidx), host(tok), host(out), host(lse)
 
 

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import RTOL, assert_rowwise, binding, check_index_rule, check_topk_properties, dev, host
+from gpu_util import (RTOL, assert_rowwise, binding, check_guards, check_index_rule, check_topk_properties, dev,
+                      guarded, guarded_workspace, host)
 
 pytestmark = pytest.mark.gpu
 import torch  # noqa: E402
@@ -21,14 +22,16 @@ def _fused_vs_separate(wl, inp, top_k, kv_len=None, q_pos=None, scores_out=True,
     kv = dev(np.asarray(kv_len, np.int32)) if kv_len is not None else None
     qp = dev(np.asarray(q_pos, np.int32)) if q_pos is not None else None
     B, n_q, n_kv = wl.B, wl.n_q, wl.n_kv
-    idx = torch.full((B, n_q, top_k), -7, dtype=torch.int32, device="cuda")
-    sc = torch.full((B, n_q, n_kv), 3.0, dtype=torch.float32, device="cuda") if scores_out else None
-    L.dsa_index_score_topk(q, k, w, idx, top_k, scores=sc, kv_len=kv, q_pos=qp, scale=wl.scale)
-    ref_sc = torch.full((B, n_q, n_kv), 5.0, dtype=torch.float32, device="cuda")
+    idx = guarded((B, n_q, top_k), torch.int32, fill=-7)
+    sc = guarded((B, n_q, n_kv), torch.float32, fill=3.0) if scores_out else None
+    ws = guarded_workspace(L.dsa_index_score_topk_workspace_size(B, n_q, wl.H, wl.D, n_kv, top_k, wl.idx_dtype,
+                                                                 not scores_out))
+    L.dsa_index_score_topk(q, k, w, idx, top_k, scores=sc, kv_len=kv, q_pos=qp, scale=wl.scale, workspace=ws)
+    ref_sc = guarded((B, n_q, n_kv), torch.float32, fill=5.0)
     L.dsa_index_score(q, k, w, ref_sc, kv_len=kv, q_pos=qp, scale=wl.scale)
-    ref_idx = torch.full((B, n_q, top_k), -9, dtype=torch.int32, device="cuda")
-    L.dsa_topk(ref_sc, ref_idx, top_k)
-    torch.cuda.synchronize()
+    ref_idx = guarded((B, n_q, top_k), torch.int32, fill=-9)
+    L.dsa_topk(ref_sc, ref_idx, top_k, workspace=guarded_workspace(L.dsa_topk_workspace_size(B * n_q, n_kv, top_k)))
+    check_guards(f"{wl.name} fused score -> top-k")
     if sc is not None:
         assert torch.equal(sc.view(torch.int32), ref_sc.view(torch.int32)), "fused scores differ from dsa_index_score"
     g_idx = host(idx)

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import RTOL, assert_rowwise, binding, dev, host
+from gpu_util import RTOL, assert_rowwise, binding, check_guards, dev, guarded, guarded_workspace, host
 
 pytestmark = pytest.mark.gpu
 import torch  # noqa: E402
@@ -27,12 +27,13 @@ def _indices(B, n_q, n_kv, top_k, seed, pad=0, bad=0):
 def _run(wl, idx, seed, n_split=0, kv_len=None):
     L = binding()
     inp = workloads.gen_all(wl, seed, parts=("qa", "latent"))
-    out = torch.full((wl.B, wl.n_q, wl.Hm, wl.d_latent), 3.0, dtype=torch.float32, device="cuda")
-    lse = torch.full((wl.B, wl.n_q, wl.Hm), 3.0, dtype=torch.float32, device="cuda")
+    out = guarded((wl.B, wl.n_q, wl.Hm, wl.d_latent), torch.float32, fill=3.0)
+    lse = guarded((wl.B, wl.n_q, wl.Hm), torch.float32, fill=3.0)
+    ws = guarded_workspace(L.dsa_sparse_mla_workspace_size(wl.B, wl.n_q, wl.Hm, idx.shape[-1], wl.d_latent, n_split))
     L.dsa_sparse_mla_attn(dev(inp["qa"], wl.mla_dtype), dev(inp["latent"], wl.mla_dtype), dev(idx), out,
                           wl.d_latent, wl.sm_scale, lse=lse, kv_len=dev(np.asarray(kv_len, np.int32)) if kv_len is not None else None,
-                          n_split=n_split)
-    torch.cuda.synchronize()
+                          n_split=n_split, workspace=ws)
+    check_guards(f"{wl.name} attention")
     o_w, l_w = oracle.sparse_mla(inp["qa"], inp["latent"], idx, wl.sm_scale, wl.d_latent, wl.mla_dtype, kv_len)
     rt = RTOL[wl.mla_dtype]
     assert_rowwise(host(out), o_w, rt, f"{wl.name} out")

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import binding, check_topk_properties, dev, host
+from gpu_util import binding, check_guards, check_topk_properties, dev, guarded, guarded_workspace, host
 
 pytestmark = pytest.mark.gpu
 import torch  # noqa: E402
@@ -23,10 +23,10 @@ def path(request):
 def _run(scores: np.ndarray, top_k: int):
     L = binding()
     rows, n = scores.shape
-    idx = torch.full((rows, top_k), -7, dtype=torch.int32, device="cuda")
+    idx = guarded((rows, top_k), torch.int32, fill=-7)
     s = dev(scores)
-    L.dsa_topk(s, idx, top_k)
-    torch.cuda.synchronize()
+    L.dsa_topk(s, idx, top_k, workspace=guarded_workspace(L.dsa_topk_workspace_size(rows, n, top_k)))
+    check_guards(f"top-k {rows} x {n}, k {top_k}")
     got = host(idx)
     want = oracle.topk(scores, top_k)
     bad = np.nonzero((got != want).any(axis=1))[0]
