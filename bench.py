@@ -120,7 +120,8 @@ def write_traffic(wl_name, fetch_csv, write_csv, copy_mib):
     for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _counter_rows(path, counter)
         copies = [v for _, name, v in rows if "copyBuffer" in name][-3:]
-        score = [v for _, name, v in rows if "index_score_" in name]
+        # the separate-call decode score kernel (the fused call's variant ends in "true>(")
+        score = [v for _, name, v in rows if "index_score_decode_mfma<" in name and ", false>(" in name]
         if len(copies) < 3 or not score:
             sys.exit(f"{path}: no calibration copies or score dispatches with {counter}")
         factor = sum(copies) / len(copies) * 1024 / copy_bytes
@@ -508,11 +509,14 @@ def prefill_leg(dsa, dev, steps, warmup, seed):
     wl = workloads.CHUNKED_PREFILL_16K
     ins = device_inputs(wl, dev, seed, 1)
     chain = Chain(dsa, wl, dev, *ins)
-    n = max(3, steps // 20)
-    for _ in range(max(1, warmup // 10)):
+    # about 2.5 ms a step: the first few calls of the scoring kernel run slower (measured 517 ->
+    # 427 us over nine calls), so the leg warms up for half the decode warmup and times at least
+    # 10 steps
+    n = max(10, steps // 10)
+    for _ in range(max(3, warmup // 2)):
         chain.step(0)
     per, _ = time_calls(chain, n, lambda s: 0)
-    step_s = graph_seconds(lambda m: [chain.step(0) for _ in range(m)], n, 1)
+    step_s = graph_seconds(lambda m: [chain.step(0) for _ in range(m)], n, 3)
     fl = score_flops(wl)
     tfl = fl / (per["index_score"] * 1e-3) / 1e12
     dense = score_flops(wl, causal=False) / (per["index_score"] * 1e-3) / 1e12

@@ -551,8 +551,11 @@ static int decode_iters(long rows, int n_kv, bool tuned = true) {
 // evenly, mu = G top_k / n_kv, plus 4 standard deviations and 4, so that a wave seldom holds
 // more of the top-k than it keeps (the selection then re-reads that wave's scores, and the
 // select kernel lasts as long as its slowest row: at 2.5 deviations about one row in five of
-// the batched decode shape needed a re-read). Waves take more chunks while the union of the
-// candidates would not fit one select workgroup.
+// the batched decode shape needed a re-read). The fused path is taken only when the union of
+// the candidates fits one select workgroup with the score kernel's own chunks per wave: with
+// longer waves (fewer, larger ranges) the score kernel itself slowed down more than the fusion
+// saved (8 x 131072: 47.4 -> 54.2 us at four chunks per wave), so such shapes run the score and
+// top-k kernels one after the other.
 ScoreTopkPlan plan_score_topk(int B, int n_q, int H, int D, int n_kv, int top_k, int dtype) {
   ScoreTopkPlan p{false, 0, 0, 0, 0};
   const long rows = (long)B * n_q;
@@ -560,7 +563,7 @@ ScoreTopkPlan plan_score_topk(int B, int n_q, int H, int D, int n_kv, int top_k,
     return p;
   const long chunks = (n_kv + 255) / 256;
   // the automatic rule only, so that the workspace size does not depend on tuning switches
-  for (int iters = decode_iters(rows, n_kv, false); iters <= 8; iters *= 2) {
+  for (int iters = decode_iters(rows, n_kv, false), last = iters; iters <= last; iters *= 2) {
     const long n_w = (chunks + iters - 1) / iters * 4;
     const int G = 64 * iters;
     const double mu = top_k >= n_kv ? (double)G : (double)G * top_k / n_kv;
