@@ -376,7 +376,16 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   const bool scores = score_wave && hg * 16 < Hm;
   const int head = hg * 16 + r16;
 
-  for (int j = tid; j < nslots; j += 512) {
+  // score waves: query operand (B of the score MFMA), lane holds head, dims 32 s + 8 g .. +8.
+  // Loaded first; the slot indices go to the value waves first (slots 0 .. 255), so that the
+  // two loads are in flight together rather than one after the other.
+  i32x4 qreg[KSW];
+  if (scores) {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(qa) + ((long)bi * Hm + head) * ROWB;
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) qreg[s] = *reinterpret_cast<const i32x4*>(qp + (4 * s + g) * 16);
+  }
+  for (int j = (tid + 256) & 511; j < nslots; j += 512) {
     int r;
     if constexpr (KP) r = kpool_slot_token(ks, bq, s0 + j, b, n_q, n_kv, len);
     else r = idx[(long)bq * top_k + s0 + j];
@@ -385,14 +394,6 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   {  // heads without a score wave keep zero probabilities
     uint4* p4 = reinterpret_cast<uint4*>(&s_p[0][0][0]);
     for (int j = tid; j < (int)(sizeof(s_p) / 16); j += 512) p4[j] = make_uint4(0u, 0u, 0u, 0u);
-  }
-
-  // score waves: query operand (B of the score MFMA), lane holds head, dims 32 s + 8 g .. +8
-  i32x4 qreg[KSW];
-  if (scores) {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(qa) + ((long)bi * Hm + head) * ROWB;
-#pragma unroll
-    for (int s = 0; s < KSW; ++s) qreg[s] = *reinterpret_cast<const i32x4*>(qp + (4 * s + g) * 16);
   }
   constexpr int n_ht = NHT;  // 32-head tiles: (Hm + 31) / 32
   wait_vmcnt<0>();  // query registers ready before the first DMA, so later waits count DMAs only
