@@ -125,6 +125,33 @@ __device__ __forceinline__ void wave_count_min_max(uint32_t& cnt, uint32_t& kmin
   kmin = lane_value(wave_scan(kmin, 0xffffffffu, OpMin()), 63);
   kmax = lane_value(wave_scan(kmax, 0u, OpMax()), 63);
 }
+// count, min, max and a second sum over the workgroup, the same in every thread. Each wave
+// reduces its lanes and leaves (count, min, max, sum) in red[wave]; wave 0 reduces those and
+// leaves the totals in red[BLOCK / 64], which every thread then reads once (rather than every
+// thread reading every wave's entry). red holds BLOCK / 64 + 1 entries.
+template <int BLOCK>
+__device__ __forceinline__ void block_count_min_max(uint32_t& cnt, uint32_t& kmin, uint32_t& kmax, uint32_t& sum,
+                                                    uint4* red) {
+  constexpr int NW = BLOCK / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  wave_count_min_max(cnt, kmin, kmax);
+  sum = lane_value(wave_scan(sum, 0u, OpAdd()), 63);
+  if (lane == 0) red[wave] = make_uint4(cnt, kmin, kmax, sum);
+  __syncthreads();
+  if (wave == 0) {
+    const uint4 r = lane < NW ? red[lane] : make_uint4(0u, 0xffffffffu, 0u, 0u);
+    uint32_t c = r.x, mn = r.y, mx = r.z;
+    wave_count_min_max(c, mn, mx);
+    const uint32_t sw = lane_value(wave_scan((uint32_t)r.w, 0u, OpAdd()), 63);
+    if (lane == 0) red[NW] = make_uint4(c, mn, mx, sw);
+  }
+  __syncthreads();
+  const uint4 t = red[NW];
+  cnt = t.x;
+  kmin = t.y;
+  kmax = t.z;
+  sum = t.w;
+}
 
 // Finding the bin d of hist[0, NB) (bins ascend with the key) that holds the need-th largest
 // counted key, 1 <= need <= total count: the workgroup sums runs of bins (bin_parts), one
@@ -214,7 +241,8 @@ __device__ __forceinline__ void wave_find_in(const uint32_t* hist, BinScan bs, u
 template <int BLOCK>
 struct StreamSmem {
   uint32_t hist[4096];
-  uint32_t wsum[BLOCK / 64], wa[BLOCK / 64], wb[BLOCK / 64], wc[BLOCK / 64];
+  uint4 red[BLOCK / 64 + 1];
+  uint32_t wsum[BLOCK / 64], wa[BLOCK / 64], wb[BLOCK / 64];
   uint32_t sel[2];
 };
 
@@ -244,23 +272,9 @@ __device__ __forceinline__ void select_streaming(StreamSmem<BLOCK>& sm, const fl
       }
     }
   }
-  wave_count_min_max(cnt, kmin, kmax);
-  if (lane == 0) {
-    sm.wa[wave] = cnt;
-    sm.wb[wave] = kmin;
-    sm.wc[wave] = kmax;
-  }
-  __syncthreads();
-  uint32_t n_valid = 0;
-  kmin = 0xffffffffu;
-  kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    n_valid += sm.wa[w];
-    kmin = min(kmin, sm.wb[w]);
-    kmax = max(kmax, sm.wc[w]);
-  }
-  __syncthreads();
+  uint32_t unused = 0;
+  block_count_min_max<BLOCK>(cnt, kmin, kmax, unused, sm.red);
+  const uint32_t n_valid = cnt;
   const uint32_t K = min((uint32_t)top_k, n_valid);
   if (K == 0) {
     for (int p = tid; p < top_k; p += BLOCK) o_idx[p] = -1;
@@ -357,7 +371,7 @@ template <int BLOCK, int ITEMS>
 struct ResidentSmem {
   uint32_t hist[8192];
   uint32_t part[BLOCK];  // 16-byte aligned: follows hist
-  uint32_t wa[BLOCK / 64], wb[BLOCK / 64], wc[BLOCK / 64];
+  uint4 red[BLOCK / 64 + 1];
   uint32_t cnt[ITEMS * (BLOCK / 64)];   // per chunk: (keys > T) << 16 | (keys == T)
   uint32_t eqb[ITEMS * (BLOCK / 64)];   // keys == T before the chunk
   uint32_t selb[ITEMS * (BLOCK / 64)];  // output slots before the chunk
@@ -531,22 +545,9 @@ __device__ __forceinline__ void select_resident(ResidentSmem<BLOCK, ITEMS>& sm, 
       kmax = max(kmax, key[j]);
     }
   }
-  wave_count_min_max(cnt, kmin, kmax);
-  if (lane == 0) {
-    sm.wa[wave] = cnt;
-    sm.wb[wave] = kmin;
-    sm.wc[wave] = kmax;
-  }
-  __syncthreads();
-  uint32_t n_valid = 0;
-  kmin = 0xffffffffu;
-  kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    n_valid += sm.wa[w];
-    kmin = min(kmin, sm.wb[w]);
-    kmax = max(kmax, sm.wc[w]);
-  }
+  uint32_t unused = 0;
+  block_count_min_max<BLOCK>(cnt, kmin, kmax, unused, sm.red);
+  const uint32_t n_valid = cnt;
   const uint32_t K = min((uint32_t)top_k, n_valid);
   if (K == 0) {
     for (int p = tid; p < top_k; p += BLOCK) {
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(BLOCK) void topk_filter(const float* __restrict__ s
   constexpr int NB = 4096, RUNS = SAMPLE / RUN;
   static_assert(NCH <= 64, "one lane per chunk in the offset scan");
   __shared__ uint32_t hist[NB];
-  __shared__ uint32_t s_wa[NW], s_wb[NW], s_wc[NW];
+  __shared__ uint4 s_red4[NW + 1];
   __shared__ uint32_t s_c[NCH];
   __shared__ __align__(16) uint32_t s_part[BLOCK];
   __shared__ uint32_t s_sel[3];
@@ -675,22 +676,9 @@ __global__ __launch_bounds__(BLOCK) void topk_filter(const float* __restrict__ s
       kmax = max(kmax, sk[j]);
     }
   }
-  wave_count_min_max(cnt, kmin, kmax);
-  if (lane == 0) {
-    s_wa[wave] = cnt;
-    s_wb[wave] = kmin;
-    s_wc[wave] = kmax;
-  }
-  __syncthreads();
-  uint32_t n_valid = 0;
-  kmin = 0xffffffffu;
-  kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    n_valid += s_wa[w];
-    kmin = min(kmin, s_wb[w]);
-    kmax = max(kmax, s_wc[w]);
-  }
+  uint32_t unused = 0;
+  block_count_min_max<BLOCK>(cnt, kmin, kmax, unused, s_red4);
+  const uint32_t n_valid = cnt;
   uint32_t G = 1u;
   if (n_valid > need) {  // uniform over the workgroup
     const int shift = max(0, bit_width(kmax - kmin) - 12);
@@ -875,7 +863,7 @@ __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restric
   __shared__ uint32_t s_keep[kCandMaxWaves];  // kept candidates of each wave
   __shared__ uint32_t s_pre[kCandMaxWaves + 1];
   __shared__ uint8_t s_off[kCandMaxWaves];    // wave re-read whole
-  __shared__ uint32_t s_red[NW][4];
+  __shared__ uint4 s_red4[NW + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long row = blockIdx.x;
   int* o_idx = out_idx + row * top_k;
@@ -914,25 +902,8 @@ __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restric
       kmax = max(kmax, key[j]);
     }
   }
-  wave_count_min_max(cnt, kmin, kmax);
-  vsum = lane_value(wave_scan(vsum, 0u, OpAdd()), 63);
-  if (lane == 0) {
-    s_red[wave][0] = cnt;
-    s_red[wave][1] = kmin;
-    s_red[wave][2] = kmax;
-    s_red[wave][3] = vsum;
-  }
-  __syncthreads();
-  uint32_t n_u = 0, n_valid = 0;
-  kmin = 0xffffffffu;
-  kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    n_u += s_red[w][0];
-    kmin = min(kmin, s_red[w][1]);
-    kmax = max(kmax, s_red[w][2]);
-    n_valid += s_red[w][3];
-  }
+  block_count_min_max<BLOCK>(cnt, kmin, kmax, vsum, s_red4);
+  const uint32_t n_u = cnt, n_valid = vsum;
   const uint32_t K = min((uint32_t)top_k, n_valid);
   if (K == 0) {
     for (int p = tid; p < top_k; p += BLOCK) o_idx[p] = -1;
