@@ -495,9 +495,11 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
       }
   }
 
-  // One step: wait for this wave's DMA of the score tiles, barrier, refill the freed stages.
-  // In step it the score waves take the tiles of step u = it + 1, the value waves those of
-  // step it. Both kinds of wave run the same steps (and barriers) in loops of their own, so
+  // One step: wait for this wave's DMA of the score tiles, barrier, refill the freed stages
+  // (a score wave issues its share of the refill once its first tile's operand reads are out,
+  // so the issue overlaps their latency; measured a little faster in decode than issuing it
+  // right after the barrier). In step it the score waves take the tiles of step u = it + 1,
+  // the value waves those of step it. Both kinds of wave run the same steps (and barriers) in loops of their own, so
   // each keeps only its own state in registers. su = stage of tile TPS (it + 1).
   // Steady steps (0 <= it, TPS it <= ntiles - kNst: MAXA later tiles are in flight and all TPS
   // tiles are issued) are compiled apart from the others, without the bounds tests and the
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     st += d;
     return st < 0 ? st + kNst : (st >= kNst ? st - kNst : st);
   };
-  auto step = [&](int it, int su, auto steady) {
+  auto step_sync = [&](int it, auto steady) {
     constexpr bool S = decltype(steady)::value;
     const int u = it + 1;  // score step
     if constexpr (S) {
@@ -517,11 +519,21 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
       if (u < nsteps) wait_tiles(max(0, min(TPS * (it - 1) + kNst, ntiles) - TPS * (u + 1)));
     }
     lds_barrier();
+  };
+  auto step_issue = [&](int it, int su, auto steady) {
+    constexpr bool S = decltype(steady)::value;
 #pragma unroll
     for (int h = 0; h < TPS; ++h)
       if (S || TPS * (it - 1) + kNst + h < ntiles) issue(stage_add(su, h - 2 * TPS), next_rows[h]);
+  };
+  auto step_rows = [&](int it) {
 #pragma unroll
     for (int h = 0; h < TPS; ++h) tile_rows(TPS * it + kNst + h, next_rows[h]);
+  };
+  auto step = [&](int it, int su, auto steady) {
+    step_sync(it, steady);
+    step_issue(it, su, steady);
+    step_rows(it);
   };
   // it = -1, then the steady steps, then the rest, with su = TPS (it + 1) % kNst
   auto run_steps = [&](auto&& body) {
@@ -538,9 +550,14 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     const bool scores_u = wave_u * 16 < Hm;
     auto score_step = [&](int it, int su, auto steady) {
       constexpr bool S = decltype(steady)::value;
-      step(it, su, steady);
+      step_sync(it, steady);
       const int u = it + 1;
-      if (scores_u && (S || u < nsteps)) {
+      const bool sc_now = scores_u && (S || u < nsteps);
+      if (!sc_now) {
+        step_issue(it, su, steady);
+        step_rows(it);
+      }
+      if (sc_now) {
         const int buf = u & 1;
         int sv = -1;
         if (lane < SR) {
@@ -565,6 +582,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
             constexpr int st = KH + decltype(K)::value;
             kb[st - KH] = ds_read_b128_off<128 * (st >> 1)>((st & 1) ? sb1 : sb0);
           });
+          if constexpr (h == 0) step_issue(it, su, steady);  // while the first tile's operands arrive
           lds_wait_first<KH>(ka);
           f32x4 sacc[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
           static_for<0, KH>([&](auto K) {
@@ -621,6 +639,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
         }
         if (lane < 16) s_alpha[buf][head] = alpha;
         if (lane == 0) s_flag[buf][hg] = rescale ? 1u : 0u;
+        step_rows(it);
       } else if (u < nsteps && lane == 0) {
         s_flag[u & 1][hg] = 0u;
       }
