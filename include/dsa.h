@@ -250,8 +250,9 @@ int dsa_topk_source_layer(int layer);
  * down to 1, 2, 4 or 8). key "score_prefill_waves": waves per workgroup of the 16-bit
  * scoring kernel for 8 or more queries per sequence, each wave taking 2 queries (0 =
  * automatic, else 4 or 8). key "mla_tiles_per_step": 16-row tiles of selected latent rows
- * that the 16-bit sparse MLA kernel takes between two workgroup barriers (2 = default, or 1;
- * both give results within the same tolerance, with a different summation order). key
+ * that the 16-bit sparse MLA kernel takes between two workgroup barriers (0 = automatic: 3
+ * when a part holds at least 1024 selected slots, else 2; or 1, 2 or 3 for every call; all
+ * give results within the same tolerance, with a different summation order). key
  * "mla_head_split": run each query's 64 heads as two 32-head workgroups sharing the query's
  * selected rows (0 = automatic: when 64-head workgroups would fill at most half of the 256
  * CUs; 1 = never; 2 = always for 64 heads). key "topk_cand_block": threads of the workgroup that

@@ -92,8 +92,8 @@ int dsa_set_tuning(const char* key, int value) {
     return ok();
   }
   if (std::strcmp(key, "mla_tiles_per_step") == 0) {
-    if (value != 1 && value != 2)
-      return fail(DSA_ERR_SHAPE, "mla_tiles_per_step must be 1 or 2 (got %d)", value);
+    if (value < 0 || value > 3)
+      return fail(DSA_ERR_SHAPE, "mla_tiles_per_step must be 0, 1, 2 or 3 (got %d)", value);
     dsa::g_mla_tiles_per_step.store(value);
     return ok();
   }

@@ -73,7 +73,7 @@ constexpr size_t kTopkScratchBytes = size_t(16) << 20;
 hipError_t topk_scratch(void** ptr);
 
 // sparse MLA
-extern std::atomic<int> g_mla_tiles_per_step;  // 16-row tiles per step of the 16-bit MLA kernel (1 or 2, default 2)
+extern std::atomic<int> g_mla_tiles_per_step;  // 16-row tiles per step of the 16-bit MLA kernel (0 automatic, 1, 2 or 3)
 extern std::atomic<int> g_mla_head_split;      // 64 heads as two 32-head workgroup rows: 0 automatic, 1 never, 2 always
 int mla_auto_splits(int B, int n_q, int top_k);
 size_t mla_workspace_bytes(int B, int n_q, int Hm, int top_k, int d_latent, int n_split);

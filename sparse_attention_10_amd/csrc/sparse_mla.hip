@@ -343,10 +343,15 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   constexpr int NJ = DmaShare<NBLK>::hi;
   static_assert(kTileRows * CPR % 64 == 0 && KSW % SB == 0, "tile shape");
   constexpr int SR = kTileRows * TPS;           // rows per step
-  constexpr int MAXA = kNst - 3 * TPS;          // later tiles in flight when a step's tiles are due
-  static_assert(MAXA >= 1 && MAXA <= 4, "ring depth");
+  // Two tiles a step: a 7-stage ring, step it refills the stages of step it - 1 (MAXA later
+  // tiles in flight when a step's tiles are due). Three tiles a step (OWN): a 6-stage ring,
+  // step it refills its own stages with step it + 2's tiles (none in flight at the wait).
+  constexpr bool OWN = TPS == 3;
+  constexpr int NST = OWN ? 2 * TPS : kNst;     // ring stages
+  constexpr int MAXA = OWN ? 0 : kNst - 3 * TPS;
+  static_assert(OWN || (MAXA >= 1 && MAXA <= 4), "ring depth");
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kNst * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[NST * TILE_BYTES];
   __shared__ int s_idx[kMlaMaxChunk];
   // probabilities of one step's rows: [buffer][hi, lo][head][row], bf16 bits. A head's rows are
   // PS = SR + 8 values apart (SR·2 + 16 bytes): with that stride the 8-byte writes of 16 heads
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
       rows[j] = ((j < NBLK / 8 || j * 8 + wave_u < NBLK) && ts < nslots) ? s_idx[ts] : -1;
     }
   };
-  // ring stage st = tile % kNst, kept by the callers as a counter (no division per step)
+  // ring stage st = tile % NST, kept by the callers as a counter (no division per step)
   auto issue = [&](int st, const int (&rows)[NJ]) {
     uint8_t* stage = s_ring + st * TILE_BYTES;
 #pragma unroll
@@ -444,6 +449,16 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   };
   // waits: at most `ahead` (<= MAXA) later tiles of this wave's DMA may still be in flight
   auto wait_tiles = [&](int ahead) {
+    if constexpr (OWN) {  // ahead is 0 or TPS (the prologue's second step)
+      if (my_blocks == DmaShare<NBLK>::hi) {
+        if (ahead >= TPS) wait_vmcnt<TPS * DmaShare<NBLK>::hi>();
+        else wait_vmcnt<0>();
+      } else {
+        if (ahead >= TPS) wait_vmcnt<TPS * DmaShare<NBLK>::lo>();
+        else wait_vmcnt<0>();
+      }
+      return;
+    }
     if (my_blocks == DmaShare<NBLK>::hi) {
       constexpr int h = DmaShare<NBLK>::hi;
       if (ahead >= 4 && MAXA >= 4) wait_vmcnt<4 * h>();
@@ -461,17 +476,22 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     }
   };
   __syncthreads();  // s_idx and the zeroed probabilities are visible
-  // Tile t goes to stage t % kNst. Before the first step tiles [0, kNst - 2 TPS) are issued;
-  // step it then issues tiles TPS (it - 1) + kNst + h (h < TPS) into the stages of step it - 1's
-  // tiles, which both kinds of wave are done with once step it's barrier has passed.
+  // Tile t goes to stage t % NST. Two tiles a step: before the first step tiles
+  // [0, kNst - 2 TPS) are issued; step it then issues tiles TPS (it - 1) + kNst + h (h < TPS)
+  // into the stages of step it - 1's tiles, which both kinds of wave are done with once step
+  // it's barrier has passed. Three tiles a step: steps 0 and 1's tiles fill the ring before
+  // the first step, and step it >= 0 issues step it + 2's tiles into its own stages, free once
+  // its barrier has passed (the value waves read a step's operands at the end of the step
+  // before it).
+  constexpr int PRO = OWN ? 2 * TPS : kNst - 2 * TPS;  // tiles issued before the first step
   int next_rows[TPS][NJ];
-  for (int p = 0; p < kNst - 2 * TPS; ++p)
+  for (int p = 0; p < PRO; ++p)
     if (p < ntiles) {
       tile_rows(p, next_rows[0]);
       issue(p, next_rows[0]);  // stage p
     }
 #pragma unroll
-  for (int h = 0; h < TPS; ++h) tile_rows(kNst - 2 * TPS + h, next_rows[h]);
+  for (int h = 0; h < TPS; ++h) tile_rows(PRO + h, next_rows[h]);
 
   // Score reads: row r16, chunk 4 s + g stored at (4 s + g) ^ (r16 & 7); for k-steps of one
   // parity the offset grows by 128 bytes per two steps, so two bases cover all steps.
@@ -504,14 +524,18 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   // Steady steps (0 <= it, TPS it <= ntiles - kNst: MAXA later tiles are in flight and all TPS
   // tiles are issued) are compiled apart from the others, without the bounds tests and the
   // case analysis of the wait count, which cost the waves scalar instructions on every step.
-  auto stage_add = [](int st, int d) {  // (st + d) mod kNst for -kNst <= d < kNst
+  auto stage_add = [](int st, int d) {  // (st + d) mod NST for -NST <= d < NST
     st += d;
-    return st < 0 ? st + kNst : (st >= kNst ? st - kNst : st);
+    return st < 0 ? st + NST : (st >= NST ? st - NST : st);
   };
   auto step_sync = [&](int it, auto steady) {
     constexpr bool S = decltype(steady)::value;
     const int u = it + 1;  // score step
-    if constexpr (S) {
+    if constexpr (OWN && S) {
+      wait_vmcnt<0>();  // step u's tiles are the only ones in flight
+    } else if constexpr (OWN) {
+      if (u < nsteps) wait_tiles(it < 0 ? max(0, min(2 * TPS, ntiles) - TPS) : 0);
+    } else if constexpr (S) {
       if (my_blocks == DmaShare<NBLK>::hi) wait_vmcnt<MAXA * DmaShare<NBLK>::hi>();
       else wait_vmcnt<MAXA * DmaShare<NBLK>::lo>();
     } else {
@@ -522,24 +546,33 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
   };
   auto step_issue = [&](int it, int su, auto steady) {
     constexpr bool S = decltype(steady)::value;
+    if constexpr (OWN) {
+      if (S || it >= 0) {
 #pragma unroll
-    for (int h = 0; h < TPS; ++h)
-      if (S || TPS * (it - 1) + kNst + h < ntiles) issue(stage_add(su, h - 2 * TPS), next_rows[h]);
+        for (int h = 0; h < TPS; ++h)
+          if (S || TPS * (it + 2) + h < ntiles) issue(stage_add(su, h - TPS), next_rows[h]);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < TPS; ++h)
+        if (S || TPS * (it - 1) + kNst + h < ntiles) issue(stage_add(su, h - 2 * TPS), next_rows[h]);
+    }
   };
   auto step_rows = [&](int it) {
 #pragma unroll
-    for (int h = 0; h < TPS; ++h) tile_rows(TPS * it + kNst + h, next_rows[h]);
+    for (int h = 0; h < TPS; ++h) tile_rows(OWN ? TPS * (it + 3) + h : TPS * it + kNst + h, next_rows[h]);
   };
   auto step = [&](int it, int su, auto steady) {
     step_sync(it, steady);
     step_issue(it, su, steady);
     step_rows(it);
   };
-  // it = -1, then the steady steps, then the rest, with su = TPS (it + 1) % kNst
+  // it = -1, then the steady steps, then the rest, with su = TPS (it + 1) % NST
   auto run_steps = [&](auto&& body) {
     int it = -1, su = 0;
     body(it, su, std::false_type());
-    for (++it, su = TPS; TPS * it <= ntiles - kNst; ++it, su = stage_add(su, TPS)) body(it, su, std::true_type());
+    for (++it, su = TPS; OWN ? it + 3 <= nsteps : TPS * it <= ntiles - kNst; ++it, su = stage_add(su, TPS))
+      body(it, su, std::true_type());
     for (; it < nsteps; ++it, su = stage_add(su, TPS)) body(it, su, std::false_type());
   };
 
@@ -901,7 +934,7 @@ __global__ __launch_bounds__(256) void mla_merge(const float* __restrict__ ws_o,
 // ---------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-std::atomic<int> g_mla_tiles_per_step{2};
+std::atomic<int> g_mla_tiles_per_step{0};
 std::atomic<int> g_mla_head_split{0};
 
 // Workgroup rows per query of the MFMA kernel: 2 (32 heads each) when 64 heads would leave
@@ -956,7 +989,11 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
   }
   // the tuning switches are read once, so the attention kernel and its merge agree on the layout
   const int hs = mla_head_split(Hm, rows, n_split, g_mla_head_split.load(std::memory_order_relaxed));
-  const int tps = g_mla_tiles_per_step.load(std::memory_order_relaxed);
+  // tiles per step: three for parts of at least 1024 slots (43 barrier steps instead of 64 for
+  // 2048 slots: 1.81-1.83 -> 1.75-1.77 ms for the chunked prefill of 4096 queries), else two
+  // (decode parts of 128 or 256 slots would end in a mostly empty 48-row step)
+  const int tuned_tps = g_mla_tiles_per_step.load(std::memory_order_relaxed);
+  const int tps = tuned_tps ? tuned_tps : (chunk >= 1024 ? 3 : 2);
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
     const int Hk = Hm / hs;  // heads per workgroup row; the [query][head] arrays are read as [query * hs][Hk]
     const unsigned blocks = (unsigned)(rows * hs * n_split);
@@ -964,6 +1001,9 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
     auto kernel = kp
         ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2, true> : sparse_mla_mfma<64, 1, 2, true>)
                         : (Hk > 32 ? sparse_mla_mfma<0, 2, 2, true> : sparse_mla_mfma<0, 1, 2, true>))
+        : tps == 3
+        ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 3> : sparse_mla_mfma<64, 1, 3>)
+                        : (Hk > 32 ? sparse_mla_mfma<0, 2, 3> : sparse_mla_mfma<0, 1, 3>))
         : tps == 2
         ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2> : sparse_mla_mfma<64, 1, 2>)
                         : (Hk > 32 ? sparse_mla_mfma<0, 2, 2> : sparse_mla_mfma<0, 1, 2>))

@@ -142,10 +142,10 @@ def test_tuning_switch(lib):
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", 0) == OK
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", 65) == E_SHAPE
     assert lib.dsa_set_tuning(b"score_chunks_per_wave", -1) == E_SHAPE
-    assert lib.dsa_set_tuning(b"mla_tiles_per_step", 1) == OK
-    assert lib.dsa_set_tuning(b"mla_tiles_per_step", 0) == E_SHAPE
-    assert lib.dsa_set_tuning(b"mla_tiles_per_step", 3) == E_SHAPE
-    assert lib.dsa_set_tuning(b"mla_tiles_per_step", 2) == OK
+    for v in (1, 2, 3, 0):
+        assert lib.dsa_set_tuning(b"mla_tiles_per_step", v) == OK
+    assert lib.dsa_set_tuning(b"mla_tiles_per_step", 4) == E_SHAPE
+    assert lib.dsa_set_tuning(b"mla_tiles_per_step", -1) == E_SHAPE
     for v in (1, 2, 0):
         assert lib.dsa_set_tuning(b"mla_head_split", v) == OK
     assert lib.dsa_set_tuning(b"mla_head_split", 3) == E_SHAPE

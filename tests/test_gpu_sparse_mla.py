@@ -125,11 +125,22 @@ def test_deterministic():
 
 @pytest.fixture
 def one_tile_per_step():
-    """The kernel variant taking one 16-row tile between barriers (the default takes two)."""
+    """The kernel variant taking one 16-row tile between barriers (the automatic choice takes
+    two, or three for parts of 1024 slots or more)."""
     L = binding()
     L.dsa_set_tuning("mla_tiles_per_step", 1)
     yield
-    L.dsa_set_tuning("mla_tiles_per_step", 2)
+    L.dsa_set_tuning("mla_tiles_per_step", 0)
+
+
+@pytest.fixture
+def three_tiles_per_step():
+    """The kernel variant taking three 16-row tiles between barriers (a 6-stage ring in which a
+    step refills its own stages), forced on every shape."""
+    L = binding()
+    L.dsa_set_tuning("mla_tiles_per_step", 3)
+    yield
+    L.dsa_set_tuning("mla_tiles_per_step", 0)
 
 
 @pytest.mark.parametrize("Hm,top_k,n_split,d_rope", [(64, 1, 1, 64), (64, 17, 1, 64), (64, 32, 1, 64),
@@ -142,6 +153,31 @@ def test_one_tile_per_step(one_tile_per_step, Hm, top_k, n_split, d_rope):
     padding tile, which the default-path tests above cover)."""
     wl = DEC.scaled(B=2, n_kv=3000, Hm=Hm, top_k=top_k, d_rope=d_rope)
     _run(wl, _indices(2, 1, wl.n_kv, top_k, top_k + 11), 1, n_split)
+
+
+@pytest.mark.parametrize("Hm,top_k,n_split,d_rope", [(64, 1, 1, 64), (64, 47, 1, 64), (64, 48, 1, 64),
+                                                     (64, 49, 1, 64), (64, 95, 1, 64), (64, 97, 2, 64),
+                                                     (16, 300, 2, 64), (48, 256, 4, 64), (64, 2048, 0, 64),
+                                                     (64, 2048, 8, 64), (32, 513, 5, 64), (64, 2051, 0, 0),
+                                                     (64, 2048, 1, 64), (64, 288, 1, 64)])
+def test_three_tiles_per_step(three_tiles_per_step, Hm, top_k, n_split, d_rope):
+    """The MFMA shapes with three 16-row tiles between barriers: slot counts below one step,
+    at and around a step's 48 rows, ragged parts, the ring's two-step prologue with one or two
+    steps in all, 32-head rows and 512-wide rows."""
+    wl = DEC.scaled(B=2, n_kv=3000, Hm=Hm, top_k=top_k, d_rope=d_rope)
+    _run(wl, _indices(2, 1, wl.n_kv, top_k, top_k + 13), 1, n_split)
+
+
+def test_three_tiles_per_step_padding_kv_len_and_peaks(three_tiles_per_step):
+    wl = DEC.scaled(B=3, n_q=2, n_kv=500, top_k=200)
+    _run(wl, _indices(3, 2, wl.n_kv, 200, 2, pad=37, bad=9), 2, n_split=3, kv_len=[500, 250, 499])
+    test_peaked_softmax()
+    test_empty_selection()
+    wl = DEC.scaled(B=2, n_kv=5000, top_k=2048)
+    idx = _indices(2, 1, 5000, 2048, 7)
+    a, _ = _run(wl, idx, 7, n_split=1)
+    b, _ = _run(wl, idx, 7, n_split=16)
+    assert_rowwise(b, a, 1e-5, "three tiles per step: split 16 vs 1")
 
 
 def test_one_tile_per_step_padding_kv_len_and_peaks(one_tile_per_step):
