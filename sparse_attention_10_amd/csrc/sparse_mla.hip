@@ -139,15 +139,27 @@ __global__ __launch_bounds__(256) void sparse_mla_plain(
       s_l[h] = alpha * s_l[h] + sum;
     }
     __syncthreads();
+    // o = alpha o + sum_j p_j row_j, row by row (each output takes the same operations in the
+    // same order as a per-output loop, with one row's values and weights live at a time)
 #pragma unroll
-    for (int c = 0; c < kMaxD; ++c) {
-      const int d = tid + 256 * c;
-      if (d >= d_latent) break;
+    for (int h = 0; h < kPlainHeads; ++h) {
+      const float a = s_alpha[h];
+#pragma unroll
+      for (int c = 0; c < kMaxD; ++c) o[h][c] *= a;
+    }
+#pragma unroll 2
+    for (int j = 0; j < kPlainRows; ++j) {
+      float rv[kMaxD];
+#pragma unroll
+      for (int c = 0; c < kMaxD; ++c) {
+        const int d = tid + 256 * c;
+        rv[c] = d < d_latent ? s_rows[j * Dc + d] : 0.f;
+      }
 #pragma unroll
       for (int h = 0; h < kPlainHeads; ++h) {
-        float acc = o[h][c] * s_alpha[h];
-        for (int j = 0; j < kPlainRows; ++j) acc = fmaf(s_z[h * kPlainRows + j], s_rows[j * Dc + d], acc);
-        o[h][c] = acc;
+        const float p = s_z[h * kPlainRows + j];
+#pragma unroll
+        for (int c = 0; c < kMaxD; ++c) o[h][c] = fmaf(p, rv[c], o[h][c]);
       }
     }
   }
