@@ -533,9 +533,7 @@ template <int BLOCK, int ITEMS, typename IdOf>
 __device__ __forceinline__ void select_resident(ResidentSmem<BLOCK, ITEMS>& sm, const uint32_t (&key)[ITEMS],
                                                 int top_k, IdOf id_of, int* __restrict__ o_idx,
                                                 float* __restrict__ o_val) {
-  constexpr int NW = BLOCK / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
+  const int tid = threadIdx.x;
   uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
@@ -864,7 +862,7 @@ __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restric
   __shared__ uint32_t s_pre[kCandMaxWaves + 1];
   __shared__ uint8_t s_off[kCandMaxWaves];    // wave re-read whole
   __shared__ uint4 s_red4[NW + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const long row = blockIdx.x;
   int* o_idx = out_idx + row * top_k;
   const int slots = n_w * m;
