@@ -754,6 +754,13 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
     auto value_step = [&](int it, int su, auto steady) {
       constexpr bool S = decltype(steady)::value;
       step(it, su, steady);  // its lgkmcnt(0) wait completes the reads into va
+      // With three tiles a step, the value wave yields its SIMD for about 640 cycles after the
+      // barrier, so that the score wave on the same SIMD (waves w and w + 4 share one) issues
+      // its products before the value wave's 48 queue ahead of them on the matrix core; the
+      // softmax, which waits for those products, then starts earlier. Measured on the chunked
+      // prefill (4096 x 2048 slots, A/B on one box): 1.73-1.76 ms without, 1.71-1.73 with 512
+      // cycles, 1.69-1.72 with 640, 1.70-1.72 with 768. Two tiles a step gained nothing.
+      if constexpr (TPS == 3) __builtin_amdgcn_s_sleep(10);
       if (S || it >= 0) {
         const int buf = it & 1;
         const uint4 fl = *reinterpret_cast<const uint4*>(s_flag[buf]);
