@@ -51,7 +51,7 @@ DEC = workloads.GLM_DECODE_8K
 
 @pytest.mark.parametrize("Hm,top_k,n_split", [(64, 1, 1), (64, 31, 1), (64, 32, 1), (64, 33, 1), (64, 100, 3),
                                               (16, 300, 2), (48, 256, 1), (64, 2048, 0), (64, 2048, 8),
-                                              (32, 513, 5), (48, 256, 4)])
+                                              (32, 513, 5), (48, 256, 4), (16, 300, 1), (32, 100, 1)])
 def test_mfma_shapes(Hm, top_k, n_split):
     wl = DEC.scaled(B=2, n_kv=3000, Hm=Hm, top_k=top_k)
     _run(wl, _indices(2, 1, wl.n_kv, top_k, top_k), 1, n_split)
@@ -159,7 +159,8 @@ def test_one_tile_per_step(one_tile_per_step, Hm, top_k, n_split, d_rope):
                                                      (64, 49, 1, 64), (64, 95, 1, 64), (64, 97, 2, 64),
                                                      (16, 300, 2, 64), (48, 256, 4, 64), (64, 2048, 0, 64),
                                                      (64, 2048, 8, 64), (32, 513, 5, 64), (64, 2051, 0, 0),
-                                                     (64, 2048, 1, 64), (64, 288, 1, 64)])
+                                                     (64, 2048, 1, 64), (64, 288, 1, 64), (32, 700, 1, 0),
+                                                     (16, 1100, 1, 64)])
 def test_three_tiles_per_step(three_tiles_per_step, Hm, top_k, n_split, d_rope):
     """The MFMA shapes with three 16-row tiles between barriers: slot counts below one step,
     at and around a step's 48 rows, ragged parts, the ring's two-step prologue with one or two
