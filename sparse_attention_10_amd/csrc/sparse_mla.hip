@@ -921,6 +921,94 @@ __global__ __launch_bounds__(256) void mla_merge_frag(const float* __restrict__ 
   if (lse && d == 0) lse[bi * Hm + h] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
+// The same merge with PG threads per slot, for calls whose slots alone would give too few
+// workgroups (few queries, many parts): thread group g of a block (SPB = 256 / PG consecutive
+// slots) takes parts [g n_split / PG, (g + 1) n_split / PG), and group 0 combines the groups'
+// (M, L, acc) through LDS. Long decode (8 queries, 16 parts of 128 slots): 256 workgroups,
+// attention with its merge 22.0 us; 1024 workgroups of four groups 19.0 us (eight groups:
+// 21.2 us). The batched decode's 1024 workgroups gain nothing from groups (two: 34.8 -> 35.9).
+template <int PG>
+__global__ __launch_bounds__(256) void mla_merge_frag_g(const float* __restrict__ ws_o,
+                                                        const float* __restrict__ ws_ml,
+                                                        float* __restrict__ out, float* __restrict__ lse,
+                                                        int Hm, int n_ht, int n_split, long total) {
+  constexpr int SPB = 256 / PG;
+  __shared__ f32x4 s_acc[PG][SPB];
+  __shared__ float s_m[PG][SPB], s_l[PG][SPB];
+  const int grp = threadIdx.x / SPB, ls = threadIdx.x - grp * SPB;
+  const long gid = (long)xcd_remap(blockIdx.x, gridDim.x) * SPB + ls;
+  const int per = n_ht * kFragSlots;  // slots per part
+  const long bi = gid / per;
+  const int s = (int)(gid - bi * per);
+  const int lane = s & 63, c = (s >> 6) & 3, dt = (s >> 8) & 3, hq = s >> 10;
+  const int ht = hq % n_ht, pq = hq / n_ht;
+  const int h = 32 * ht + (lane & 31);
+  const bool live = gid < total && h < Hm;
+  const int d = 128 * pq + 32 * dt + 8 * c + 4 * (lane >> 5);
+  const int p0 = grp * n_split / PG, p1 = (grp + 1) * n_split / PG;
+  constexpr int SB = 8;
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    for (int s0 = p0; s0 < p1; s0 += SB) {
+      float m[SB], l[SB];
+      f32x4 v[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const long part = bi * n_split + s0 + j;
+        const bool in = s0 + j < p1;
+        m[j] = in ? ws_ml[2 * (part * Hm + h)] : -INFINITY;
+        l[j] = in ? ws_ml[2 * (part * Hm + h) + 1] : 0.f;
+        v[j] = in ? *reinterpret_cast<const f32x4*>(ws_o + (part * per + s) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float mb = M;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) mb = fmaxf(mb, m[j]);
+      if (mb == -INFINITY) continue;
+      const float r = M == -INFINITY ? 0.f : __expf(M - mb);
+      L *= r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] *= r;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        if (m[j] == -INFINITY) continue;
+        const float f = __expf(m[j] - mb);
+        L = fmaf(f, l[j], L);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = fmaf(f, v[j][k], acc[k]);
+      }
+      M = mb;
+    }
+  }
+  s_m[grp][ls] = M;
+  s_l[grp][ls] = L;
+  s_acc[grp][ls] = acc;
+  __syncthreads();
+  if (grp != 0 || !live) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < PG; ++g) Mt = fmaxf(Mt, s_m[g][ls]);
+  float Lt = 0.f;
+  f32x4 at = {0.f, 0.f, 0.f, 0.f};
+  if (Mt != -INFINITY) {
+#pragma unroll
+    for (int g = 0; g < PG; ++g) {
+      const float mg = s_m[g][ls];
+      if (mg == -INFINITY) continue;
+      const float f = __expf(mg - Mt);
+      Lt = fmaf(f, s_l[g][ls], Lt);
+      const f32x4 ag = s_acc[g][ls];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) at[k] = fmaf(f, ag[k], at[k]);
+    }
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) at[k] *= inv;
+  *reinterpret_cast<f32x4*>(out + (bi * Hm + h) * 512 + d) = at;
+  if (lse && d == 0) lse[bi * Hm + h] = Lt > 0.f ? Mt + __logf(Lt) : -INFINITY;
+}
+
 // ---------------------------------------------------------------------------------------
 // merge: one thread per 4 output values (d_latent % 4 == 0), or per value otherwise.
 // Consecutive threads read consecutive 16-byte pieces of each split's partial output.
@@ -1089,8 +1177,20 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
   if (mla_mfma_supported(Hm, d_latent, d_rope, dtype)) {
     const int n_ht = (Hm / hs + 31) / 32;
     const long total = rows * hs * n_ht * kFragSlots;
-    hipLaunchKernelGGL(mla_merge_frag, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws_o,
-                       ws_ml, out, lse, Hm / hs, n_ht, n_split, total);
+    // thread groups per slot: doubled while the merge has fewer than 1024 workgroups and every
+    // group keeps two parts or more
+    int pg = 1;
+    while (pg < 4 && (total + 255) / 256 * pg < 1024 && n_split >= 4 * pg) pg *= 2;
+    const unsigned nb = (unsigned)((total * pg + 255) / 256);
+    if (pg == 4)
+      hipLaunchKernelGGL(mla_merge_frag_g<4>, dim3(nb), dim3(256), 0, stream, ws_o, ws_ml, out, lse, Hm / hs, n_ht,
+                         n_split, total);
+    else if (pg == 2)
+      hipLaunchKernelGGL(mla_merge_frag_g<2>, dim3(nb), dim3(256), 0, stream, ws_o, ws_ml, out, lse, Hm / hs, n_ht,
+                         n_split, total);
+    else
+      hipLaunchKernelGGL(mla_merge_frag, dim3(nb), dim3(256), 0, stream, ws_o, ws_ml, out, lse, Hm / hs, n_ht,
+                         n_split, total);
   } else if (d_latent % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
     const long total = rows * Hm * (d_latent / 4);
     hipLaunchKernelGGL(mla_merge<4>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws_o, ws_ml,
