@@ -8,6 +8,8 @@ case runs the three calls in the bench's launch configuration and the fused scor
 call, and is checked by the chain's rules: S1 scores within tolerance, S3 indices by the
 end-to-end rule, S5 outputs and lse within tolerance of the oracle on the GPU's indices, the
 fused call equal to the three calls bit for bit, and no write past any output or workspace.
+Three fixed cases add a batch holding an empty sequence (kv_len 0) beside a one-row and a full
+one.
 """
 import numpy as np
 import pytest
@@ -44,6 +46,13 @@ def _cases():
 CASES = _cases()
 
 
+# sequences with no cached row (a padded batch slot), one row, and a full cache, through the
+# decode and the prefill-sized query counts
+EDGE = [dict(i=100 + j, B=3, n_q=n_q, n_kv=3000, H=32, top_k=2048, Hm=64, d_rope=64, idx_dtype=workloads.BF16,
+             n_split=0, kv_len=np.array([0, n_q, 3000], np.int32)) for j, n_q in enumerate((1, 2, 9))]
+CASES = CASES + EDGE
+
+
 @pytest.mark.parametrize("c", CASES, ids=[f"case{c['i']}_B{c['B']}_q{c['n_q']}_kv{c['n_kv']}_k{c['top_k']}"
                                           f"_Hm{c['Hm']}_r{c['d_rope']}_s{c['n_split']}" for c in CASES])
 def test_random_shape(c):
@@ -71,3 +80,6 @@ def test_random_shape(c):
     scores, idx, out, lse = (host(t) for t in (scores_t, idx_t, out_t, lse_t))
     for _ in _compare_rows(wl, inp, scores, idx, out, lse, range(wl.B), range(wl.n_q)):
         pass
+    for b in np.nonzero(c["kv_len"] == 0)[0]:  # an empty sequence selects nothing and attends to nothing
+        assert np.all(np.isneginf(scores[b])) and np.all(idx[b] == -1)
+        assert np.all(out[b] == 0.0) and np.all(np.isneginf(lse[b]))
