@@ -148,12 +148,15 @@ def test_indexshare_shared_layer_reuses_indices():
     assert_rowwise(host(lse), o_lse, RTOL[wl.mla_dtype], "shared layer lse")
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("fused,B", [(False, 4), (True, 4), (True, 2)])
+def test_graph_replays_match_eager(fused, B):
     """The chain captured in a HIP graph (how the bench times it) gives, on every replay, the
     bits of the eager run: the library records no memset nodes and keeps no state between
-    calls. Eager work and synchronisations run between the replays."""
+    calls. Eager work and synchronisations run between the replays. fused: the fused score ->
+    top-k call and the attention (the bench's step); two sequences take 16 parts, whose merge
+    gives each slot four threads."""
     L = binding()
-    wl = workloads.BATCHED_DECODE_32K.scaled(B=4, n_kv=8192)
+    wl = workloads.BATCHED_DECODE_32K.scaled(B=B, n_kv=8192)
     inp = workloads.gen_all(wl, 3)
     d = to_device_inputs(wl, inp)
     rows = wl.B * wl.n_q
@@ -166,9 +169,16 @@ def test_graph_replays_match_eager():
     out = torch.empty((wl.B, wl.n_q, wl.Hm, wl.d_latent), dtype=torch.float32, device="cuda")
     lse = torch.empty((wl.B, wl.n_q, wl.Hm), dtype=torch.float32, device="cuda")
 
+    ws_f = torch.empty(max(1, L.dsa_index_score_topk_workspace_size(wl.B, wl.n_q, wl.H, wl.D, wl.n_kv, wl.top_k,
+                                                                      wl.idx_dtype)), dtype=torch.uint8, device="cuda")
+
     def step():
-        L.dsa_index_score(d["q"], d["k"], d["w"], scores, kv_len=d["kv_len"], scale=wl.scale)
-        L.dsa_topk(scores, idx, wl.top_k, workspace=ws_t)
+        if fused:
+            L.dsa_index_score_topk(d["q"], d["k"], d["w"], idx, wl.top_k, scores=scores, kv_len=d["kv_len"],
+                                   scale=wl.scale, workspace=ws_f)
+        else:
+            L.dsa_index_score(d["q"], d["k"], d["w"], scores, kv_len=d["kv_len"], scale=wl.scale)
+            L.dsa_topk(scores, idx, wl.top_k, workspace=ws_t)
         L.dsa_sparse_mla_attn(d["qa"], d["latent"], idx, out, wl.d_latent, wl.sm_scale, lse=lse,
                               kv_len=d["kv_len"], n_split=ns, workspace=ws_m)
 
