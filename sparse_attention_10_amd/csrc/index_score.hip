@@ -204,7 +204,10 @@ __device__ __forceinline__ float tile_reduce(float p0, float p1, float p2, float
 // reads real data and chunks past the range cost no extra HBM traffic; their scores are
 // replaced by -inf at the store. A wave only reads the LDS tile it wrote itself, so waves
 // never wait for each other: LDS operations of one wave execute in issue order, and a
-// compiler-only fence keeps that order in the code.
+// compiler-only fence keeps that order in the code. The key loads are nontemporal (the nt
+// cache policy): every key row is read once per call, and streaming them past the caches'
+// normal replacement measured 50.8 -> 46.2 us on 32 x 32768 keys (a plain read of 1 GiB
+// reaches about 6.9 TB/s this way against 6.1 TB/s with default loads).
 // ---------------------------------------------------------------------------------------
 constexpr int kDecWaves = 4;
 
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int row = min(kb + 4 * j + g, last);
-      pre[j] = *reinterpret_cast<const i32x4*>(kseq + (long)row * 256 + r16 * 16);
+      pre[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kseq + (long)row * 256 + r16 * 16));
     }
   };
 

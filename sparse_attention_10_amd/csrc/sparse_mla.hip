@@ -338,7 +338,9 @@ __device__ __forceinline__ int kpool_slot_token(const KpoolSlots& ks, int bq, in
   return ok ? (int)t : -1;
 }
 
-template <int DR, int NHT, int TPS, bool KP = false>
+// NT: the calls whose cache rows are not shared between queries (one query per sequence) read
+// the tiles with the nontemporal cache policy; see the DMA issue below.
+template <int DR, int NHT, int TPS, bool KP = false, bool NT = false>
 __global__ __launch_bounds__(512) void sparse_mla_mfma(
     const bf16_t* __restrict__ qa, const bf16_t* __restrict__ lat, const int* __restrict__ idx,
     const int* __restrict__ kv_len, float* __restrict__ out, float* __restrict__ lse,
@@ -458,7 +460,11 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
         const uintptr_t real = reinterpret_cast<uintptr_t>(latb) + (uintptr_t)((long)max(rows[j], 0) * ROWB);
         const uint8_t* src = reinterpret_cast<const uint8_t*>(
             (rows[j] >= 0 ? real : reinterpret_cast<uintptr_t>(zero)) + dma_c[j]);
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + blk * 1024), 16, 0, 0);
+        // NT sets the nt cache-policy bit (aux bit 1): rows read once per call stream past the
+        // caches' normal replacement (attention with its merge, 32 queries x 2048 rows:
+        // 34.1 -> 32.9 us; 8 x 2048: 19.0 -> 18.45 us; the chunked prefill, whose 4096
+        // queries share most rows through the caches, slowed 1.76 -> 1.99 ms with it)
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + blk * 1024), 16, 0, NT ? 2 : 0);
       }
     }
   };
@@ -866,7 +872,10 @@ __global__ __launch_bounds__(512) void sparse_mla_mfma(
 // merge of the MFMA kernel's partials, stored per part in fragment order: 16-byte slot
 // ((((pq * n_ht + ht) * 4 + dt) * 4 + c) * 64 + lane) holds output dims
 // d = 128 pq + 32 dt + 8 c + 4 (lane / 32) .. +3 of head 32 ht + lane % 32. One thread per
-// slot; consecutive threads read consecutive slots of every part.
+// slot; consecutive threads read consecutive slots of every part. (Nontemporal loads of the
+// partials here measured 34.1 -> 33.6 us for the batched decode's attention with its merge
+// alone, but 32.9 -> 34.3 us beside the attention kernel's nontemporal tile reads, so they stay
+// default; nontemporal stores of the partials were slower as well.)
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mla_merge_frag(const float* __restrict__ ws_o,
                                                       const float* __restrict__ ws_ml,
@@ -1137,9 +1146,17 @@ hipError_t launch_sparse_mla(const void* q_abs, const void* latent, const int* i
     const int Hk = Hm / hs;  // heads per workgroup row; the [query][head] arrays are read as [query * hs][Hk]
     const unsigned blocks = (unsigned)(rows * hs * n_split);
     // the pooled-indexer slots (kp) run with two tiles per step whatever the tuning
+    // one query per sequence: no row is shared between the call's workgroups of different
+    // queries, so the two-tile kernels stream the rows (NT)
+    const bool nt = n_q == 1;
     auto kernel = kp
-        ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2, true> : sparse_mla_mfma<64, 1, 2, true>)
-                        : (Hk > 32 ? sparse_mla_mfma<0, 2, 2, true> : sparse_mla_mfma<0, 1, 2, true>))
+        ? (nt ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2, true, true> : sparse_mla_mfma<64, 1, 2, true, true>)
+                              : (Hk > 32 ? sparse_mla_mfma<0, 2, 2, true, true> : sparse_mla_mfma<0, 1, 2, true, true>))
+              : (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2, true> : sparse_mla_mfma<64, 1, 2, true>)
+                              : (Hk > 32 ? sparse_mla_mfma<0, 2, 2, true> : sparse_mla_mfma<0, 1, 2, true>)))
+        : tps == 2 && nt
+        ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 2, false, true> : sparse_mla_mfma<64, 1, 2, false, true>)
+                        : (Hk > 32 ? sparse_mla_mfma<0, 2, 2, false, true> : sparse_mla_mfma<0, 1, 2, false, true>))
         : tps == 3
         ? (d_rope == 64 ? (Hk > 32 ? sparse_mla_mfma<64, 2, 3> : sparse_mla_mfma<64, 1, 3>)
                         : (Hk > 32 ? sparse_mla_mfma<0, 2, 3> : sparse_mla_mfma<0, 1, 3>))
