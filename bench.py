@@ -154,13 +154,15 @@ def kpool_bytes(wl, width):
             "step": score + topk + expand + mla, "fused_sparse_mla": fused, "fused_step": score + topk + fused}
 
 
-def kpool_leg(dsa, dev, steps, warmup, seed):
+def kpool_leg(dsa, dev, steps, warmup, seed, layers=4):
     """The pooled-indexer (kpool) decode step at the batched 32K decode shape, timed like the main
-    step: compress the cache's complete pools once (the prefill-time cost), then K steps of
-    pool scores -> top-k over pools -> sparse MLA (no rope) that expands the pools to tokens
-    itself, replayed from a graph (and the same step with the expansion as a call of its own);
-    per-call times from HIP events in an eager pass. Inputs are drawn on the device
-    from torch's seeded generator with the distributions of workloads.gen_kpool."""
+    step: compress every layer's complete pools once (the prefill-time cost), then K steps of
+    the pool compression its new token completes -> pool scores -> top-k over pools -> sparse
+    MLA (no rope) that expands the pools to tokens itself, rotating over `layers` layers' caches
+    (layer 0 drawn, the others copies at their own addresses) and replayed from a graph; the same
+    step with the expansion as a call of its own, and with every step on layer 0, beside it.
+    Per-call times from HIP events in an eager pass over the rotation. Inputs are drawn on the
+    device from torch's seeded generator with the distributions of workloads.gen_kpool."""
     import torch
     import workloads
     wl = workloads.KPOOL_DECODE_32K
@@ -178,7 +180,9 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
     w = torch.rand((B, 1, wl.H), generator=g, device=dev) * wl.w_scale
     qa = torch.randn((B, 1, wl.Hm, wl.Dc), generator=g, device=dev).bfloat16()
     lat = (torch.randn((B, n_kv, wl.Dc), generator=g, device=dev) * wl.latent_std).bfloat16()
-    pooled = torch.empty((B, n_pool, D), dtype=torch.float16, device=dev)
+    packs = [packed] + [packed.clone() for _ in range(layers - 1)]
+    lats = [lat] + [lat.clone() for _ in range(layers - 1)]
+    pooled = [torch.empty((B, n_pool, D), dtype=torch.float16, device=dev) for _ in range(layers)]
     scores = torch.empty((B, 1, n_pool), dtype=torch.float32, device=dev)
     pidx = torch.empty((B, 1, kp), dtype=torch.int32, device=dev)
     tok = torch.empty((B, 1, width), dtype=torch.int32, device=dev)
@@ -190,86 +194,64 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def compress_all():
-        dsa.dsa_kpool_compress(packed, ape, pooled, D, kpool)
+    def compress_all(l):
+        dsa.dsa_kpool_compress(packs[l], ape, pooled[l], D, kpool)
 
-    score_call = lambda: dsa.dsa_kpool_index_score(q, pooled, w, scores, kpool, kv_len=kv_len, scale=wl.scale)  # noqa: E731
-    topk_call = lambda: dsa.dsa_topk(scores, pidx, kp, workspace=ws_t)  # noqa: E731
-    # the step: pool scores, top-k over pools, and the attention call that expands the pools itself
-    calls = {
-        "index_score": score_call,
-        "topk": topk_call,
-        "sparse_mla": lambda: dsa.dsa_kpool_sparse_mla_attn(qa, lat, pidx, packed, D, kpool, out, wl.d_latent,
-                                                            wl.sm_scale, lse=lse, kv_len=kv_len, n_split=ns,
-                                                            workspace=ws_m),
-    }
-    # the same step with the expansion as a call of its own
-    two_calls = {
-        "index_score": score_call,
-        "topk": topk_call,
-        "expand": lambda: dsa.dsa_kpool_expand(pidx, packed, D, tok, kpool, kv_len=kv_len),
-        "sparse_mla": lambda: dsa.dsa_sparse_mla_attn(qa, lat, tok, out, wl.d_latent, wl.sm_scale, lse=lse,
-                                                      kv_len=kv_len, n_split=ns, workspace=ws_m),
-    }
+    def calls_of(l, own_expand):
+        # a decode step compresses the pool its new token completes (the last pool here), scores
+        # the pools, selects pools, and runs the attention that expands the pools itself (or,
+        # own_expand, the expansion as a call of its own and the token-index attention)
+        c = {"compress": lambda: dsa.dsa_kpool_compress(packs[l], ape, pooled[l], D, kpool, pool_begin=n_pool - 1,
+                                                        pool_end=n_pool),
+             "index_score": lambda: dsa.dsa_kpool_index_score(q, pooled[l], w, scores, kpool, kv_len=kv_len,
+                                                              scale=wl.scale),
+             "topk": lambda: dsa.dsa_topk(scores, pidx, kp, workspace=ws_t)}
+        if own_expand:
+            c["expand"] = lambda: dsa.dsa_kpool_expand(pidx, packs[l], D, tok, kpool, kv_len=kv_len)
+            c["sparse_mla"] = lambda: dsa.dsa_sparse_mla_attn(qa, lats[l], tok, out, wl.d_latent, wl.sm_scale,
+                                                              lse=lse, kv_len=kv_len, n_split=ns, workspace=ws_m)
+        else:
+            c["sparse_mla"] = lambda: dsa.dsa_kpool_sparse_mla_attn(qa, lats[l], pidx, packs[l], D, kpool, out,
+                                                                    wl.d_latent, wl.sm_scale, lse=lse,
+                                                                    kv_len=kv_len, n_split=ns, workspace=ws_m)
+        return c
 
-    # a decode step also compresses the pool its new token completes (the last pool here)
-    compress_one = lambda: dsa.dsa_kpool_compress(packed, ape, pooled, D, kpool, pool_begin=n_pool - 1,  # noqa: E731
-                                                  pool_end=n_pool)
-    calls = {"compress": compress_one, **calls}
-    two_calls = {"compress": compress_one, **two_calls}
+    calls = [calls_of(l, False) for l in range(layers)]
+    two_calls = [calls_of(l, True) for l in range(layers)]
 
-    def kstep():
-        for f in calls.values():
+    def kstep(l, two=False):
+        for f in (two_calls if two else calls)[l].values():
             f()
 
-    def kstep_two():
-        for f in two_calls.values():
-            f()
-
-    for _ in range(3):
-        compress_all()
+    for l in range(layers):
+        compress_all(l)
+    for _ in range(2):
+        compress_all(0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(10):
-        compress_all()
+    for i in range(10):
+        compress_all(i % layers)
     e1.record(stream)
     torch.cuda.synchronize()
     compress_ms = e0.elapsed_time(e1) / 10
     compress_b = B * n_kv * (2 * D + 1) * 2 + B * n_pool * D * 2 + kpool * D * 4
-    for _ in range(max(1, warmup)):
-        kstep()
+    for s_ in range(max(layers, warmup)):
+        kstep(s_ % layers)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    names = list(calls[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     for s_ in range(steps):
         ev[s_][0].record(stream)
-        for j, f in enumerate(calls.values()):
+        for j, f in enumerate(calls[s_ % layers].values()):
             f()
             ev[s_][j + 1].record(stream)
     torch.cuda.synchronize()
     per = {name: sum(ev[s_][j].elapsed_time(ev[s_][j + 1]) for s_ in range(steps)) / steps
-           for j, name in enumerate(calls)}
-    def graph_time(fn):
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            fn()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            fn()
-        for _ in range(max(1, warmup)):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
-
-    step_s = graph_time(kstep)
-    two_s = graph_time(kstep_two)
+           for j, name in enumerate(names)}
+    step_s = graph_seconds(lambda n: [kstep(s_ % layers) for s_ in range(n)], steps, warmup)
+    two_s = graph_seconds(lambda n: [kstep(s_ % layers, True) for s_ in range(n)], steps, warmup)
+    one_s = graph_seconds(lambda n: [kstep(0) for _ in range(n)], steps, warmup)
     ab = kpool_bytes(wl, width)
     ab["sparse_mla"] = ab["fused_sparse_mla"]
     # the one-pool compression: each sequence's 4 packed rows read, its pool key written
@@ -277,11 +259,13 @@ def kpool_leg(dsa, dev, steps, warmup, seed):
     ab["fused_step"] += ab["compress"]
     return {"workload": wl.name, "B": B, "n_kv": n_kv, "kpool": kpool, "top_k_tokens": wl.top_k,
             "pools_selected": kp, "attended_width": width, "d_rope": wl.d_rope, "indexer_dtype": "f16",
+            "layers_rotated": layers,
             "step": "compress the completed pool, pool scores, top-k over pools, attention with the expansion",
             "ms_per_step": round(step_s * 1e3, 4), "tokens_per_s": round(B / step_s, 1),
             "step_algorithmic_bytes": ab["fused_step"], "step_hbm_gbs": round(ab["fused_step"] / step_s / 1e9, 1),
             "step_hbm_frac": round(ab["fused_step"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
             "expansion_as_own_call_ms_per_step": round(two_s * 1e3, 4),
+            "single_layer_ms_per_step": round(one_s * 1e3, 4),
             "kernels_ms": {k_: round(v, 4) for k_, v in per.items()},
             "kernels_gbs": {k_: round(ab[k_] / (per[k_] * 1e-3) / 1e9, 1) for k_ in per},
             "compress_all_pools": {"ms": round(compress_ms, 4), "bytes": compress_b,
