@@ -219,9 +219,12 @@ __device__ __forceinline__ void wave_lds_order() {
 
 //
 // With CAND (the fused score -> top-k call) each wave walks ITERS consecutive chunks, so that a
-// wave's keys form one range, and after its stores it also writes that range's m largest keys
-// as candidates for the selection (the keys of the stored scores, so the selection over the
-// candidates and over the stored row agree bit for bit).
+// wave's keys form one range, and after its stores it also writes m of that range's keys as
+// candidates for the selection: every key whose upper 16 bits exceed those of the m-th largest
+// key, then keys sharing those 16 bits in index order (the keys of the stored scores, so the
+// selection over the candidates and over the stored row agree bit for bit). The header's bound
+// on the keys left out is then the top of that 16-bit bin; deciding 16 bits instead of all 32
+// halves the ballot rounds (fused call 58.0 -> 57.2 us on 32 x 32768 keys).
 template <typename T16, int ITERS, bool FULLH, bool CAND>
 __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     const T16* __restrict__ q, const T16* __restrict__ k, const float* __restrict__ w,
@@ -311,24 +314,24 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
       key[it] = (t < n_kv && t < limit) ? score_key(sk.add(t, scale * res[it])) : 0u;
       nv += (uint32_t)__popcll(__ballot(key[it] != 0u));
     }
-    // the m-th largest key tau, by deciding its bits from the top: the largest prefix with at
-    // least m keys at or above it (with nv <= m every valid key is kept: tau = 1)
+    // the 16-bit prefix p of the m-th largest key, by deciding its bits from the top: the
+    // largest prefix with at least m keys at or above it. Keys with a larger prefix (fewer than
+    // m) are kept, then keys of prefix p in index order up to m; every key left out is at most
+    // z = p << 16 | 0xffff, the bound the header carries (with nv <= m every valid key is kept)
     const uint32_t m = (uint32_t)cand.m;
-    uint32_t tau = 1u, take_eq = 0xffffffffu;
+    uint32_t pb = 0u, take_eq = 0xffffffffu;
     if (nv > m) {
-      uint32_t pre = 0u;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = pre | (1u << bit);
+      for (int bit = 15; bit >= 0; --bit) {
+        const uint32_t c = pb | (1u << bit);
         uint32_t cnt = 0;
 #pragma unroll
-        for (int it = 0; it < ITERS; ++it) cnt += (uint32_t)__popcll(__ballot(key[it] >= c));
-        if (cnt >= m) pre = c;
+        for (int it = 0; it < ITERS; ++it) cnt += (uint32_t)__popcll(__ballot((key[it] >> 16) >= c));
+        if (cnt >= m) pb = c;
       }
-      tau = pre;
-      uint32_t ngt = 0;
+      uint32_t nab = 0;
 #pragma unroll
-      for (int it = 0; it < ITERS; ++it) ngt += (uint32_t)__popcll(__ballot(key[it] > tau));
-      take_eq = m - ngt;  // keys equal to tau that are kept, the lowest indices first
+      for (int it = 0; it < ITERS; ++it) nab += (uint32_t)__popcll(__ballot((key[it] >> 16) > pb));
+      take_eq = m - nab;  // keys of prefix pb that are kept, the lowest indices first
     }
     const int nw = (int)gridDim.x * kDecWaves;
     const long slot = (long)bi * nw + (long)blockIdx.x * kDecWaves + wave;
@@ -337,8 +340,9 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     uint32_t eq_before = 0, sel_before = 0;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      const uint64_t eqm = __ballot(key[it] == tau);
-      const bool sel = key[it] > tau || (key[it] == tau && eq_before + mbcnt(eqm) < take_eq);
+      const bool inb = key[it] != 0u && (key[it] >> 16) == pb;
+      const uint64_t eqm = __ballot(inb);
+      const bool sel = (key[it] >> 16) > pb || (inb && eq_before + mbcnt(eqm) < take_eq);
       const uint64_t selm = __ballot(sel);
       if (sel) {
         const uint32_t p = sel_before + mbcnt(selm);
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
       eq_before += (uint32_t)__popcll(eqm);
       sel_before += (uint32_t)__popcll(selm);
     }
-    if (lane == 0) cand.hdr[slot] = make_uint4(min(nv, m), nv, nv > m ? tau : 0u, 0u);
+    if (lane == 0) cand.hdr[slot] = make_uint4(min(nv, m), nv, nv > m ? (pb << 16 | 0xffffu) : 0u, 0u);
   }
 }
 
