@@ -549,10 +549,15 @@ __global__ __launch_bounds__(NWV * 64) void index_score_prefill_mfma(
 // 64-key chunks per wave of the decode kernel: about 2048 blocks (short-lived waves of two
 // chunks each measured fastest: more independent streams in flight than a few long-lived
 // waves), or the tuning switch when `tuned`.
+// Chunks per wave: about one per 2048 block steps of the call, and at least two once the call
+// has 1024 block steps (workgroups at one chunk per wave): two chunks per wave measured faster
+// from there on (8 x 32768 keys: 17.1 -> 16.3 us, 16 x 32768: 28.3 -> 26.6, 1 x 262144:
+// 17.2 -> 16.6, 4 x 65536: 17.2 -> 16.5, the pooled 32 x 8192: 17.9 -> 17.3 us).
 static int decode_iters(long rows, int n_kv, bool tuned = true) {
   const long chunks = (n_kv + 255) / 256;  // 256-key block steps per query
   const int cpw = tuned ? g_score_cpw.load(std::memory_order_relaxed) : 0;
-  const long want = cpw > 0 ? cpw : (chunks * rows) / 2048;
+  long want = cpw > 0 ? cpw : (chunks * rows) / 2048;
+  if (cpw <= 0 && chunks * rows >= 1024 && want < 2) want = 2;
   return want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
 }
 
