@@ -3,7 +3,8 @@ bit for bit, its indices equal dsa_topk's over those scores bit for bit, and bot
 oracle's rules (scores within the dtype's tolerance, indices by the end-to-end rule). Cases
 cover the candidate path at the decode workloads' shapes, ragged caches and rows, several
 queries per sequence, fewer heads, top_k above n_kv, rows whose answer sits in a few key
-ranges (the re-read of a range) and rows of equal scores (the whole-row fallback)."""
+ranges (the re-read of a range), rows of nearly equal scores (a range's cut inside one 16-bit
+bin) and rows of equal scores (the whole-row fallback)."""
 import numpy as np
 import pytest
 
@@ -118,6 +119,22 @@ def test_equal_scores_fall_back_to_whole_rows():
         inp["q"] = np.zeros_like(inp["q"])
         idx = _fused_vs_separate(wl, inp, 2048)
         assert np.array_equal(idx[0, 0], np.arange(2048))  # ties go to the lowest indices
+
+
+@pytest.mark.parametrize("noise", [0.002, 0.01, 0.05])
+@pytest.mark.parametrize("B,n_kv", [(2, 16384), (8, 32768)])
+def test_near_equal_scores_share_the_cut_bin(B, n_kv, noise):
+    """Keys are one shared key plus a little noise, so scores differ by a fraction of a percent
+    and most of a range's keys share the upper 16 bits of its m-th key: each range keeps part
+    of that bin in index order, not by value (at 1 % noise every range's kept set differs from
+    its m largest keys while the bin's top stays below the row's K-th key, checked with the
+    oracle's scores on the host), or, at 0.2 %, every range's bound reaches that key and the
+    ranges are re-read. The indices must still equal dsa_topk's."""
+    wl = DEC.scaled(B=B, n_kv=n_kv)
+    inp = workloads.gen_all(wl, 13, parts=("q", "k", "w"))
+    k = oracle.decode(inp["k"], wl.idx_dtype)
+    inp["k"] = workloads.round_to(k[:, :1, :] + noise * k, wl.idx_dtype)
+    _fused_vs_separate(wl, inp, 2048, oracle_rows=(0,))
 
 
 @pytest.mark.parametrize("block", [256, 512, 1024])
