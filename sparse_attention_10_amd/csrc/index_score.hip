@@ -354,6 +354,9 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
       eq_before += (uint32_t)__popcll(eqm);
       sel_before += (uint32_t)__popcll(selm);
     }
+    // slots past the kept keys hold key 0 (invalid), so the selection reads the candidates
+    // without waiting for the headers
+    for (uint32_t p = sel_before + lane; p < m; p += 64) ok[p] = 0u;
     if (lane == 0) cand.hdr[slot] = make_uint4(min(nv, m), nv, nv > m ? (pb << 16 | 0xffffu) : 0u, 0u);
   }
 }

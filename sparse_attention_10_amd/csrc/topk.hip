@@ -858,7 +858,6 @@ __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restric
   constexpr int NW = BLOCK / 64;
   constexpr int WPT = (kCandMaxWaves + BLOCK - 1) / BLOCK;  // waves (headers) per thread: tid * WPT + i
   __shared__ FilterSelectSmem<BLOCK, ITEMS> sm;
-  __shared__ uint32_t s_keep[kCandMaxWaves];  // kept candidates of each wave
   __shared__ uint32_t s_pre[kCandMaxWaves + 1];
   __shared__ uint8_t s_off[kCandMaxWaves];    // wave re-read whole
   __shared__ uint4 s_red4[NW + 1];
@@ -868,7 +867,7 @@ __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restric
   const int slots = n_w * m;
   const long cbase = row * (long)slots;
 
-  // candidates (issued first) and headers
+  // candidates (issued first; a wave's slots past its kept count hold key 0) and headers
   uint32_t key[ITEMS];
   int ci[ITEMS];
 #pragma unroll
@@ -883,17 +882,11 @@ __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restric
   for (int i = 0; i < WPT; ++i) {
     const int w = tid * WPT + i;
     h[i] = w < n_w ? chdr[row * n_w + w] : make_uint4(0u, 0u, 0u, 0u);
-    if (w < n_w) s_keep[w] = h[i].x;
     vsum += h[i].y;
   }
-  __syncthreads();
-  // a wave's slots past its kept count hold stale values
   uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
-    const int e = j * BLOCK + tid;
-    const int w = e / m;
-    if (e >= slots || (uint32_t)(e - w * m) >= s_keep[min(w, n_w - 1)]) key[j] = 0u;
     if (key[j]) {
       ++cnt;
       kmin = min(kmin, key[j]);
