@@ -569,12 +569,14 @@ static int decode_iters(long rows, int n_kv, bool tuned = true) {
 // more of the top-k than it keeps (the selection then re-reads that wave's scores, and the
 // select kernel lasts as long as its slowest row: at 2.5 deviations about one row in five of
 // the batched decode shape needed a re-read). The fused path is taken only when the union of
-// the candidates fits one select workgroup with the score kernel's own chunks per wave: with
-// longer waves (fewer, larger ranges) the score kernel itself slowed down more than the fusion
-// saved (8 x 131072: 47.4 -> 54.2 us at four chunks per wave), so such shapes run the score and
-// top-k kernels one after the other.
+// the candidates fits one select workgroup (8192 keys, or 16384 with 16 per thread: 8 x 131072
+// keys, 12288 candidates, fused call 60.8 -> 58.2 us against the score kernel with the filter
+// and its select) with the score kernel's own chunks per wave: with longer waves (fewer, larger
+// ranges) the score kernel itself slowed down more than the fusion saved (8 x 131072: 47.4 ->
+// 54.2 us at four chunks per wave), so shapes beyond that run the score and top-k kernels one
+// after the other.
 ScoreTopkPlan plan_score_topk(int B, int n_q, int H, int D, int n_kv, int top_k, int dtype) {
-  ScoreTopkPlan p{false, 0, 0, 0, 0};
+  ScoreTopkPlan p{false, 0, 0, 0, 0, false};
   const long rows = (long)B * n_q;
   if (!(D == 128 && H >= 1 && H <= 32 && (dtype == kBF16 || dtype == kF16) && n_q < 8 && rows <= 65535))
     return p;
@@ -586,8 +588,9 @@ ScoreTopkPlan plan_score_topk(int B, int n_q, int H, int D, int n_kv, int top_k,
     const double mu = top_k >= n_kv ? (double)G : (double)G * top_k / n_kv;
     int m = (int)ceil(mu + 4.0 * sqrt(mu) + 4.0);
     m = m > G ? G : m;
-    if (n_w <= kCandMaxWaves && n_w * m <= kCandCap) {
+    if (n_w <= kCandMaxWaves && n_w * m <= kCandCapWide) {
       p.ok = true;
+      p.wide = n_w * m > kCandCap;
       p.iters = iters;
       p.m = m;
       p.n_w = (int)n_w;

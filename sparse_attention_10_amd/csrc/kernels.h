@@ -40,8 +40,10 @@ struct ScoreTopkPlan {
   bool ok;
   int iters, m, n_w;
   size_t cand_bytes;  // candidate keys, indices and headers
+  bool wide;          // more than kCandCap candidates per row: the select holds kCandCapWide
 };
-constexpr int kCandCap = 8192;       // candidates one select workgroup holds in registers
+constexpr int kCandCap = 8192;        // candidates one select workgroup holds in registers
+constexpr int kCandCapWide = 16384;   // the same with 16 per thread, for rows of more ranges
 constexpr int kCandMaxWaves = 1024;  // candidate ranges (waves) per row
 extern std::atomic<int> g_topk_cand_block;  // threads of the candidate select workgroup (0: 1024)
 ScoreTopkPlan plan_score_topk(int B, int n_q, int H, int D, int n_kv, int top_k, int dtype);

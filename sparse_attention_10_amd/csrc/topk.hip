@@ -969,10 +969,13 @@ hipError_t launch_topk_cand(const float* scores, int* idx, int rows, int n_kv, i
   const int tuned = g_topk_cand_block.load(std::memory_order_relaxed);
   const int G = 64 * plan.iters;
 #define DSA_CAND_SELECT(BL, IT)                                                                      \
-  static_assert(BL * IT == kCandCap, "one select workgroup holds the candidate union");             \
+  static_assert(BL * IT >= kCandCap, "one select workgroup holds the candidate union");             \
   hipLaunchKernelGGL((topk_cand_select<BL, IT>), dim3(rows), dim3(BL), 0, stream, scores, n_kv, top_k, \
                      plan.n_w, plan.m, G, cand.key, cand.idx, cand.hdr, idx)
-  if (tuned == 256) {
+  if (plan.wide) {
+    static_assert(1024 * 16 == kCandCapWide, "the wide select holds kCandCapWide candidates");
+    DSA_CAND_SELECT(1024, 16);
+  } else if (tuned == 256) {
     DSA_CAND_SELECT(256, 32);
   } else if (tuned == 512) {
     DSA_CAND_SELECT(512, 16);

@@ -137,6 +137,29 @@ def test_near_equal_scores_share_the_cut_bin(B, n_kv, noise):
     _fused_vs_separate(wl, inp, 2048, oracle_rows=(0,))
 
 
+@pytest.mark.parametrize("kind", ["plain", "concentrated", "near_equal", "equal"])
+def test_wide_select_128k_rows(kind):
+    """Rows of 131072 keys: 1024 ranges of 12 candidates, more than 8192, so the select holds 16
+    per thread. Plain rows, an answer concentrated in a few ranges (re-read), nearly equal scores
+    (cut inside a 16-bit bin) and equal scores (re-read set larger than the workgroup: the
+    streaming select)."""
+    wl = workloads.LONG_DECODE_128K.scaled(B=2)
+    inp = workloads.gen_all(wl, 14, parts=("q", "k", "w"))
+    if kind == "concentrated":
+        k = oracle.decode(inp["k"], wl.idx_dtype)
+        q = oracle.decode(inp["q"], wl.idx_dtype)
+        k[:, 70000:70600] += 2.0 * q[:, 0, 0][:, None, :]
+        inp["k"] = workloads.round_to(k, wl.idx_dtype)
+        inp["w"] = inp["w"].copy()
+        inp["w"][:, :, 0] = 1.0
+    elif kind == "near_equal":
+        k = oracle.decode(inp["k"], wl.idx_dtype)
+        inp["k"] = workloads.round_to(k[:, :1, :] + 0.01 * k, wl.idx_dtype)
+    elif kind == "equal":
+        inp["q"] = np.zeros_like(inp["q"])
+    _fused_vs_separate(wl, inp, wl.top_k, oracle_rows=(0,))
+
+
 @pytest.mark.parametrize("block", [256, 512, 1024])
 def test_select_block_sizes(block):
     """Every select workgroup size gives the same answer, on the plain path, the re-read path and
