@@ -1099,6 +1099,12 @@ int mla_auto_splits(int B, int n_q, int top_k) {
   // attention with its merge, 24 queries x 2048 slots: 45.8 us at 11 parts, 33.1 us at 10;
   // 48 queries: 62.9 us at 6 parts, 43.2 us at 5)
   long s = 256 / rows;
+  // parts shorter than 400 slots: about three workgroups per four CUs instead. A short part's
+  // fixed costs (slot and query loads, the partial stores and their merge) weigh more than the
+  // idle CUs (attention with its merge, 2048 slots: 24 queries 33.0 -> 30.4 us at 8 parts
+  // instead of 10, 16 queries 26.9 -> 25.9 at 12 instead of 16; 32 queries 34.2 -> 33.7 at 6
+  // instead of 8, the same decode step within noise)
+  if (s >= 1 && top_k / s < 400 && 192 / rows >= 1) s = 192 / rows;
   // at least 128 slots per part; short selections may still take up to 4 parts of 16 slots
   // (one tile each), which cuts the serial row fetches of a single workgroup
   long max_s = top_k / 128;
