@@ -133,6 +133,21 @@ def test_sparse_mla_workspace_size(lib):
     assert f(32, 1, 64, 2048, 512, 0) == f(32, 1, 64, 2048, 512, auto)
 
 
+def test_auto_splits_fit_one_round_of_workgroups(lib):
+    """The automatic part count never asks for more than one workgroup per CU (256) beyond what
+    the selection's length forces, and keeps parts of at least 128 slots when it splits."""
+    f = lib.dsa_sparse_mla_num_splits
+    for top_k in (64, 2048, 2051):
+        for rows in range(1, 300):
+            s = f(rows, 1, top_k)
+            assert s >= 1
+            forced = -(-top_k // 2048)  # one part holds at most 2048 slots
+            assert rows * s <= 256 or s == forced, (rows, top_k, s)
+            assert s == 1 or top_k // s >= 16, (rows, top_k, s)
+    assert f(32, 1, 2048) == 6 and f(64, 1, 2048) == 4 and f(8, 1, 2048) == 16
+    assert f(1, 4096, 2048) == 1  # a prefill chunk: one part per query
+
+
 def test_tuning_switch(lib):
     assert lib.dsa_set_tuning(b"topk_path", 2) == OK
     assert lib.dsa_set_tuning(b"topk_path", 0) == OK
