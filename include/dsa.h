@@ -184,6 +184,11 @@ int dsa_topk_noalloc(const float* scores, int32_t* idx, int rows, int n_kv, int 
  * dtype: F32 or BF16. BF16 with Hm a multiple of 16 (<= 64), d_latent = 512 and
  * d_rope in {0, 64} runs on MFMA; other shapes run a plain kernel that needs
  * Dc <= 1024, d_latent <= 1024 and B * n_q <= 65535 (DSA_ERR_UNSUPPORTED otherwise).
+ *
+ * dsa_sparse_mla_num_splits: the automatic part count, a host-side rule (no device work):
+ * floor(256 / (B n_q)) parts, or floor(192 / (B n_q)) when parts would hold fewer than 400
+ * slots, at most top_k / 128 (short selections: up to 4 parts of 16 slots or more) and at
+ * least ceil(top_k / 2048); never fewer than 1.
  */
 int dsa_sparse_mla_num_splits(int B, int n_q, int top_k);
 size_t dsa_sparse_mla_workspace_size(int B, int n_q, int Hm, int top_k, int d_latent, int n_split);
