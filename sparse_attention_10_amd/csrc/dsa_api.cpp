@@ -209,8 +209,7 @@ int dsa_index_score_topk(const void* q, const void* k_cache, const float* w, con
     return hip_status(dsa::launch_topk(sc, idx, rows, n_kv, top_k, tp, ws, stream), "dsa_index_score_topk top-k launch");
   }
   const size_t slots = (size_t)rows * plan.n_w * plan.m;
-  dsa::CandOut cand{reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int*>(ws + align256(slots * 4)),
-                    reinterpret_cast<uint4*>(ws + 2 * align256(slots * 4)), plan.m};
+  dsa::CandOut cand{reinterpret_cast<uint2*>(ws), reinterpret_cast<uint4*>(ws + align256(slots * 8)), plan.m};
   hipError_t e = dsa::launch_index_score_cand(q, k_cache, w, kv_len, q_pos, sc, B, n_q, H, n_kv, q_dtype, scale, plan,
                                               cand, stream);
   if (e != hipSuccess) return hip_status(e, "dsa_index_score_topk score launch");

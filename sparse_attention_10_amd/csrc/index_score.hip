@@ -337,8 +337,7 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
     }
     const int nw = (int)gridDim.x * kDecWaves;
     const long slot = (long)bi * nw + (long)wave * gridDim.x + blockIdx.x;
-    uint32_t* ok = cand.key + slot * m;
-    int* oi = cand.idx + slot * m;
+    uint2* okv = cand.kv + slot * m;  // (key, index) in one 8-byte store
     uint32_t eq_before = 0, sel_before = 0;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -348,15 +347,14 @@ __global__ __launch_bounds__(256, 2) void index_score_decode_mfma(
       const uint64_t selm = __ballot(sel);
       if (sel) {
         const uint32_t p = sel_before + mbcnt(selm);
-        ok[p] = key[it];
-        oi[p] = kb_of(it) + lane;
+        okv[p] = make_uint2(key[it], (uint32_t)(kb_of(it) + lane));
       }
       eq_before += (uint32_t)__popcll(eqm);
       sel_before += (uint32_t)__popcll(selm);
     }
     // slots past the kept keys hold key 0 (invalid), so the selection reads the candidates
     // without waiting for the headers
-    for (uint32_t p = sel_before + lane; p < m; p += 64) ok[p] = 0u;
+    for (uint32_t p = sel_before + lane; p < m; p += 64) okv[p] = make_uint2(0u, 0u);
     if (lane == 0) cand.hdr[slot] = make_uint4(min(nv, m), nv, nv > m ? (pb << 16 | 0xffffu) : 0u, 0u);
   }
 }
@@ -595,7 +593,7 @@ ScoreTopkPlan plan_score_topk(int B, int n_q, int H, int D, int n_kv, int top_k,
       p.m = m;
       p.n_w = (int)n_w;
       const size_t slots = (size_t)rows * n_w * m;
-      p.cand_bytes = (slots * 4 + 255) / 256 * 256 * 2 + (size_t)rows * n_w * 16;
+      p.cand_bytes = (slots * 8 + 255) / 256 * 256 + (size_t)rows * n_w * 16;
       return p;
     }
   }
@@ -670,11 +668,11 @@ static hipError_t launch_mfma(const void* q, const void* k, const float* w, cons
   if (H == 32)                                                                                \
     hipLaunchKernelGGL((index_score_decode_mfma<T16, N, true, false>), grid, dim3(256), 0, stream, \
                        (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, sink, \
-                       CandOut{nullptr, nullptr, nullptr, 0});                                \
+                       CandOut{nullptr, nullptr, 0});                                \
   else                                                                                        \
     hipLaunchKernelGGL((index_score_decode_mfma<T16, N, false, false>), grid, dim3(256), 0, stream, \
                        (const T16*)q, (const T16*)k, w, kv_len, q_pos, scores, n_q, H, n_kv, scale, sink, \
-                       CandOut{nullptr, nullptr, nullptr, 0})
+                       CandOut{nullptr, nullptr, 0})
     switch (iters) {
       case 8: DSA_DECODE_LAUNCH(8); break;
       case 4: DSA_DECODE_LAUNCH(4); break;

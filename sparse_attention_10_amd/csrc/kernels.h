@@ -24,13 +24,13 @@ struct ScoreArgs {
 
 // Tuning switches (dsa_set_tuning): process-wide, each read once per call.
 // Candidate output of the decode score kernel for the fused score -> top-k call: every wave
-// (n_w per row, each over its own G = ITERS * 64 consecutive keys) writes its m largest valid
-// keys (order-preserving keys, ties to the lower index) in index order, and a header
-// {kept, valid keys, m-th largest key when valid > m (else 0), 0}.
+// (n_w per row, each over its own G = ITERS * 64 consecutive keys) writes min(valid, m) of its
+// valid keys (order-preserving keys) in index order as (key, index) pairs, key 0 in the slots
+// it leaves unused, and a header {kept, valid keys, bound tau, 0}: when it holds more than m
+// valid keys, every key it did not keep is at most tau (else tau = 0).
 struct CandOut {
-  uint32_t* key;  // [rows][n_w * m]
-  int* idx;       // [rows][n_w * m]
-  uint4* hdr;     // [rows][n_w]
+  uint2* kv;   // [rows][n_w * m]: (key, index) pairs, 8 bytes each
+  uint4* hdr;  // [rows][n_w]
   int m;
 };
 // Plan of the fused score -> top-k path for decode rows (16-bit, D = 128, H <= 32, n_q < 8):

@@ -837,9 +837,10 @@ __global__ __launch_bounds__(BLOCK) void topk_filtered_select(const float* __res
 // ---------------------------------------------------------------------------------------
 // Selection over the candidates of the fused score -> top-k call: one workgroup per row.
 //
-// The score kernel left, for each wave w of the row (keys [w G, w G + G)), its e_w = min(v_w, m)
-// largest valid keys in index order, its valid count v_w and, when it held more than m valid
-// keys (truncated), its m-th largest key tau_w. Let K = min(top_k, sum v_w) and T the K-th
+// The score kernel left, for each wave w of the row (its range of G keys), e_w = min(v_w, m) of
+// its valid keys in index order as (key, index) pairs (key 0 in the unused slots), its valid
+// count v_w and, when it held more than m valid keys (truncated), a bound tau_w on every key it
+// did not keep (the top of the 16-bit bin it was cut in). Let K = min(top_k, sum v_w) and T the K-th
 // largest of the union U of the kept keys. A key a truncated wave did not keep is at most
 // tau_w, so when tau_w < T it is below K keys of U and cannot be chosen: if every truncated
 // wave has tau_w < T, the top-k of U is the top-k of the row. Otherwise the waves with
@@ -852,8 +853,7 @@ __global__ __launch_bounds__(BLOCK) void topk_filtered_select(const float* __res
 // ---------------------------------------------------------------------------------------
 template <int BLOCK, int ITEMS>
 __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restrict__ scores, int n_kv, int top_k,
-                                                          int n_w, int m, int G, const uint32_t* __restrict__ ckey,
-                                                          const int* __restrict__ cidx,
+                                                          int n_w, int m, int G, const uint2* __restrict__ ckv,
                                                           const uint4* __restrict__ chdr, int* __restrict__ out_idx) {
   constexpr int NW = BLOCK / 64;
   constexpr int WPT = (kCandMaxWaves + BLOCK - 1) / BLOCK;  // waves (headers) per thread: tid * WPT + i
@@ -873,8 +873,9 @@ __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restric
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
     const int e = j * BLOCK + tid;
-    key[j] = e < slots ? ckey[cbase + e] : 0u;
-    ci[j] = e < slots ? cidx[cbase + e] : -1;
+    const uint2 v = e < slots ? ckv[cbase + e] : make_uint2(0u, 0xffffffffu);
+    key[j] = v.x;
+    ci[j] = (int)v.y;
   }
   uint4 h[WPT];
   uint32_t vsum = 0;
@@ -953,8 +954,9 @@ __global__ __launch_bounds__(BLOCK) void topk_cand_select(const float* __restric
         key[j] = score_key(scores[row * n_kv + t]);
         ci[j] = t;
       } else {
-        key[j] = ckey[cbase + (long)w * m + slot];
-        ci[j] = cidx[cbase + (long)w * m + slot];
+        const uint2 v = ckv[cbase + (long)w * m + slot];
+        key[j] = v.x;
+        ci[j] = (int)v.y;
       }
     }
   }
@@ -971,7 +973,7 @@ hipError_t launch_topk_cand(const float* scores, int* idx, int rows, int n_kv, i
 #define DSA_CAND_SELECT(BL, IT)                                                                      \
   static_assert(BL * IT >= kCandCap, "one select workgroup holds the candidate union");             \
   hipLaunchKernelGGL((topk_cand_select<BL, IT>), dim3(rows), dim3(BL), 0, stream, scores, n_kv, top_k, \
-                     plan.n_w, plan.m, G, cand.key, cand.idx, cand.hdr, idx)
+                     plan.n_w, plan.m, G, cand.kv, cand.hdr, idx)
   if (plan.wide) {
     static_assert(1024 * 16 == kCandCapWide, "the wide select holds kCandCapWide candidates");
     DSA_CAND_SELECT(1024, 16);
