@@ -137,6 +137,49 @@ def test_near_equal_scores_share_the_cut_bin(B, n_kv, noise):
     _fused_vs_separate(wl, inp, 2048, oracle_rows=(0,))
 
 
+@pytest.mark.parametrize("B,n_kv", [(2, 16384), (2, 131072)])
+def test_nonfinite_scores(B, n_kv):
+    """Non-finite scores: sequence 0 weighs head 0 by +inf, so its scores are +inf where that
+    head's relu is positive and NaN (inf x 0) where it is zero, many +inf ties and NaN (invalid)
+    keys; sequence 1 holds key rows whose head-0 dot overflows to +inf among finite scores, and
+    NaN key rows. The fused call's indices must equal dsa_topk's over the same scores (no oracle
+    comparison: its rules are stated for finite inputs)."""
+    L = binding()
+    wl = DEC.scaled(B=B, n_kv=n_kv)
+    inp = workloads.gen_all(wl, 15, parts=("q", "k", "w"))
+    k = oracle.decode(inp["k"], wl.idx_dtype)
+    rng = np.random.default_rng(15)
+    rows = rng.choice(n_kv, size=64, replace=False)
+    q0 = oracle.decode(inp["q"], wl.idx_dtype)[1, 0, 0, :]
+    k[1, rows[:32]] = 1e38 * np.sign(q0)[None, :]  # head 0's dot overflows to +inf
+    k[1, rows[32:]] = np.nan
+    inp["k"] = workloads.round_to(k, wl.idx_dtype)
+    w_np = inp["w"].copy()
+    w_np[0, 0, 0] = np.inf
+    q, kk, w = dev(inp["q"], wl.idx_dtype), dev(inp["k"], wl.idx_dtype), dev(w_np)
+    idx = guarded((B, 1, 2048), torch.int32, fill=-7)
+    sc = guarded((B, 1, n_kv), torch.float32, fill=3.0)
+    L.dsa_index_score_topk(q, kk, w, idx, 2048, scores=sc, scale=wl.scale,
+                           workspace=guarded_workspace(L.dsa_index_score_topk_workspace_size(
+                               B, 1, wl.H, wl.D, n_kv, 2048, wl.idx_dtype)))
+    ref_sc = guarded((B, 1, n_kv), torch.float32, fill=5.0)
+    L.dsa_index_score(q, kk, w, ref_sc, scale=wl.scale)
+    ref_idx = guarded((B, 1, 2048), torch.int32, fill=-9)
+    L.dsa_topk(ref_sc, ref_idx, 2048, workspace=guarded_workspace(L.dsa_topk_workspace_size(B, n_kv, 2048)))
+    check_guards("non-finite scores")
+    h = host(ref_sc)
+    print(f"[nonfinite] seq 0: +inf {int(np.isposinf(h[0]).sum())}, NaN {int(np.isnan(h[0]).sum())}; "
+          f"seq 1: +inf {int(np.isposinf(h[1]).sum())}, NaN {int(np.isnan(h[1]).sum())}", flush=True)
+    assert np.isposinf(h[0]).sum() > 2048 and np.isnan(h[0]).any(), "sequence 0 should hold +inf ties and NaN"
+    assert np.isposinf(h[1]).any(), "sequence 1 should hold +inf scores"
+    assert torch.equal(sc.view(torch.int32), ref_sc.view(torch.int32))
+    assert torch.equal(idx, ref_idx), "fused indices differ from dsa_topk over the same scores"
+    check_topk_properties(ref_sc, idx, 2048, "non-finite scores")
+    g = host(idx)
+    assert np.all(np.isposinf(h[0, 0, g[0, 0]])), "sequence 0 keeps +inf keys only"
+    assert np.array_equal(g[0, 0], np.nonzero(np.isposinf(h[0, 0]))[0][:2048]), "+inf ties go to the lowest indices"
+
+
 @pytest.mark.parametrize("kind", ["plain", "concentrated", "near_equal", "equal"])
 def test_wide_select_128k_rows(kind):
     """Rows of 131072 keys: 1024 ranges of 12 candidates, more than 8192, so the select holds 16
